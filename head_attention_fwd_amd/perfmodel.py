@@ -1,0 +1,50 @@
+"""Work model of attention: allowed (query, key) pairs and algorithmic FLOPs/bytes.
+
+Complexity per layer of self-attention is O(n^2 * d) (page "Attention Is All
+You Need/paper/es", §4, Table 1); counted exactly here from the mask: each
+allowed pair costs 2*d_k FLOPs for its score and 2*d_v for its share of the
+weighted sum of values.  Softmax work (exp, max, sum) is not counted.
+"""
+
+
+def clamp_length(length, Lk):
+    return int(min(max(int(length), 0), Lk))
+
+
+def pair_count(B, H, Lq, Lk, causal, key_lengths=None):
+    """Number of (query, key) pairs the mask allows, summed over batch and heads.
+
+    Key j is allowed for query i when j < len_b and, for causal attention, j <= i;
+    len_b = clamp(key_lengths[b], 0, Lk), or Lk without key_lengths.
+    """
+    total = 0
+    for b in range(B):
+        lb = Lk if key_lengths is None else clamp_length(key_lengths[b], Lk)
+        if not causal:
+            total += Lq * lb
+        elif lb <= Lq:
+            # rows i < lb see i+1 keys, rows i >= lb see lb keys
+            total += lb * (lb + 1) // 2 + (Lq - lb) * lb
+        else:
+            total += Lq * (Lq + 1) // 2
+    return total * H
+
+
+def flops(B, H, Lq, Lk, d_k, d_v, causal, key_lengths=None):
+    """Algorithmic FLOPs: (2*d_k + 2*d_v) per allowed pair."""
+    return (2 * d_k + 2 * d_v) * pair_count(B, H, Lq, Lk, causal, key_lengths)
+
+
+def min_bytes(B, H, Lq, Lk, d_k, d_v, causal, key_lengths=None, elem=2):
+    """Algorithmic HBM bytes: Q and O once, and every key/value row some query may use.
+
+    Rows j >= len_b are never needed; causal attention with Lq < Lk never needs
+    rows j >= Lq.
+    """
+    rows_kv = 0
+    for b in range(B):
+        lb = Lk if key_lengths is None else clamp_length(key_lengths[b], Lk)
+        if causal:
+            lb = min(lb, Lq)
+        rows_kv += lb
+    return elem * H * (B * Lq * (d_k + d_v) + rows_kv * (d_k + d_v))

@@ -1,0 +1,221 @@
+/*
+ * sdpa_oracle.c -- plain fp64 CPU oracle for multi-head scaled dot-product
+ * attention, forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the ground truth that the HIP path is
+ * checked against.  Only tests/, __graft_entry__.smoke() and bench.py's
+ * cpu_baseline leg may load it.  It shares no code, header or constant with the
+ * HIP library and must never be used to produce a product result.
+ *
+ * What it computes (one definition, written out; no blocking, no fusion, no
+ * online rescaling):
+ *
+ *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
+ *     -- page "Attention Is All You Need/paper/es", §3.2.1, Eq. (1): dot products
+ *        of the query with every key, each divided by sqrt(d_k), a softmax for
+ *        the weights, and the output as the weighted sum of the values (§3.2).
+ *
+ *   Masking: "illegal connections" get the score -infinity before the softmax
+ *     -- same page, §3.2.3 (decoder self-attention may attend to every position
+ *        up to and including its own).  Page "Arquitectura Transformer",
+ *        section "Cómo hacerlo": a score of -infinity has exponential 0, and the
+ *        triangular mask keeps the current and earlier positions, rows being
+ *        queries and columns keys.
+ *
+ *   Key padding (readings stated where the pages are silent):
+ *     key j is illegal for every query of sequence b when j >= len_b, with
+ *     len_b = clamp(key_lengths[b], 0, Lk) (Lk when key_lengths is NULL);
+ *     causal masking is top-left aligned: key j is illegal for query i when j > i;
+ *     a row whose every key is illegal has output 0 and all weights 0.
+ *
+ *   Softmax: exponentials divided by their sum (page "Arquitectura Transformer",
+ *     "Cómo funciona").  The row maximum is subtracted before exponentiating;
+ *     softmax is unchanged by a common shift of its inputs (page
+ *     "Self-Attention คืออะไร (แบบจับต้องได้)", section on dividing by sqrt(d_k):
+ *     [100,100,100] splits exactly like [0,0,0]).
+ *
+ * Layout: Q [B,H,Lq,d_k], K [B,H,Lk,d_k], V [B,H,Lk,d_v], O [B,H,Lq,d_v],
+ * all fp64, contiguous, row-major.  Heads and batch entries are independent
+ * (§3.2.2: the h heads run in parallel).
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math: IEEE semantics are
+ * relied upon for exp(-inf) == 0).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Is key j a legal connection for query i of a sequence with len keys? */
+static int is_legal(int64_t i, int64_t j, int64_t len, int causal)
+{
+    if (j >= len) return 0;             /* key padding */
+    if (causal && j > i) return 0;      /* future position */
+    return 1;
+}
+
+static int64_t clamp_len(const int32_t *key_lengths, int64_t b, int64_t Lk)
+{
+    if (!key_lengths) return Lk;
+    int64_t l = key_lengths[b];
+    if (l < 0) l = 0;
+    if (l > Lk) l = Lk;
+    return l;
+}
+
+/*
+ * One query row: q[d_k] against K[Lk][d_k], V[Lk][d_v].
+ *   s[j]  = (q . k_j) / sqrt(d_k), or -inf if illegal     (Eq. 1, §3.2.3)
+ *   w[j]  = exp(s[j] - max_j s[j])                        (softmax numerator)
+ *   p[j]  = w[j] / sum_j w[j]                             (weights, sum to 1)
+ *   o[t]  = sum_j p[j] * V[j][t]                          (weighted sum of values)
+ * s and w are caller-provided scratch of length Lk.  p_out (length Lk) and lse
+ * (log of the softmax denominator of the scaled scores, m + log Z) are optional.
+ */
+static void attention_row(const double *q, const double *K, const double *V,
+                          int64_t Lk, int64_t d_k, int64_t d_v, int64_t len,
+                          int causal, int64_t i, double *s, double *w,
+                          double *o, double *p_out, double *lse)
+{
+    const double root_dk = sqrt((double)d_k);
+    for (int64_t j = 0; j < Lk; ++j) {
+        if (!is_legal(i, j, len, causal)) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        const double *k = K + j * d_k;
+        double dot = 0.0;
+        for (int64_t t = 0; t < d_k; ++t) dot += q[t] * k[t];
+        s[j] = dot / root_dk;
+    }
+
+    double m = -INFINITY;
+    for (int64_t j = 0; j < Lk; ++j)
+        if (s[j] > m) m = s[j];
+
+    if (m == -INFINITY) {               /* no legal key: empty weighted sum */
+        for (int64_t t = 0; t < d_v; ++t) o[t] = 0.0;
+        if (p_out) for (int64_t j = 0; j < Lk; ++j) p_out[j] = 0.0;
+        if (lse) *lse = -INFINITY;
+        return;
+    }
+
+    double Z = 0.0;
+    for (int64_t j = 0; j < Lk; ++j) {
+        w[j] = exp(s[j] - m);           /* exp(-inf) == 0 exactly */
+        Z += w[j];
+    }
+    for (int64_t j = 0; j < Lk; ++j) w[j] = w[j] / Z;   /* w now holds p */
+
+    for (int64_t t = 0; t < d_v; ++t) o[t] = 0.0;
+    for (int64_t j = 0; j < Lk; ++j) {
+        const double pj = w[j];
+        const double *v = V + j * d_v;
+        for (int64_t t = 0; t < d_v; ++t) o[t] += pj * v[t];
+    }
+    if (p_out) memcpy(p_out, w, (size_t)Lk * sizeof(double));
+    if (lse) *lse = m + log(Z);
+}
+
+static int bad_shape(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_k, int64_t d_v)
+{
+    return B < 0 || H < 0 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1;
+}
+
+/*
+ * Full attention over every (b, head, i).
+ *   O   [B,H,Lq,d_v]  required
+ *   P   [B,H,Lq,Lk]   optional (NULL): the softmax weights
+ *   LSE [B,H,Lq]      optional (NULL)
+ * Returns 0 on success, 1 on a bad shape, 2 on allocation failure.
+ */
+int oracle_attention(const double *Q, const double *K, const double *V,
+                     const int32_t *key_lengths, int causal,
+                     int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                     int64_t d_k, int64_t d_v,
+                     double *O, double *P, double *LSE, int nthreads)
+{
+    if (bad_shape(B, H, Lq, Lk, d_k, d_v)) return 1;
+    const int64_t nrows = B * H * Lq;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *s = (double *)malloc((size_t)(Lk > 0 ? Lk : 1) * sizeof(double));
+        double *w = (double *)malloc((size_t)(Lk > 0 ? Lk : 1) * sizeof(double));
+        if (!s || !w) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < nrows; ++r) {
+                const int64_t i = r % Lq;
+                const int64_t bh = r / Lq;
+                const int64_t b = bh / H;
+                const double *Kh = K + bh * Lk * d_k;
+                const double *Vh = V + bh * Lk * d_v;
+                attention_row(Q + r * d_k, Kh, Vh, Lk, d_k, d_v,
+                              clamp_len(key_lengths, b, Lk), causal, i, s, w,
+                              O + r * d_v, P ? P + r * Lk : NULL,
+                              LSE ? LSE + r : NULL);
+            }
+        }
+        free(s);
+        free(w);
+    }
+    return failed ? 2 : 0;
+}
+
+/*
+ * Attention for a chosen set of rows only.  rows[n] is the flat row index
+ * (b*H + head)*Lq + i.  O_rows is [nrows, d_v]; LSE_rows is optional [nrows].
+ * Same definition as oracle_attention, row by row.
+ */
+int oracle_attention_rows(const double *Q, const double *K, const double *V,
+                          const int32_t *key_lengths, int causal,
+                          int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                          int64_t d_k, int64_t d_v,
+                          const int64_t *rows, int64_t nrows,
+                          double *O_rows, double *LSE_rows, int nthreads)
+{
+    if (bad_shape(B, H, Lq, Lk, d_k, d_v)) return 1;
+    for (int64_t n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= B * H * Lq) return 1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *s = (double *)malloc((size_t)(Lk > 0 ? Lk : 1) * sizeof(double));
+        double *w = (double *)malloc((size_t)(Lk > 0 ? Lk : 1) * sizeof(double));
+        if (!s || !w) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t n = 0; n < nrows; ++n) {
+                const int64_t r = rows[n];
+                const int64_t i = r % Lq;
+                const int64_t bh = r / Lq;
+                const int64_t b = bh / H;
+                attention_row(Q + r * d_k, K + bh * Lk * d_k, V + bh * Lk * d_v,
+                              Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, i,
+                              s, w, O_rows + n * d_v, NULL,
+                              LSE_rows ? LSE_rows + n : NULL);
+            }
+        }
+        free(s);
+        free(w);
+    }
+    return failed ? 2 : 0;
+}

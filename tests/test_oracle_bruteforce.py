@@ -1,0 +1,31 @@
+"""Exhaustive tiny cases: the oracle against the pure-Python brute force.
+
+Covers every key length 0..Lk (plus one beyond each end), both mask modes,
+Lq < Lk, Lq = Lk and Lq > Lk, and d_k != d_v.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import bruteforce
+import oracle
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (1, 4), (3, 2), (4, 4), (6, 5), (2, 6)])
+@pytest.mark.parametrize("dk,dv", [(1, 1), (3, 2), (4, 4)])
+def test_exhaustive_tiny(Lq, Lk, dk, dv):
+    rng = np.random.default_rng(1000 * Lq + 100 * Lk + 10 * dk + dv)
+    B, H = 2, 2
+    q = rng.standard_normal((B, H, Lq, dk))
+    k = rng.standard_normal((B, H, Lk, dk))
+    v = rng.standard_normal((B, H, Lk, dv))
+    lengths = list(range(-1, Lk + 2))
+    for causal, (l0, l1) in itertools.product((False, True), zip(lengths, reversed(lengths))):
+        kl = [l0, l1]
+        got = oracle.attention(q, k, v, key_lengths=kl, causal=causal)
+        ref = np.array(bruteforce.attention(q, k, v, kl, causal))
+        assert np.max(np.abs(got - ref)) <= 1e-12, (causal, kl)
+    got = oracle.attention(q, k, v, causal=True)
+    ref = np.array(bruteforce.attention(q, k, v, None, True))
+    assert np.max(np.abs(got - ref)) <= 1e-12

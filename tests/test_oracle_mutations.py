@@ -1,0 +1,67 @@
+"""Plant plausible mistakes in the oracle's C source and check the pins catch them.
+
+Each mutant is a copy of oracle/sdpa_oracle.c with one textual change (a dropped
+term, a wrong sign, a wrong index or an off-by-one in a mask), compiled with gcc
+into a temporary library.  The pin battery of ``pins.py`` must pass on the real
+oracle and fail on every mutant.  Nothing here touches the GPU.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTATIONS = {
+    "scale_dropped": ("s[j] = dot / root_dk;", "s[j] = dot;"),
+    "scale_by_dk": ("const double root_dk = sqrt((double)d_k);",
+                    "const double root_dk = (double)d_k;"),
+    "scale_by_dv": ("const double root_dk = sqrt((double)d_k);",
+                    "const double root_dk = sqrt((double)d_v);"),
+    "causal_diagonal_excluded": ("if (causal && j > i) return 0;",
+                                 "if (causal && j >= i) return 0;"),
+    "causal_reversed": ("if (causal && j > i) return 0;", "if (causal && j < i) return 0;"),
+    "padding_off_by_one": ("if (j >= len) return 0;", "if (j > len) return 0;"),
+    "exp_sign": ("w[j] = exp(s[j] - m);", "w[j] = exp(m - s[j]);"),
+    "not_normalised": ("w[j] = w[j] / Z;", "w[j] = w[j];"),
+    "max_reversed": ("if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
+    "dot_wrong_index": ("dot += q[t] * k[t];", "dot += q[t] * k[0];"),
+    "key_stride_dv": ("const double *k = K + j * d_k;", "const double *k = K + j * d_v;"),
+    "value_wrong_column": ("o[t] += pj * v[t];", "o[t] += pj * v[0];"),
+    "value_head_zero": ("const double *Vh = V + bh * Lk * d_v;",
+                        "const double *Vh = V + b * H * Lk * d_v;"),
+    "key_head_zero": ("const double *Kh = K + bh * Lk * d_k;",
+                      "const double *Kh = K + b * H * Lk * d_k;"),
+    "query_row_zero": ("attention_row(Q + r * d_k, Kh, Vh,", "attention_row(Q + bh * Lq * d_k, Kh, Vh,"),
+    "empty_row_nan": ("for (int64_t t = 0; t < d_v; ++t) o[t] = 0.0;\n        if (p_out)",
+                      "for (int64_t t = 0; t < d_v; ++t) o[t] = NAN;\n        if (p_out)"),
+    "lse_without_max": ("if (lse) *lse = m + log(Z);", "if (lse) *lse = log(Z);"),
+    "rows_api_causal_dropped": ("Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, i,",
+                                "Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), 0, i,"),
+}
+
+
+def _run_battery(orc):
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except (AssertionError, RuntimeError, ValueError, FloatingPointError) as e:
+            failed.append((check.__name__, str(e)[:120]))
+    return failed
+
+
+def test_real_oracle_passes_battery():
+    assert _run_battery(oracle.default()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(oracle.SOURCE, encoding="utf-8").read()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: %r" % old
+    path = tmp_path / ("mutant_%s.c" % name)
+    path.write_text(src.replace(old, new), encoding="utf-8")
+    lib = oracle.compile_oracle(str(path), str(tmp_path / ("libmutant_%s.so" % name)))
+    failed = _run_battery(oracle.Oracle(lib))
+    assert failed, "mutant %s passed every pin" % name

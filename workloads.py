@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for multi-head scaled dot-product attention.
+
+This module is the only code shared by the CPU oracle (``oracle/``) and the HIP
+path (``head_attention_fwd_amd/``).  It draws random numbers and rounds them to
+the storage type; it performs none of the attention arithmetic.
+
+Shapes follow the base and big models of "Attention Is All You Need"
+(page "Attention Is All You Need/paper/es", §3.2.2: h = 8 heads with
+d_k = d_v = d_model / h = 64 for d_model = 512; Table 3, row "big": d_model =
+1024, h = 16).  The pages train on length-bucketed batches (§5.1), so the
+key-padding configurations draw one key length per sequence.
+
+Recipe (identical for every configuration):
+  rng = numpy.random.Generator(numpy.random.PCG64(seed))
+  Q, K, V = rng.standard_normal(shape) each, in that order, as float64,
+            multiplied by ``scale`` (0.5 for the long causal case), rounded to
+            float32 (round to nearest even), then, for bf16 configurations,
+            rounded again to bfloat16 (round to nearest even);
+  key_lengths = rng.integers(lo, hi, size=B, endpoint=True) as int32, drawn
+            after V, only for configurations with key padding.
+All arrays are returned as float32 numpy arrays whose values are exactly
+representable in the configuration's storage type.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    description: str
+    dtype: str            # "f32" or "bf16": storage and arithmetic type of the GPU path
+    B: int
+    H: int
+    Lq: int
+    Lk: int
+    d_k: int
+    d_v: int
+    causal: bool
+    key_len_range: Optional[tuple]   # inclusive (lo, hi) or None for "no padding"
+    scale: float
+    seed: int
+
+
+CONFIGS = {
+    "tiny_causal_f32": Config(
+        "tiny_causal_f32", "tiny causal self-attention, fp32", "f32",
+        B=2, H=2, Lq=16, Lk=16, d_k=8, d_v=8, causal=True, key_len_range=None,
+        scale=1.0, seed=0),
+    "base_encoder_bf16": Config(
+        "base_encoder_bf16", "base-model encoder self-attention with key padding", "bf16",
+        B=64, H=8, Lq=256, Lk=256, d_k=64, d_v=64, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=1),
+    "base_decoder_causal_bf16": Config(
+        "base_decoder_causal_bf16", "base-model decoder causal self-attention with key padding",
+        "bf16", B=64, H=8, Lq=256, Lk=256, d_k=64, d_v=64, causal=True,
+        key_len_range=(64, 256), scale=1.0, seed=2),
+    "big_cross_bf16": Config(
+        "big_cross_bf16", "big-model encoder-decoder cross-attention with encoder padding",
+        "bf16", B=32, H=16, Lq=256, Lk=320, d_k=64, d_v=64, causal=False,
+        key_len_range=(128, 320), scale=1.0, seed=3),
+    "long_causal_bf16": Config(
+        "long_causal_bf16", "long-sequence causal self-attention, inputs scaled by 0.5", "bf16",
+        B=4, H=16, Lq=8192, Lk=8192, d_k=64, d_v=64, causal=True, key_len_range=None,
+        scale=0.5, seed=4),
+}
+
+#: Configuration order used by tests and reports (smallest first).
+ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
+         "big_cross_bf16", "long_causal_bf16"]
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32.
+
+    Inputs must be finite.  bfloat16 is the upper 16 bits of an IEEE float32.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    bits = (bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16) << np.uint64(16)
+    return bits.astype(np.uint32).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    config: Config
+    q: np.ndarray                       # [B, H, Lq, d_k] float32
+    k: np.ndarray                       # [B, H, Lk, d_k] float32
+    v: np.ndarray                       # [B, H, Lk, d_v] float32
+    key_lengths: Optional[np.ndarray]   # [B] int32 or None
+
+
+def draw(B: int, H: int, Lq: int, Lk: int, d_k: int, d_v: int, *, dtype: str = "bf16",
+         seed: int = 0, scale: float = 1.0, key_len_range: Optional[tuple] = None):
+    """Draw (q, k, v, key_lengths) with the module's recipe for any shape."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def one(shape):
+        a = rng.standard_normal(shape)
+        if scale != 1.0:
+            a = a * scale
+        a = a.astype(np.float32)
+        return round_to_bf16(a) if dtype == "bf16" else a
+
+    q = one((B, H, Lq, d_k))
+    k = one((B, H, Lk, d_k))
+    v = one((B, H, Lk, d_v))
+    kl = None
+    if key_len_range is not None:
+        lo, hi = key_len_range
+        kl = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    return q, k, v, kl
+
+
+def generate(name: str) -> Inputs:
+    """Inputs for one named configuration."""
+    c = CONFIGS[name]
+    q, k, v, kl = draw(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dtype=c.dtype, seed=c.seed,
+                       scale=c.scale, key_len_range=c.key_len_range)
+    return Inputs(c, q, k, v, kl)

@@ -1,0 +1,225 @@
+"""Benchmark of libsdpa's attention forward on one MI355X.
+
+One step = one sdpa_forward call over the whole workload (one kernel launch),
+inputs resident in HBM.  Prints ONE JSON line (see the keys below).
+
+Default workload: the long-sequence causal self-attention, B=4, h=16,
+Lq=Lk=8192, d_k=d_v=64, bf16, inputs N(0,1)*0.5 -- the configuration on which
+the fraction of bf16 matrix-core peak is the figure of merit.  Other named
+workloads (--config) are available for profiling; they are parity cases, not
+headline lines.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                  [--no-cpu-baseline] [--rotate R]
+
+FLOPs are algorithmic: (2*d_k + 2*d_v) per (query, key) pair the mask allows
+(page "Attention Is All You Need/paper/es", §4, Table 1: O(n^2 d) per layer),
+counted exactly from the drawn key lengths.  Bytes are algorithmic too: Q and
+O once, each key/value row a query may use once.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+from head_attention_fwd_amd import perfmodel  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak (h=8/16, d_k=64) on 1 MI355X"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense peaks (matrix bf16; fp32 vector)
+PEAK_HBM_GBS = 8000.0
+DEFAULT_CONFIG = "long_causal_bf16"
+KERNEL_SOURCES = ["head_attention_fwd_amd/csrc/sdpa_fwd_mfma_d64.hip",
+                  "head_attention_fwd_amd/csrc/sdpa_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(config_name)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(x, target_seconds=15.0):
+    """The fp64 oracle, as it is, on a bounded random sample of the workload's rows.
+
+    Rows (b, h, i) are drawn uniformly, so FLOPs/s on the sample estimate the
+    oracle's throughput on the whole workload.  Runs on the host cores only.
+    """
+    import oracle
+
+    c = x.config
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(1234)
+
+    def sample(n):
+        return np.stack([rng.integers(0, c.B, n), rng.integers(0, c.H, n),
+                         rng.integers(0, c.Lq, n)], axis=1)
+
+    def row_flops(rows):
+        tot = 0
+        for b, h, i in rows:
+            lb = c.Lk if x.key_lengths is None else perfmodel.clamp_length(x.key_lengths[b], c.Lk)
+            n = min(lb, i + 1) if c.causal else lb
+            tot += (2 * c.d_k + 2 * c.d_v) * n
+        return tot
+
+    oracle.default()   # build/load outside the timed region
+    # fp64 copies made once, outside the timed region (the oracle's input type)
+    q64, k64, v64 = (np.ascontiguousarray(a, dtype=np.float64) for a in (x.q, x.k, x.v))
+    # calibrate on growing samples (small ones are dominated by fixed costs), then
+    # size the measured sample for about target_seconds of oracle work
+    n = max(threads * 4, 64)
+    for budget in (0.5, 2.0, target_seconds):
+        rows = sample(n)
+        t0 = time.perf_counter()
+        oracle.attention_rows(q64, k64, v64, rows, key_lengths=x.key_lengths, causal=c.causal,
+                              nthreads=threads)
+        dt = time.perf_counter() - t0
+        if budget == target_seconds:
+            break
+        nxt = 2.0 if budget == 0.5 else target_seconds
+        n = int(n * max(1.0, nxt / max(dt, 1e-3)))
+        n = max(64, min(n, c.B * c.H * c.Lq))
+    f = row_flops(rows)
+    del q64, k64, v64
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d uniformly drawn query rows (%.3g of the workload's FLOPs, %.1f s), "
+                      "fp64 C oracle with OpenMP" % (n, f / perfmodel.flops(
+                          c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths), dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets cycled through (0: enough for >= 1 GiB on HBM-bound "
+                         "workloads, 1 otherwise)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this attention forward has no multi-GPU "
+              "path (every (batch, head) is independent; sharding them needs no "
+              "communication). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_attention_fwd_amd as sdpa
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    x = workloads.generate(args.config)
+    c = x.config
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    flops = perfmodel.flops(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths)
+    nbytes = perfmodel.min_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
+                                 elem=2 if c.dtype == "bf16" else 4)
+    hbm_bound = flops / nbytes < (PEAK_TFLOPS[c.dtype] * 1e12) / (PEAK_HBM_GBS * 1e9)
+
+    rotate = args.rotate
+    if rotate <= 0:
+        rotate = max(1, -(-(1 << 30) // nbytes)) if hbm_bound else 1
+
+    def up(a):
+        return torch.from_numpy(a).to(tdt).to(dev)
+
+    sets = []
+    base = (up(x.q), up(x.k), up(x.v))
+    kl = None if x.key_lengths is None else torch.as_tensor(x.key_lengths).to(dev)
+    for r in range(rotate):
+        qkv = base if r == 0 else tuple(t.clone() for t in base)
+        out = torch.empty((c.B, c.H, c.Lq, c.d_v), dtype=tdt, device=dev)
+        sets.append((qkv, out))
+
+    def step(n):
+        (q, k, v), out = sets[n % rotate]
+        sdpa.forward(q, k, v, key_lengths=kl, causal=c.causal, out=out)
+
+    for n in range(args.warmup):
+        step(n)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()        # barrier (one rank) + synchronize
+    t0 = time.perf_counter()
+    for n in range(args.steps):
+        starts[n].record(stream)
+        step(n)
+        ends[n].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    window_ms = starts[0].elapsed_time(ends[-1])
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    ms_per_step = window_ms / args.steps
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved_tflops = flops / (kern_ms * 1e-3) / 1e12
+    achieved_gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.config)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_TFLOPS[c.dtype],
+                "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_TFLOPS[c.dtype],
+                "traffic": traffic}
+    roof["kernel"] = ("sdpa_fwd_mfma_d64_kernel" if (c.dtype == "bf16" and c.d_k == 64 and
+                                                      c.d_v == 64) else "sdpa_fwd_generic_kernel")
+    roof["algorithmic_flops"] = flops
+    roof["algorithmic_bytes"] = nbytes
+    roof["kernel_ms"] = kern_ms
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x)
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": c.name, "description": c.description, "B": c.B, "h": c.H,
+                   "Lq": c.Lq, "Lk": c.Lk, "d_k": c.d_k, "d_v": c.d_v, "causal": c.causal,
+                   "key_lengths": None if x.key_lengths is None else "U{%d..%d} seed %d" % (
+                       c.key_len_range[0], c.key_len_range[1], c.seed),
+                   "input_sets": rotate},
+        "frac_of_peak": value / PEAK_TFLOPS[c.dtype],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

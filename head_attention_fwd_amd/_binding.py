@@ -1,0 +1,132 @@
+"""ctypes binding of libsdpa (include/sdpa.h): argument marshalling only.
+
+Every step of the computation runs in the HIP kernels of libsdpa.so.  PyTorch
+tensors only provide device memory and the stream.  If libsdpa.so is missing
+or fails to load, every call raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libsdpa.so")
+
+SDPA_OK = 0
+SDPA_ERR_NULL_POINTER = 1
+SDPA_ERR_BAD_SHAPE = 2
+SDPA_ERR_UNSUPPORTED = 3
+SDPA_ERR_ALIAS = 4
+SDPA_ERR_HIP = 5
+
+SDPA_F32 = 0
+SDPA_BF16 = 1
+
+#: Symbols include/sdpa.h declares.
+EXPORTED = ("sdpa_forward", "sdpa_status_str", "sdpa_last_hip_error")
+
+_lib = None
+
+
+class SdpaError(RuntimeError):
+    """A non-zero sdpa_status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("sdpa_forward failed (%d): %s" % (status, message))
+        self.status = status
+
+
+def load_library(path: str = LIBRARY):
+    """Load libsdpa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libsdpa.so is not built (%s); run __graft_entry__.build() or "
+                           "python head_attention_fwd_amd/build.py" % path)
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.sdpa_forward.restype = ctypes.c_int
+    lib.sdpa_forward.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64,
+                                 i64, ctypes.c_int, vp]
+    lib.sdpa_status_str.restype = ctypes.c_char_p
+    lib.sdpa_status_str.argtypes = [ctypes.c_int]
+    lib.sdpa_last_hip_error.restype = ctypes.c_int
+    lib.sdpa_last_hip_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def sdpa_forward(Q: int, K: int, V: int, key_lengths: int, causal: int, out: int,
+                 B: int, H: int, Lq: int, Lk: int, d_k: int, d_v: int, dtype: int,
+                 stream: int) -> int:
+    """Raw C call; pointers and the stream are integers (0 = NULL).  Returns the status."""
+    return load_library().sdpa_forward(Q or None, K or None, V or None, key_lengths or None,
+                                       int(causal), out or None, B, H, Lq, Lk, d_k, d_v,
+                                       int(dtype), stream or None)
+
+
+def sdpa_status_str(status: int) -> str:
+    return load_library().sdpa_status_str(int(status)).decode()
+
+
+def sdpa_last_hip_error() -> int:
+    return load_library().sdpa_last_hip_error()
+
+
+def forward(q, k, v, key_lengths=None, causal: bool = False, out=None):
+    """Attention forward on torch CUDA tensors (HIP on ROCm).
+
+    q [B,H,Lq,d_k], k [B,H,Lk,d_k], v [B,H,Lk,d_v]: contiguous, one dtype
+    (torch.float32 or torch.bfloat16), one device.  key_lengths: None, or an
+    int32 tensor [B] on that device (other integer sequences are copied there).
+    out: optional preallocated contiguous [B,H,Lq,d_v] tensor of the same dtype.
+    The kernel is enqueued on the device's current stream; returns out.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, L, d]")
+    B, H, Lq, d_k = q.shape
+    Lk = k.shape[2]
+    d_v = v.shape[3]
+    if tuple(k.shape) != (B, H, Lk, d_k) or tuple(v.shape) != (B, H, Lk, d_v):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                             tuple(v.shape)))
+    if q.dtype == torch.bfloat16:
+        dtype = SDPA_BF16
+    elif q.dtype == torch.float32:
+        dtype = SDPA_F32
+    else:
+        raise TypeError("unsupported dtype %s" % q.dtype)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.device != dev:
+            raise ValueError("%s must match q in dtype and device" % name)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if key_lengths is not None and not isinstance(key_lengths, torch.Tensor):
+        key_lengths = torch.as_tensor(list(key_lengths), dtype=torch.int32, device=dev)
+    if key_lengths is not None:
+        if key_lengths.dtype != torch.int32 or key_lengths.device != dev or \
+                tuple(key_lengths.shape) != (B,) or not key_lengths.is_contiguous():
+            raise ValueError("key_lengths must be a contiguous int32 [B] tensor on q's device")
+    if out is None:
+        out = torch.empty((B, H, Lq, d_v), dtype=q.dtype, device=dev)
+    elif tuple(out.shape) != (B, H, Lq, d_v) or out.dtype != q.dtype or out.device != dev or \
+            not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,H,Lq,d_v] tensor like q")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          0 if key_lengths is None else key_lengths.data_ptr(), int(bool(causal)),
+                          out.data_ptr(), B, H, Lq, Lk, d_k, d_v, dtype, stream)
+    if st != SDPA_OK:
+        msg = sdpa_status_str(st)
+        if st == SDPA_ERR_HIP:
+            msg += " (hipError %d)" % sdpa_last_hip_error()
+        raise SdpaError(st, msg)
+    return out

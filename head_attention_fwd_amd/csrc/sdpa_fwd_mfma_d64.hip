@@ -1,0 +1,324 @@
+// Scaled dot-product attention forward for bf16 inputs with d_k = d_v = 64 on
+// the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+// What it computes: Eq. (1) of page "Attention Is All You Need/paper/es"
+// (§3.2.1), softmax(Q K^T / sqrt(d_k)) V per head (§3.2.2: d_k = d_v = 64 in
+// the base and big models), with -inf for illegal connections before the
+// softmax (§3.2.3): keys j >= len_b (padding) and, when causal, keys j > i.
+// Both products are dense contractions ("highly optimised matrix multiplication
+// code", §3.2.1), so they run on the matrix cores; the Lq x Lk score matrix
+// never leaves registers.
+//
+// Design (one workgroup = NW waves = 32*NW query rows of one (b, h)):
+//
+//  * Scores are formed transposed, S^T = K Q^T, one 32x32 block per MFMA
+//    chain: A = 32 keys x 16 dims (from LDS), B = 16 dims x 32 queries (the
+//    wave's Q rows, loaded once into registers).  In the accumulator layout a
+//    lane then holds 16 scores of ONE query (lane % 32), and the other half of
+//    the wave holds the other 16 keys of the same query.  The row maximum is an
+//    in-lane reduction plus one exchange with lane ^ 32; the row sum needs no
+//    exchange until the epilogue.
+//  * The weights P^T (bf16) are exactly the B operand of the second product,
+//    O^T += V^T P^T (A = 32 dims x 16 keys from LDS): no LDS round trip for P.
+//    For that the 32 key rows of a score block are fed to the first MFMA in
+//    the order pi(m) = m with bits 2 and 3 swapped; then lane half g of the
+//    accumulator holds, in registers r = 8h..8h+7, the 8 consecutive keys
+//    16h + 8g + (r % 8), which is what the second MFMA expects of its B operand.
+//  * The output accumulator O^T also holds one query per lane, so the online
+//    rescaling factor exp(m_old - m_new) is a per-lane scalar.
+//  * K is staged in LDS row-major (rows stored in pi order), V transposed
+//    (rows = dims), both with 16-byte chunks XOR-swizzled by the row so that the
+//    16-byte operand reads of a wave are free of bank conflicts.  Two LDS
+//    buffers: tile t+1 is fetched from HBM into registers while tile t is
+//    multiplied, one barrier per tile.
+//  * Softmax in base 2: p = exp2(s * log2(e)/sqrt(d_k) - m), with m tracked in
+//    the same scaled units; exp2 is v_exp_f32.  Masks are applied only in tiles
+//    that cross the causal diagonal or the padding boundary; tiles entirely
+//    above a wave's diagonal are skipped by that wave, and tiles entirely
+//    beyond the key length are never loaded.
+//  * Causal grids are issued longest-first (last query tile first) so the
+//    triangle's long tiles do not finish last.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sdpa_kernels.h"
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 64;       // d_k = d_v
+constexpr int kBN = 64;      // keys per tile
+constexpr int kTileElems = kBN * kD;  // bf16 elements per K (or V^T) tile
+
+// 16-byte chunk swizzle: rows r and r' that a wave reads in the same LDS cycle
+// get different chunk positions (injective on any 8 consecutive rows and on the
+// 8 even or 8 odd rows of any 16 consecutive rows).
+__device__ inline int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Key row order fed to the score MFMA: swap bits 2 and 3 (an involution).
+__device__ inline int pi32(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32, nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ inline f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NW>
+struct TileLoader {
+    static constexpr int kThreads = NW * 64;
+    // K: 64 rows x 8 chunks of 16 B; V: 32 key pairs x 8 dim-chunks.
+    static constexpr int kKChunks = (kBN * 8 + kThreads - 1) / kThreads;
+    static constexpr int kVTasks = (kBN / 2 * 8 + kThreads - 1) / kThreads;
+    u32x4_t k[kKChunks];
+    u32x4_t v0[kVTasks], v1[kVTasks];
+
+    // Global -> registers.  Rows at or beyond `valid` (the key length) load as
+    // zero, so the contents of padded rows never enter the arithmetic.
+    __device__ inline void fetch(const uint16_t *Kh, const uint16_t *Vh, int64_t kv0,
+                                 int64_t valid, int tid)
+    {
+#pragma unroll
+        for (int it = 0; it < kKChunks; ++it) {
+            const int ci = tid + it * kThreads;
+            const int r = ci >> 3, c = ci & 7;
+            const int64_t row = kv0 + r;
+            k[it] = (u32x4_t){0u, 0u, 0u, 0u};
+            if (ci < kBN * 8 && row < valid)
+                k[it] = *(const u32x4_t *)(Kh + row * kD + c * 8);
+        }
+#pragma unroll
+        for (int it = 0; it < kVTasks; ++it) {
+            const int ti = tid + it * kThreads;
+            const int p = ti & 31, c = ti >> 5;
+            const int64_t row = kv0 + 2 * p;
+            v0[it] = (u32x4_t){0u, 0u, 0u, 0u};
+            v1[it] = (u32x4_t){0u, 0u, 0u, 0u};
+            if (ti < kBN / 2 * 8) {
+                if (row < valid) v0[it] = *(const u32x4_t *)(Vh + row * kD + c * 8);
+                if (row + 1 < valid) v1[it] = *(const u32x4_t *)(Vh + (row + 1) * kD + c * 8);
+            }
+        }
+    }
+
+    // Registers -> LDS.  K row r goes to LDS row pi(r) (within its 32-row
+    // block); V is written transposed: dim d's row holds the tile's 64 keys.
+    __device__ inline void store(uint16_t *Ks, uint16_t *Vt, int tid) const
+    {
+#pragma unroll
+        for (int it = 0; it < kKChunks; ++it) {
+            const int ci = tid + it * kThreads;
+            if (ci < kBN * 8) {
+                const int r = ci >> 3, c = ci & 7;
+                const int pos = (r & 32) | pi32(r & 31);
+                *(u32x4_t *)(Ks + pos * kD + ((c ^ swz(pos)) << 3)) = k[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < kVTasks; ++it) {
+            const int ti = tid + it * kThreads;
+            if (ti < kBN / 2 * 8) {
+                const int p = ti & 31, c = ti >> 5;
+                // keys 2p, 2p+1 -> 32-bit word (p % 4) of chunk p / 4 of row d
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int d = c * 8 + e;
+                    const uint32_t a = v0[it][e >> 1], b = v1[it][e >> 1];
+                    const uint32_t w = (e & 1) ? ((a >> 16) | (b & 0xFFFF0000u))
+                                               : ((a & 0xFFFFu) | (b << 16));
+                    *(uint32_t *)(Vt + d * kBN + (((p >> 2) ^ swz(d)) << 3) + ((p & 3) << 1)) = w;
+                }
+            }
+        }
+    }
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
+    uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
+    uint32_t n_qtiles, uint32_t n_bh)
+{
+    constexpr int BM = 32 * NW;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileElems];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 5;      // lane half
+    const int l32 = lane & 31;
+
+    // Work item: head-major within a query-tile index; causal grids run the
+    // longest (last) query tiles first.
+    const uint32_t bh = blockIdx.x % n_bh;
+    uint32_t qt = blockIdx.x / n_bh;
+    if (causal) qt = n_qtiles - 1 - qt;
+    const int64_t b = bh / H;
+    const int64_t q0 = (int64_t)qt * BM;
+    const int64_t q0w = q0 + 32 * wave;        // first query row of this wave
+    const int64_t qrow = q0w + l32;             // this lane's query row
+
+    int64_t len = Lk;
+    if (key_lengths) {
+        const int64_t l = key_lengths[b];
+        len = l < 0 ? 0 : (l > Lk ? Lk : l);
+    }
+    int64_t kv_end = len;                        // keys the workgroup needs
+    if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
+    const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
+
+    const uint16_t *Kh = K + (int64_t)bh * Lk * kD;
+    const uint16_t *Vh = V + (int64_t)bh * Lk * kD;
+
+    // Q^T as the B operand of the score MFMA: lane holds query qrow, dims
+    // 16*kb + 8*g .. +7 for kb = 0..3.
+    bf16x8_t qf[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        u32x4_t t = {0u, 0u, 0u, 0u};
+        if (qrow < Lq) t = *(const u32x4_t *)(Q + ((int64_t)bh * Lq + qrow) * kD + kb * 16 + g * 8);
+        qf[kb] = as_bf16x8(t);
+    }
+
+    f32x16_t acc[2];                 // O^T: dims 32*blk + 8*(r/4) + 4*g + r%4, query qrow
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
+    float m_run = -INFINITY;         // running max of scaled scores (log2 units)
+    float l_run = 0.f;               // this lane's part of the running sum
+
+    TileLoader<NW> ld;
+    if (n_tiles > 0) ld.fetch(Kh, Vh, 0, len, tid);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        uint16_t *Ks = lds[t & 1][0];
+        uint16_t *Vt = lds[t & 1][1];
+        ld.store(Ks, Vt, tid);
+        __syncthreads();
+        const int64_t kv0 = (int64_t)t * kBN;
+        if (t + 1 < n_tiles) ld.fetch(Kh, Vh, kv0 + kBN, len, tid);
+
+        // A wave whose rows all precede the tile's first key has nothing to do.
+        if (causal && kv0 > q0w + 31) continue;
+
+        // ---- S^T = K Q^T for the tile's two 32-key blocks
+        f32x16_t s[2];
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
+            const int pos = bk * 32 + l32;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const u32x4_t a = *(const u32x4_t *)(Ks + pos * kD + (((2 * kb + g) ^ swz(pos)) << 3));
+                s[bk] = mfma32(as_bf16x8(a), qf[kb], s[bk]);
+            }
+        }
+
+        // ---- mask (only where the tile crosses the diagonal or the padding end)
+        const bool need_mask = (kv0 + kBN > len) || (causal && kv0 + kBN - 1 > q0w);
+        if (need_mask) {
+#pragma unroll
+            for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t key = kv0 + 32 * bk + 16 * (r >> 3) + 8 * g + (r & 7);
+                    if (key >= len || (causal && key > qrow)) s[bk][r] = -INFINITY;
+                }
+        }
+
+        // ---- online softmax (base 2)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bk][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * scale_log2);
+        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;   // all -inf so far
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+        m_run = m_new;
+
+        bf16x8_t pf[4];              // P^T B operands, k-block kk = 2*bk + (r / 8)
+        float psum = 0.f;
+#pragma unroll
+        for (int bk = 0; bk < 2; ++bk) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4_t w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i], scale_log2, -m_ref));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i + 1], scale_log2, -m_ref));
+                    psum += p0 + p1;
+                    w[i] = pack_bf16x2(p0, p1);
+                }
+                pf[2 * bk + h] = as_bf16x8(w);
+            }
+        }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { acc[0][i] *= alpha; acc[1][i] *= alpha; }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                const int d = db * 32 + l32;
+                const u32x4_t a = *(const u32x4_t *)(Vt + d * kBN + (((2 * kk + g) ^ swz(d)) << 3));
+                acc[db] = mfma32(as_bf16x8(a), pf[kk], acc[db]);
+            }
+        }
+    }
+
+    // ---- epilogue: O = acc / l, rounded to bf16
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
+    if (qrow < Lq) {
+        uint16_t *o = O + ((int64_t)bh * Lq + qrow) * kD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                u32x2_t w;
+                w[0] = pack_bf16x2(acc[db][4 * rq + 0] * inv, acc[db][4 * rq + 1] * inv);
+                w[1] = pack_bf16x2(acc[db][4 * rq + 2] * inv, acc[db][4 * rq + 3] * inv);
+                *(u32x2_t *)(o + db * 32 + rq * 8 + g * 4) = w;
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_d64(const void *Q, const void *K, const void *V,
+                           const int32_t *key_lengths, int causal, void *out,
+                           int64_t B, int64_t H, int64_t Lq, int64_t Lk, hipStream_t stream)
+{
+    constexpr int NW = 4;
+    constexpr int BM = 32 * NW;
+    const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
+    const uint32_t n_bh = (uint32_t)(B * H);
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
+    hipLaunchKernelGGL((sdpa_fwd_mfma_d64_kernel<NW>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0,
+                       stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                       key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2,
+                       n_qtiles, n_bh);
+    return hipGetLastError();
+}
+
+}  // namespace sdpa

@@ -1,0 +1,26 @@
+// Internal launchers of libsdpa's kernels.  Not part of the public C ABI.
+//
+// Every launcher assumes the host layer has validated its arguments: non-null
+// pointers, sizes >= 1, B*H and the grid within the hardware limits, and the
+// head dimensions within the kernel's compiled bounds.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+// Any 1 <= d_k, d_v <= 128; elements are fp32 (is_bf16 = false) or bf16.
+// fp32 arithmetic throughout; one lane per query row.
+hipError_t launch_generic(const void *Q, const void *K, const void *V,
+                          const int32_t *key_lengths, int causal, void *out,
+                          int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                          int d_k, int d_v, bool is_bf16, hipStream_t stream);
+
+// bf16, d_k = d_v = 64, on the matrix cores.
+hipError_t launch_mfma_d64(const void *Q, const void *K, const void *V,
+                           const int32_t *key_lengths, int causal, void *out,
+                           int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                           hipStream_t stream);
+
+}  // namespace sdpa

@@ -1,0 +1,102 @@
+/*
+ * sdpa.h -- C ABI of libsdpa: multi-head scaled dot-product attention, forward
+ * pass, on an AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Attention Is All You Need/paper/es", §3.2.1, Eq. (1);
+ * §3.2.2 for the h heads; §3.2.3 for the mask):
+ *
+ *   out[b,h,i,:] = sum_j P[b,h,i,j] * V[b,h,j,:]
+ *   P[b,h,i,:]   = softmax_j( Q[b,h,i,:] . K[b,h,j,:] / sqrt(d_k)  +  M[b,i,j] )
+ *
+ * with M[b,i,j] = -inf for an illegal connection and 0 otherwise.  Key j is
+ * illegal for query i of batch entry b when
+ *   j >= len_b            (key padding; len_b = clamp(key_lengths[b], 0, Lk),
+ *                          or Lk when key_lengths is NULL), or
+ *   causal && j > i       (a decoder position may use the positions up to and
+ *                          including its own, §3.2.3; top-left aligned when
+ *                          Lq != Lk).
+ * A query row with no legal key gets out = 0.  The scale 1/sqrt(d_k) is fixed
+ * by the method and is not a parameter.  There is no dropout in this pass.
+ *
+ * Uses covered by the same call (§3.2.3): encoder self-attention (causal = 0,
+ * Lq = Lk), decoder causal self-attention (causal = 1), encoder-decoder
+ * cross-attention (queries from the decoder, Lq != Lk allowed, key_lengths for
+ * the encoder's padding).
+ *
+ * Layout.  Q [B,H,Lq,d_k], K [B,H,Lk,d_k], V [B,H,Lk,d_v], out [B,H,Lq,d_v]:
+ * device pointers to contiguous row-major arrays of the element type `dtype`
+ * (the same type for all four).  key_lengths: device pointer to int32[B], or
+ * NULL.  Offsets are computed in 64 bits.
+ *
+ * Arithmetic.  SDPA_BF16: bf16 inputs, bf16 matrix-core products with fp32
+ * accumulation, fp32 softmax, the weights rounded to bf16 (nearest even)
+ * before the product with V, output rounded to bf16 (nearest even).
+ * SDPA_F32: fp32 throughout.  Results are deterministic run to run.
+ *
+ * Supported sizes.  SDPA_BF16: 1 <= d_k, d_v <= 128 (d_k = d_v = 64 runs on the
+ * matrix cores).  SDPA_F32: 1 <= d_k, d_v <= 128.  B*H <= 2^31 - 1,
+ * Lq, Lk <= 2^31 - 1.  B, H, Lq or Lk equal to 0 is an empty call (SDPA_OK,
+ * nothing launched).
+ *
+ * Ownership and concurrency.  The caller owns every buffer; the library
+ * allocates and frees nothing, keeps no per-call state and never synchronises.
+ * The call enqueues its kernel on `stream` (a hipStream_t; NULL is the null
+ * stream) and returns; the output is valid once that stream reaches the
+ * kernel.  `out` must not overlap Q, K, V or key_lengths.
+ *
+ * Errors.  No exception crosses this interface.  Argument errors are detected
+ * on the host before any HIP call and leave `out` untouched.  key_lengths
+ * values live on the device and are not checked on the host: the kernel
+ * clamps them to [0, Lk].
+ */
+#ifndef SDPA_H_
+#define SDPA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sdpa_status {
+    SDPA_OK = 0,
+    SDPA_ERR_NULL_POINTER = 1,   /* Q, K, V or out is NULL (with a non-empty shape) */
+    SDPA_ERR_BAD_SHAPE = 2,      /* a size is negative, or a product overflows the limits */
+    SDPA_ERR_UNSUPPORTED = 3,    /* (dtype, d_k, d_v) combination not built */
+    SDPA_ERR_ALIAS = 4,          /* out overlaps Q, K, V or key_lengths */
+    SDPA_ERR_HIP = 5             /* a HIP call failed; see sdpa_last_hip_error() */
+} sdpa_status;
+
+typedef enum sdpa_dtype {
+    SDPA_F32 = 0,
+    SDPA_BF16 = 1
+} sdpa_dtype;
+
+/*
+ * Attention forward (Eq. (1) with the mask above) over B batch entries and H
+ * heads.  Arguments:
+ *   Q, K, V      device inputs, layouts above;
+ *   key_lengths  device int32[B] key lengths, or NULL for "all Lk keys";
+ *   causal       0: no causal mask; nonzero: key j illegal for query i if j > i;
+ *   out          device output [B,H,Lq,d_v], written completely;
+ *   B, H, Lq, Lk, d_k, d_v   sizes;
+ *   dtype        element type of Q, K, V and out;
+ *   stream       hipStream_t to launch on (NULL = null stream).
+ * Returns SDPA_OK after a successful enqueue, or an error code.
+ */
+sdpa_status sdpa_forward(const void *Q, const void *K, const void *V,
+                         const int32_t *key_lengths, int causal, void *out,
+                         int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                         int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *sdpa_status_str(sdpa_status status);
+
+/* The hipError_t value behind the calling thread's last SDPA_ERR_HIP (0 if none). */
+int sdpa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_H_ */

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports what include/sdpa.h
+declares, and rejects invalid calls on the host before any HIP call.
+
+Pointers passed here are fake addresses; every call below is one the library
+must refuse (or treat as empty) before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import head_attention_fwd_amd as sdpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+FAKE_Q, FAKE_K, FAKE_V, FAKE_O = 0x10000, 0x20000, 0x30000, 0x40000
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(sdpa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sdpa.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in range(6):
+        s = sdpa.sdpa_status_str(st)
+        assert isinstance(s, str) and s
+    assert sdpa.sdpa_status_str(0) == "success"
+    assert "unknown" in sdpa.sdpa_status_str(99)
+    assert sdpa.sdpa_last_hip_error() == 0
+
+
+def call(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, causal=0, O=FAKE_O, B=2, H=2, Lq=16, Lk=16,
+         dk=64, dv=64, dtype=sdpa.SDPA_BF16):
+    return sdpa.sdpa_forward(Q, K, V, kl, causal, O, B, H, Lq, Lk, dk, dv, dtype, 0)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(Q=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(K=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(V=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(O=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(B=-1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(H=-3), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(Lq=-1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(Lk=-1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(dk=0), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(dv=0), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(Lq=2**31), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(B=2**20, H=2**20), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(B=2**16, H=2**10, Lq=2**20, Lk=1, dk=1, dv=1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(dk=129), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dv=256), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dk=129, dtype=sdpa.SDPA_F32), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=7), sdpa.SDPA_ERR_UNSUPPORTED),
+    # out overlapping an input (byte ranges computed on the host)
+    (dict(O=FAKE_Q), sdpa.SDPA_ERR_ALIAS),
+    (dict(O=FAKE_Q + 2 * 2 * 16 * 64 * 2 - 2), sdpa.SDPA_ERR_ALIAS),
+    (dict(O=FAKE_K - 2), sdpa.SDPA_ERR_ALIAS),
+    (dict(O=FAKE_V + 64), sdpa.SDPA_ERR_ALIAS),
+    (dict(kl=FAKE_O + 8), sdpa.SDPA_ERR_ALIAS),
+])
+def test_prelaunch_validation(kw, expected):
+    assert call(**kw) == expected
+
+
+def test_adjacent_buffers_are_not_aliases_but_empty_calls_launch_nothing():
+    # B == 0, H == 0 or Lq == 0: nothing to compute, success without any HIP call.
+    assert call(B=0) == sdpa.SDPA_OK
+    assert call(H=0) == sdpa.SDPA_OK
+    assert call(Lq=0) == sdpa.SDPA_OK
+    # empty call with NULL pointers is still fine
+    assert call(Q=0, K=0, V=0, O=0, Lq=0) == sdpa.SDPA_OK
+    # out exactly one past the end of Q is not an overlap (checked on an empty-free
+    # shape only through the alias helper's arithmetic: Q occupies [Q, Q + 8192)).
+    assert call(O=FAKE_Q + 2 * 2 * 16 * 64 * 2, B=0) == sdpa.SDPA_OK
+
+
+def test_python_forward_rejects_bad_arguments_without_gpu():
+    import torch
+    q = torch.zeros(1, 1, 4, 8)
+    with pytest.raises(ValueError):
+        sdpa.forward(q, q, q)          # CPU tensors are refused, never computed
+    with pytest.raises(ValueError):
+        sdpa.forward(q[0], q, q)
+    with pytest.raises(TypeError):
+        sdpa.forward(q.half(), q.half(), q.half())

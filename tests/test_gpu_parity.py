@@ -90,7 +90,7 @@ F32_CASES = [
     (2, 3, 100, 77, 1, 1, True, [77, 5]),
     (2, 3, 100, 77, 3, 17, False, [0, 60]),
     (1, 2, 65, 130, 64, 64, True, None),
-    (1, 2, 65, 130, 64, 64, False, [129, 130]),
+    (2, 2, 65, 130, 64, 64, False, [129, 130]),
     (1, 1, 40, 33, 100, 128, True, None),
     (1, 1, 40, 33, 128, 40, False, [20]),
 ]

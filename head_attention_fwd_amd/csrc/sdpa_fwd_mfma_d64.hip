@@ -26,16 +26,24 @@
 //    16h + 8g + (r % 8), which is what the second MFMA expects of its B operand.
 //  * The output accumulator O^T also holds one query per lane, so the online
 //    rescaling factor exp(m_old - m_new) is a per-lane scalar.
-//  * K is staged in LDS row-major (rows stored in pi order), V transposed
-//    (rows = dims), both with 16-byte chunks XOR-swizzled by the row so that the
-//    16-byte operand reads of a wave are free of bank conflicts.  Two LDS
-//    buffers: tile t+1 is fetched from HBM into registers while tile t is
-//    multiplied, one barrier per tile.
+//  * K and V are staged in LDS row-major, exactly as they sit in HBM (K rows
+//    stored in pi order), with 16-byte chunks XOR-swizzled by the row so that
+//    the operand reads of a wave are free of bank conflicts.  The V^T operand
+//    is read with ds_read_b64_tr_b16, which transposes 16-bit elements across
+//    each group of 16 lanes: lane i receives element i % 4 of the 4-element
+//    rows addressed by lanes 4e + i / 4 (e = 0..3), so two such reads give a
+//    lane 8 consecutive keys of one dim.  Two LDS buffers: tile t+1 is fetched
+//    from HBM into registers while tile t is multiplied, one barrier per tile.
 //  * Softmax in base 2: p = exp2(s * log2(e)/sqrt(d_k) - m), with m tracked in
-//    the same scaled units; exp2 is v_exp_f32.  Masks are applied only in tiles
-//    that cross the causal diagonal or the padding boundary; tiles entirely
-//    above a wave's diagonal are skipped by that wave, and tiles entirely
-//    beyond the key length are never loaded.
+//    the same scaled units; exp2 is v_exp_f32.  A row's reference maximum m
+//    is moved (to the row's current maximum) only when that maximum exceeds m
+//    by more than kTau; otherwise p stays below 2^kTau, harmless in fp32 and
+//    bf16.  The result is the same softmax, and after the first tiles the
+//    rescale of the accumulator is almost never taken.  The row sum adds the bf16-rounded weights
+//    (v_dot2c_f32_bf16 against 1), i.e. exactly the weights used in P.V.
+//  * Masks are applied only in tiles that cross the causal diagonal or the
+//    padding boundary; tiles entirely above a wave's diagonal are skipped by
+//    that wave, and tiles entirely beyond the key length are never loaded.
 //  * Causal grids are issued longest-first (last query tile first) so the
 //    triangle's long tiles do not finish last.
 #include <hip/hip_runtime.h>
@@ -51,15 +59,21 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 64;       // d_k = d_v
 constexpr int kBN = 64;      // keys per tile
-constexpr int kTileElems = kBN * kD;  // bf16 elements per K (or V^T) tile
+constexpr int kTileElems = kBN * kD;  // bf16 elements per K (or V) tile
+constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 
 // 16-byte chunk swizzle: rows r and r' that a wave reads in the same LDS cycle
 // get different chunk positions (injective on any 8 consecutive rows and on the
 // 8 even or 8 odd rows of any 16 consecutive rows).
 __device__ inline int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// V rows: the 4 rows one ds_read_b64_tr_b16 group touches get disjoint chunk pairs.
+__device__ inline int swz_v(int row) { return (row & 3) << 1; }
 
 // Key row order fed to the score MFMA: swap bits 2 and 3 (an involution).
 __device__ inline int pi32(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -73,6 +87,28 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 
 __device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Transposing LDS read (see the header comment for the lane mapping).
+__device__ inline u32x2_t ds_read_tr16_b64(const uint16_t *p)
+{
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p));
+}
+
+// max over the two lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic)
+__device__ inline float max_across_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ inline float sum_across_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 __device__ inline f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -81,67 +117,42 @@ __device__ inline f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
 template <int NW>
 struct TileLoader {
     static constexpr int kThreads = NW * 64;
-    // K: 64 rows x 8 chunks of 16 B; V: 32 key pairs x 8 dim-chunks.
-    static constexpr int kKChunks = (kBN * 8 + kThreads - 1) / kThreads;
-    static constexpr int kVTasks = (kBN / 2 * 8 + kThreads - 1) / kThreads;
-    u32x4_t k[kKChunks];
-    u32x4_t v0[kVTasks], v1[kVTasks];
+    // Each of K and V: 64 rows x 8 chunks of 16 B.
+    static constexpr int kChunks = (kBN * 8 + kThreads - 1) / kThreads;
+    u32x4_t k[kChunks], v[kChunks];
 
-    // Global -> registers.  Rows at or beyond `valid` (the key length) load as
-    // zero, so the contents of padded rows never enter the arithmetic.
+    // Global -> registers, 8 consecutive threads per 128-byte row.  Rows at or
+    // beyond `valid` (the key length) load as zero, so the contents of padded
+    // rows never enter the arithmetic.
     __device__ inline void fetch(const uint16_t *Kh, const uint16_t *Vh, int64_t kv0,
                                  int64_t valid, int tid)
     {
 #pragma unroll
-        for (int it = 0; it < kKChunks; ++it) {
+        for (int it = 0; it < kChunks; ++it) {
             const int ci = tid + it * kThreads;
             const int r = ci >> 3, c = ci & 7;
             const int64_t row = kv0 + r;
             k[it] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (ci < kBN * 8 && row < valid)
+            v[it] = (u32x4_t){0u, 0u, 0u, 0u};
+            if (ci < kBN * 8 && row < valid) {
                 k[it] = *(const u32x4_t *)(Kh + row * kD + c * 8);
-        }
-#pragma unroll
-        for (int it = 0; it < kVTasks; ++it) {
-            const int ti = tid + it * kThreads;
-            const int p = ti & 31, c = ti >> 5;
-            const int64_t row = kv0 + 2 * p;
-            v0[it] = (u32x4_t){0u, 0u, 0u, 0u};
-            v1[it] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (ti < kBN / 2 * 8) {
-                if (row < valid) v0[it] = *(const u32x4_t *)(Vh + row * kD + c * 8);
-                if (row + 1 < valid) v1[it] = *(const u32x4_t *)(Vh + (row + 1) * kD + c * 8);
+                v[it] = *(const u32x4_t *)(Vh + row * kD + c * 8);
             }
         }
     }
 
     // Registers -> LDS.  K row r goes to LDS row pi(r) (within its 32-row
-    // block); V is written transposed: dim d's row holds the tile's 64 keys.
-    __device__ inline void store(uint16_t *Ks, uint16_t *Vt, int tid) const
+    // block); V rows stay in order.  Both are row-major with swizzled chunks.
+    __device__ inline void store(uint16_t *Ks, uint16_t *Vs, int tid) const
     {
 #pragma unroll
-        for (int it = 0; it < kKChunks; ++it) {
+        for (int it = 0; it < kChunks; ++it) {
             const int ci = tid + it * kThreads;
             if (ci < kBN * 8) {
                 const int r = ci >> 3, c = ci & 7;
                 const int pos = (r & 32) | pi32(r & 31);
                 *(u32x4_t *)(Ks + pos * kD + ((c ^ swz(pos)) << 3)) = k[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < kVTasks; ++it) {
-            const int ti = tid + it * kThreads;
-            if (ti < kBN / 2 * 8) {
-                const int p = ti & 31, c = ti >> 5;
-                // keys 2p, 2p+1 -> 32-bit word (p % 4) of chunk p / 4 of row d
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = c * 8 + e;
-                    const uint32_t a = v0[it][e >> 1], b = v1[it][e >> 1];
-                    const uint32_t w = (e & 1) ? ((a >> 16) | (b & 0xFFFF0000u))
-                                               : ((a & 0xFFFFu) | (b << 16));
-                    *(uint32_t *)(Vt + d * kBN + (((p >> 2) ^ swz(d)) << 3) + ((p & 3) << 1)) = w;
-                }
+                *(u32x4_t *)(Vs + r * kD + ((c ^ swz_v(r)) << 3)) = v[it];
             }
         }
     }
@@ -195,19 +206,46 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
         qf[kb] = as_bf16x8(t);
     }
 
+    // LDS element offsets of this lane's operand reads (loop invariant).
+    //  K (A of S^T): row pos = 32*bk + l32, dims 16*kb + 8*g .. +7.
+    int koff[2][4];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int pos = bk * 32 + l32;
+            koff[bk][kb] = pos * kD + (((2 * kb + g) ^ swz(pos)) << 3);
+        }
+    //  V (A of O^T, transposing read): in 16-lane group G, lane i addresses row
+    //  4*e' + i/4 of a 4-row slab (e' = 0) and dims 4*(i%4) .. +3 of the
+    //  16-dim slab 32*db + 16*(G%2); slab rows are 16*kk + 8*g + 4*h.
+    int voff[2];
+    {
+        const int i = lane & 15;
+        const int G1 = (lane >> 4) & 1;
+        const int row = 8 * g + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const int col = 32 * db + 16 * G1 + 4 * (i & 3);
+            voff[db] = row * kD + ((((col >> 3) ^ swz_v(row))) << 3) + (col & 7);
+        }
+    }
+
     f32x16_t acc[2];                 // O^T: dims 32*blk + 8*(r/4) + 4*g + r%4, query qrow
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
-    float m_run = -INFINITY;         // running max of scaled scores (log2 units)
+    float m_run = -INFINITY;         // reference max of scaled scores (log2 units)
     float l_run = 0.f;               // this lane's part of the running sum
+
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     TileLoader<NW> ld;
     if (n_tiles > 0) ld.fetch(Kh, Vh, 0, len, tid);
 
     for (int t = 0; t < n_tiles; ++t) {
         uint16_t *Ks = lds[t & 1][0];
-        uint16_t *Vt = lds[t & 1][1];
-        ld.store(Ks, Vt, tid);
+        uint16_t *Vs = lds[t & 1][1];
+        ld.store(Ks, Vs, tid);
         __syncthreads();
         const int64_t kv0 = (int64_t)t * kBN;
         if (t + 1 < n_tiles) ld.fetch(Kh, Vh, kv0 + kBN, len, tid);
@@ -221,40 +259,50 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
         for (int bk = 0; bk < 2; ++bk) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
-            const int pos = bk * 32 + l32;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const u32x4_t a = *(const u32x4_t *)(Ks + pos * kD + (((2 * kb + g) ^ swz(pos)) << 3));
+                const u32x4_t a = *(const u32x4_t *)(Ks + koff[bk][kb]);
                 s[bk] = mfma32(as_bf16x8(a), qf[kb], s[bk]);
             }
         }
 
-        // ---- mask (only where the tile crosses the diagonal or the padding end)
+        // ---- mask (only where the tile crosses the diagonal or the padding end):
+        // key kv0 + rel is legal iff rel < lim.
         const bool need_mask = (kv0 + kBN > len) || (causal && kv0 + kBN - 1 > q0w);
         if (need_mask) {
+            int64_t lim64 = len - kv0;
+            if (causal && qrow + 1 - kv0 < lim64) lim64 = qrow + 1 - kv0;
+            const int lim = (int)(lim64 < 0 ? 0 : (lim64 > kBN ? kBN : lim64));
 #pragma unroll
             for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int64_t key = kv0 + 32 * bk + 16 * (r >> 3) + 8 * g + (r & 7);
-                    if (key >= len || (causal && key > qrow)) s[bk][r] = -INFINITY;
+                    const int rel = 32 * bk + 16 * (r >> 3) + 8 * g + (r & 7);
+                    if (rel >= lim) s[bk][r] = -INFINITY;
                 }
         }
 
-        // ---- online softmax (base 2)
-        float mx = -INFINITY;
+        // ---- online softmax (base 2) with a lazily moved reference maximum
+        float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int bk = 0; bk < 2; ++bk)
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bk][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * scale_log2);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;   // all -inf so far
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-        m_run = m_new;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        const float mxs = max_across_halves(mx) * scale_log2;
+        // Each row moves its own reference only (so a row's result depends on its
+        // own legal keys alone); the branch is taken when any row of the wave moves.
+        const bool grow = mxs > m_run + kTau;    // false while mxs is -inf
+        if (__any(grow)) {
+            const float m_new = grow ? mxs : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) { acc[0][i] *= alpha; acc[1][i] *= alpha; }
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;   // all -inf so far
 
         bf16x8_t pf[4];              // P^T B operands, k-block kk = 2*bk + (r / 8)
-        float psum = 0.f;
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
 #pragma unroll
@@ -262,32 +310,32 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
                 u32x4_t w;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i], scale_log2, -m_ref));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i + 1], scale_log2, -m_ref));
-                    psum += p0 + p1;
-                    w[i] = pack_bf16x2(p0, p1);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i], scale_log2, -m_use));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i + 1], scale_log2, -m_use));
+                    const uint32_t pk = pack_bf16x2(p0, p1);
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones,
+                                                            l_run, false);
+                    w[i] = pk;
                 }
                 pf[2 * bk + h] = as_bf16x8(w);
             }
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { acc[0][i] *= alpha; acc[1][i] *= alpha; }
 
         // ---- O^T += V^T P^T
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                const int d = db * 32 + l32;
-                const u32x4_t a = *(const u32x4_t *)(Vt + d * kBN + (((2 * kk + g) ^ swz(d)) << 3));
+                const u32x2_t lo = ds_read_tr16_b64(Vs + voff[db] + (16 * kk) * kD);
+                const u32x2_t hi = ds_read_tr16_b64(Vs + voff[db] + (16 * kk + 4) * kD);
+                const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
                 acc[db] = mfma32(as_bf16x8(a), pf[kk], acc[db]);
             }
         }
     }
 
     // ---- epilogue: O = acc / l, rounded to bf16
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = sum_across_halves(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
     if (qrow < Lq) {
         uint16_t *o = O + ((int64_t)bh * Lq + qrow) * kD;

@@ -114,6 +114,26 @@ def cpu_baseline(x, target_seconds=15.0):
                           c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths), dt)}
 
 
+def copy_calibration(torch, dev, args):
+    """A plain copy of known size: reads and writes args.copy_mib MiB per launch."""
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": ms,
+                      "GB_per_s_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +141,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of attention, time a plain device copy of this many MiB "
+                         "(calibrates the HBM byte counters of rocprofv3)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through (0: enough for >= 1 GiB on HBM-bound "
                          "workloads, 1 otherwise)")
@@ -136,6 +159,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     dev = torch.device("cuda:0")
+    if args.copy_mib:
+        copy_calibration(torch, dev, args)
+        return
     x = workloads.generate(args.config)
     c = x.config
     tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32

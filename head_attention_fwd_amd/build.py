@@ -15,6 +15,9 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     # no packed fp32 VALU instructions (v_pk_{add,mul,fma}_f32) in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the softmax reads every score, and
+    # AGPR-resident accumulators would cost a v_accvgpr_read per score
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

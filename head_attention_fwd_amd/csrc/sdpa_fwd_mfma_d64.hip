@@ -32,8 +32,9 @@
 //    is read with ds_read_b64_tr_b16, which transposes 16-bit elements across
 //    each group of 16 lanes: lane i receives element i % 4 of the 4-element
 //    rows addressed by lanes 4e + i / 4 (e = 0..3), so two such reads give a
-//    lane 8 consecutive keys of one dim.  Two LDS buffers: tile t+1 is fetched
-//    from HBM into registers while tile t is multiplied, one barrier per tile.
+//    lane 8 consecutive keys of one dim.  Two LDS buffers: tile t+1 is copied
+//    from HBM into LDS (asynchronously, without registers) while tile t is
+//    multiplied, one barrier per tile.
 //  * Softmax in base 2: p = exp2(s * log2(e)/sqrt(d_k) - m), with m tracked in
 //    the same scaled units; exp2 is v_exp_f32.  A row's reference maximum m
 //    is moved (to the row's current maximum) only when that maximum exceeds m
@@ -114,49 +115,64 @@ __device__ inline f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Buffer resource word 3 for raw (unswizzled, stride 0) dword access on CDNA.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// K/V tile loads go straight from HBM into LDS (buffer_load_dwordx4 ... lds): no
+// staging registers, no LDS store instructions.  One such instruction moves
+// 64 lanes x 16 B = 1 KiB = 8 rows of a tile into LDS at consecutive addresses
+// (lane L -> byte 16*L of the slice), so the LDS layout is chosen by which
+// global 16-byte chunk each lane fetches: lane L fills LDS row 8*slice + L/8,
+// physical chunk L % 8.  The buffer descriptor of each tile starts at the
+// tile's first row and covers only the rows below the key length; the
+// hardware returns 0 for reads past that bound, which zero-fills padded rows.
 template <int NW>
 struct TileLoader {
-    static constexpr int kThreads = NW * 64;
-    // Each of K and V: 64 rows x 8 chunks of 16 B.
-    static constexpr int kChunks = (kBN * 8 + kThreads - 1) / kThreads;
-    u32x4_t k[kChunks], v[kChunks];
+    static constexpr int kSlices = kBN / 8;                 // 1 KiB slices per K (or V) tile
+    static constexpr int kPerWave = (kSlices + NW - 1) / NW;
+    uint32_t koff[kPerWave], voff[kPerWave];               // byte offsets within the tile
+    int slice0;
 
-    // Global -> registers, 8 consecutive threads per 128-byte row.  Rows at or
-    // beyond `valid` (the key length) load as zero, so the contents of padded
-    // rows never enter the arithmetic.
-    __device__ inline void fetch(const uint16_t *Kh, const uint16_t *Vh, int64_t kv0,
-                                 int64_t valid, int tid)
+    __device__ inline void init(int wave, int lane)
     {
+        slice0 = wave * kPerWave;
 #pragma unroll
-        for (int it = 0; it < kChunks; ++it) {
-            const int ci = tid + it * kThreads;
-            const int r = ci >> 3, c = ci & 7;
-            const int64_t row = kv0 + r;
-            k[it] = (u32x4_t){0u, 0u, 0u, 0u};
-            v[it] = (u32x4_t){0u, 0u, 0u, 0u};
-            if (ci < kBN * 8 && row < valid) {
-                k[it] = *(const u32x4_t *)(Kh + row * kD + c * 8);
-                v[it] = *(const u32x4_t *)(Vh + row * kD + c * 8);
-            }
+        for (int j = 0; j < kPerWave; ++j) {
+            const int pos = 8 * (slice0 + j) + (lane >> 3);   // LDS row filled by this lane
+            const int pc = lane & 7;                          // physical chunk
+            const int kr = (pos & 32) | pi32(pos & 31);       // K row stored at LDS row pos
+            koff[j] = (uint32_t)(kr * kD * 2 + ((pc ^ swz(pos)) << 4));
+            voff[j] = (uint32_t)(pos * kD * 2 + ((pc ^ swz_v(pos)) << 4));
         }
     }
 
-    // Registers -> LDS.  K row r goes to LDS row pi(r) (within its 32-row
-    // block); V rows stay in order.  Both are row-major with swizzled chunks.
-    __device__ inline void store(uint16_t *Ks, uint16_t *Vs, int tid) const
+    // Issue the asynchronous copies of rows kv0 .. kv0+63 (rows >= valid read 0).
+    __device__ inline void issue(const uint16_t *Kh, const uint16_t *Vh, int64_t kv0,
+                                 int64_t valid, uint16_t *Ks, uint16_t *Vs) const
     {
+        int64_t rows = valid - kv0;
+        rows = rows < 0 ? 0 : (rows > kBN ? kBN : rows);
+        const int nbytes = (int)rows * kD * 2;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(Kh + kv0 * kD), (short)0, nbytes, kBufferRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(Vh + kv0 * kD), (short)0, nbytes, kBufferRsrcWord3);
+        typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
-        for (int it = 0; it < kChunks; ++it) {
-            const int ci = tid + it * kThreads;
-            if (ci < kBN * 8) {
-                const int r = ci >> 3, c = ci & 7;
-                const int pos = (r & 32) | pi32(r & 31);
-                *(u32x4_t *)(Ks + pos * kD + ((c ^ swz(pos)) << 3)) = k[it];
-                *(u32x4_t *)(Vs + r * kD + ((c ^ swz_v(r)) << 3)) = v[it];
+        for (int j = 0; j < kPerWave; ++j) {
+            if (slice0 + j < kSlices) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(Ks + (slice0 + j) * 8 * kD), 16,
+                                                         koff[j], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(Vs + (slice0 + j) * 8 * kD), 16,
+                                                         voff[j], 0, 0, 0);
             }
         }
     }
 };
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): this wave's
+// HBM -> LDS copies have landed.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
@@ -240,15 +256,18 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     TileLoader<NW> ld;
-    if (n_tiles > 0) ld.fetch(Kh, Vh, 0, len, tid);
+    ld.init(wave, lane);
+    if (n_tiles > 0) ld.issue(Kh, Vh, 0, len, lds[0][0], lds[0][1]);
 
     for (int t = 0; t < n_tiles; ++t) {
         uint16_t *Ks = lds[t & 1][0];
         uint16_t *Vs = lds[t & 1][1];
-        ld.store(Ks, Vs, tid);
+        // Tile t has landed for every wave, and every wave is done with tile
+        // t-1, whose buffer the next copies overwrite.
+        wait_vmem();
         __syncthreads();
         const int64_t kv0 = (int64_t)t * kBN;
-        if (t + 1 < n_tiles) ld.fetch(Kh, Vh, kv0 + kBN, len, tid);
+        if (t + 1 < n_tiles) ld.issue(Kh, Vh, kv0 + kBN, len, lds[(t + 1) & 1][0], lds[(t + 1) & 1][1]);
 
         // A wave whose rows all precede the tile's first key has nothing to do.
         if (causal && kv0 > q0w + 31) continue;

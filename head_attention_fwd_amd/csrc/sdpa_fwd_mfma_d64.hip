@@ -174,103 +174,46 @@ struct TileLoader {
 // HBM -> LDS copies have landed.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Per-wave state of the forward pass and the work on one key tile.  The tile
+// step is instantiated once per LDS buffer so that every LDS operand address is
+// a per-lane register plus an immediate offset.
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
-    uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
-    uint32_t n_qtiles, uint32_t n_bh)
-{
-    constexpr int BM = 32 * NW;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileElems];
+struct Attn {
+    static constexpr int BM = 32 * NW;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int g = lane >> 5;      // lane half
-    const int l32 = lane & 31;
-
-    // Work item: head-major within a query-tile index; causal grids run the
-    // longest (last) query tiles first.
-    const uint32_t bh = blockIdx.x % n_bh;
-    uint32_t qt = blockIdx.x / n_bh;
-    if (causal) qt = n_qtiles - 1 - qt;
-    const int64_t b = bh / H;
-    const int64_t q0 = (int64_t)qt * BM;
-    const int64_t q0w = q0 + 32 * wave;        // first query row of this wave
-    const int64_t qrow = q0w + l32;             // this lane's query row
-
-    int64_t len = Lk;
-    if (key_lengths) {
-        const int64_t l = key_lengths[b];
-        len = l < 0 ? 0 : (l > Lk ? Lk : l);
-    }
-    int64_t kv_end = len;                        // keys the workgroup needs
-    if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
-    const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
-
-    const uint16_t *Kh = K + (int64_t)bh * Lk * kD;
-    const uint16_t *Vh = V + (int64_t)bh * Lk * kD;
-
-    // Q^T as the B operand of the score MFMA: lane holds query qrow, dims
-    // 16*kb + 8*g .. +7 for kb = 0..3.
-    bf16x8_t qf[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        u32x4_t t = {0u, 0u, 0u, 0u};
-        if (qrow < Lq) t = *(const u32x4_t *)(Q + ((int64_t)bh * Lq + qrow) * kD + kb * 16 + g * 8);
-        qf[kb] = as_bf16x8(t);
-    }
-
-    // LDS element offsets of this lane's operand reads (loop invariant).
-    //  K (A of S^T): row pos = 32*bk + l32, dims 16*kb + 8*g .. +7.
-    int koff[2][4];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int pos = bk * 32 + l32;
-            koff[bk][kb] = pos * kD + (((2 * kb + g) ^ swz(pos)) << 3);
-        }
-    //  V (A of O^T, transposing read): in 16-lane group G, lane i addresses row
-    //  4*e' + i/4 of a 4-row slab (e' = 0) and dims 4*(i%4) .. +3 of the
-    //  16-dim slab 32*db + 16*(G%2); slab rows are 16*kk + 8*g + 4*h.
-    int voff[2];
-    {
-        const int i = lane & 15;
-        const int G1 = (lane >> 4) & 1;
-        const int row = 8 * g + (i >> 2);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            const int col = 32 * db + 16 * G1 + 4 * (i & 3);
-            voff[db] = row * kD + ((((col >> 3) ^ swz_v(row))) << 3) + (col & 7);
-        }
-    }
-
-    f32x16_t acc[2];                 // O^T: dims 32*blk + 8*(r/4) + 4*g + r%4, query qrow
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { acc[0][i] = 0.f; acc[1][i] = 0.f; }
-    float m_run = -INFINITY;         // reference max of scaled scores (log2 units)
-    float l_run = 0.f;               // this lane's part of the running sum
-
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    uint16_t *lds;                   // [2 buffers][K, V][kTileElems]
+    const uint16_t *Kh, *Vh;
+    int64_t len;                     // legal keys of this batch entry (clamped)
+    int64_t q0w;                     // first query row of this wave (wave-uniform)
+    int64_t qrow;                    // this lane's query row
+    int causal;
+    int n_tiles;
+    float scale_log2;
+    int g;                           // lane half
 
     TileLoader<NW> ld;
-    ld.init(wave, lane);
-    if (n_tiles > 0) ld.issue(Kh, Vh, 0, len, lds[0][0], lds[0][1]);
+    bf16x8_t qf[4];                  // Q^T operand (B of S^T = K Q^T)
+    int koff[2][4];                  // LDS element offsets, K operand reads
+    int voff[2];                     // LDS element offsets, V transposing reads
+    f32x16_t acc[2];                 // O^T: dims 32*db + 8*(r/4) + 4*g + r%4, query qrow
+    float m_run, l_run;
 
-    for (int t = 0; t < n_tiles; ++t) {
-        uint16_t *Ks = lds[t & 1][0];
-        uint16_t *Vs = lds[t & 1][1];
+    template <int BUF>
+    __device__ __forceinline__ void tile(int t)
+    {
+        const uint16_t *Ks = lds + BUF * 2 * kTileElems;
+        const uint16_t *Vs = Ks + kTileElems;
         // Tile t has landed for every wave, and every wave is done with tile
         // t-1, whose buffer the next copies overwrite.
         wait_vmem();
         __syncthreads();
         const int64_t kv0 = (int64_t)t * kBN;
-        if (t + 1 < n_tiles) ld.issue(Kh, Vh, kv0 + kBN, len, lds[(t + 1) & 1][0], lds[(t + 1) & 1][1]);
+        if (t + 1 < n_tiles)
+            ld.issue(Kh, Vh, kv0 + kBN, len, lds + (1 - BUF) * 2 * kTileElems,
+                     lds + (1 - BUF) * 2 * kTileElems + kTileElems);
 
         // A wave whose rows all precede the tile's first key has nothing to do.
-        if (causal && kv0 > q0w + 31) continue;
+        if (causal && kv0 > q0w + 31) return;
 
         // ---- S^T = K Q^T for the tile's two 32-key blocks
         f32x16_t s[2];
@@ -311,7 +254,10 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
         // Each row moves its own reference only (so a row's result depends on its
         // own legal keys alone); the branch is taken when any row of the wave moves.
         const bool grow = mxs > m_run + kTau;    // false while mxs is -inf
-        if (__any(grow)) {
+        if (__builtin_expect(__any(grow), 0)) {
+            // Keep this a real branch: after the first tiles it is almost never
+            // taken, and if-converted it would cost 34 multiplies on every tile.
+            asm volatile("" ::: "memory");
             const float m_new = grow ? mxs : m_run;
             const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             m_run = m_new;
@@ -321,6 +267,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;   // all -inf so far
 
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
         bf16x8_t pf[4];              // P^T B operands, k-block kk = 2*bk + (r / 8)
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
@@ -331,6 +278,9 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i], scale_log2, -m_use));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i + 1], scale_log2, -m_use));
+                    // The row sum adds the bf16-rounded weights, the ones used in P V.
+                    // (The packed word is summed as a scalar: hipcc 7.2 passed the
+                    // first word to every dot2 when given elements of a vector.)
                     const uint32_t pk = pack_bf16x2(p0, p1);
                     l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones,
                                                             l_run, false);
@@ -352,19 +302,111 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
             }
         }
     }
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
+    uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
+    uint32_t n_qtiles, uint32_t n_bh)
+{
+    constexpr int BM = 32 * NW;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * kTileElems];
+
+    const int lane = threadIdx.x & 63;
+    // wave index as a scalar (it is uniform across the wave)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5;      // lane half
+    const int l32 = lane & 31;
+
+    // Work item: head-major within a query-tile index; causal grids run the
+    // longest (last) query tiles first.
+    const uint32_t bh = blockIdx.x % n_bh;
+    uint32_t qt = blockIdx.x / n_bh;
+    if (causal) qt = n_qtiles - 1 - qt;
+    const int64_t b = bh / H;
+    const int64_t q0 = (int64_t)qt * BM;
+
+    Attn<NW> st;
+    st.lds = lds;
+    st.causal = causal;
+    st.scale_log2 = scale_log2;
+    st.g = g;
+    st.q0w = q0 + 32 * wave;
+    st.qrow = st.q0w + l32;
+
+    int64_t len = Lk;
+    if (key_lengths) {
+        const int64_t l = key_lengths[b];
+        len = l < 0 ? 0 : (l > Lk ? Lk : l);
+    }
+    st.len = len;
+    int64_t kv_end = len;                        // keys the workgroup needs
+    if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
+    st.n_tiles = (int)((kv_end + kBN - 1) / kBN);
+
+    st.Kh = K + (int64_t)bh * Lk * kD;
+    st.Vh = V + (int64_t)bh * Lk * kD;
+
+    // Q^T as the B operand of the score MFMA: lane holds query qrow, dims
+    // 16*kb + 8*g .. +7 for kb = 0..3.
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        u32x4_t t = {0u, 0u, 0u, 0u};
+        if (st.qrow < Lq)
+            t = *(const u32x4_t *)(Q + ((int64_t)bh * Lq + st.qrow) * kD + kb * 16 + g * 8);
+        st.qf[kb] = as_bf16x8(t);
+    }
+
+    // LDS element offsets of this lane's operand reads.
+    //  K (A of S^T): row pos = 32*bk + l32, dims 16*kb + 8*g .. +7.
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int pos = bk * 32 + l32;
+            st.koff[bk][kb] = pos * kD + (((2 * kb + g) ^ swz(pos)) << 3);
+        }
+    //  V (A of O^T, transposing read): in 16-lane group G, lane i addresses row
+    //  i/4 of a 4-row slab and dims 4*(i%4) .. +3 of the 16-dim slab
+    //  32*db + 16*(G%2); slab rows are 16*kk + 8*g + 4*h.
+    {
+        const int i = lane & 15;
+        const int G1 = (lane >> 4) & 1;
+        const int row = 8 * g + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const int col = 32 * db + 16 * G1 + 4 * (i & 3);
+            st.voff[db] = row * kD + ((((col >> 3) ^ swz_v(row))) << 3) + (col & 7);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { st.acc[0][i] = 0.f; st.acc[1][i] = 0.f; }
+    st.m_run = -INFINITY;         // reference max of scaled scores (log2 units)
+    st.l_run = 0.f;               // this lane's part of the running sum
+
+    st.ld.init(wave, lane);
+    if (st.n_tiles > 0) st.ld.issue(st.Kh, st.Vh, 0, len, lds, lds + kTileElems);
+
+    for (int t = 0; t < st.n_tiles; t += 2) {
+        st.template tile<0>(t);
+        if (t + 1 < st.n_tiles) st.template tile<1>(t + 1);
+    }
 
     // ---- epilogue: O = acc / l, rounded to bf16
-    const float l_tot = sum_across_halves(l_run);
+    const float l_tot = sum_across_halves(st.l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
-    if (qrow < Lq) {
-        uint16_t *o = O + ((int64_t)bh * Lq + qrow) * kD;
+    if (st.qrow < Lq) {
+        uint16_t *o = O + ((int64_t)bh * Lq + st.qrow) * kD;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 u32x2_t w;
-                w[0] = pack_bf16x2(acc[db][4 * rq + 0] * inv, acc[db][4 * rq + 1] * inv);
-                w[1] = pack_bf16x2(acc[db][4 * rq + 2] * inv, acc[db][4 * rq + 3] * inv);
+                w[0] = pack_bf16x2(st.acc[db][4 * rq + 0] * inv, st.acc[db][4 * rq + 1] * inv);
+                w[1] = pack_bf16x2(st.acc[db][4 * rq + 2] * inv, st.acc[db][4 * rq + 3] * inv);
                 *(u32x2_t *)(o + db * 32 + rq * 8 + g * 4) = w;
             }
     }

@@ -9,7 +9,8 @@
 // code", §3.2.1), so they run on the matrix cores; the Lq x Lk score matrix
 // never leaves registers.
 //
-// Design (one workgroup = NW waves = 32*NW query rows of one (b, h)):
+// Design (one workgroup = NW waves = 32*NW query rows of one (b, h); keys in
+// tiles of 32*NB, processed as NB blocks of 32):
 //
 //  * Scores are formed transposed, S^T = K Q^T, one 32x32 block per MFMA
 //    chain: A = 32 keys x 16 dims (from LDS), B = 16 dims x 32 queries (the
@@ -42,11 +43,24 @@
 //    bf16.  The result is the same softmax, and after the first tiles the
 //    rescale of the accumulator is almost never taken.  The row sum adds the bf16-rounded weights
 //    (v_dot2c_f32_bf16 against 1), i.e. exactly the weights used in P.V.
+//  * Software pipeline inside a tile: while a wave evaluates the softmax of
+//    block b on the VALU, the matrix core works on S of block b+1 and on P.V
+//    of block b-1 (the MFMA and VALU instructions share one issue port, so the
+//    wave needs independent matrix work in its instruction stream to keep both
+//    units busy).  P.V of block b-1 is issued before block b's rescale check,
+//    so a rare move of the reference maximum only rescales the accumulator.
+//  * The pipelined path computes no row maximum: a row's weights are taken
+//    against its reference maximum, and only when they sum past 2^20 (rare)
+//    does the row recompute them against the block's maximum.
 //  * Masks are applied only in tiles that cross the causal diagonal or the
-//    padding boundary; tiles entirely above a wave's diagonal are skipped by
-//    that wave, and tiles entirely beyond the key length are never loaded.
-//  * Causal grids are issued longest-first (last query tile first) so the
-//    triangle's long tiles do not finish last.
+//    padding boundary; those tiles (and the first tile, which sets every
+//    row's reference maximum) take a block-by-block path with block maxima
+//    that also skips blocks entirely above the wave's diagonal.  Tiles entirely beyond the key
+//    length are never loaded.
+//  * Work order: head-major, spread over the 8 XCDs in contiguous runs so
+//    the workgroups streaming one head's K/V share an L2; long causal grids
+//    pair query tiles p and n-1-p in one workgroup (equal work per
+//    workgroup), short ones run each head's longest tiles first.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -63,10 +77,25 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kD = 64;       // d_k = d_v
-constexpr int kBN = 64;      // keys per tile
-constexpr int kTileElems = kBN * kD;  // bf16 elements per K (or V) tile
+constexpr int kD = 64;                // d_k = d_v
+constexpr int kRowBytes = kD * 2;     // one K or V row in HBM and LDS
 constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
+
+// Build-time shape of the kernel (tuned on MI355X; see the launcher).
+#ifndef SDPA_MFMA_WAVES
+#define SDPA_MFMA_WAVES 4         // waves per workgroup (32 query rows each)
+#endif
+#ifndef SDPA_MFMA_KEY_BLOCKS
+#define SDPA_MFMA_KEY_BLOCKS 2    // 32-key blocks per LDS tile
+#endif
+#ifndef SDPA_MFMA_WAVES_PER_SIMD
+#define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget for 3 waves per SIMD (0: no hint)
+#endif
+#if SDPA_MFMA_WAVES_PER_SIMD > 0
+#define SDPA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(SDPA_MFMA_WAVES_PER_SIMD, SDPA_MFMA_WAVES_PER_SIMD)))
+#else
+#define SDPA_OCCUPANCY
+#endif
 
 // 16-byte chunk swizzle: rows r and r' that a wave reads in the same LDS cycle
 // get different chunk positions (injective on any 8 consecutive rows and on the
@@ -81,12 +110,12 @@ __device__ inline int pi32(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8)
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32, nearest even
     return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ inline u32x4_t as_u32x4(bf16x8_t v) { return __builtin_bit_cast(u32x4_t, v); }
 
 // Transposing LDS read (see the header comment for the lane mapping).
 __device__ inline u32x2_t ds_read_tr16_b64(const uint16_t *p)
@@ -95,7 +124,7 @@ __device__ inline u32x2_t ds_read_tr16_b64(const uint16_t *p)
     return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p));
 }
 
-// max over the two lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic)
+// max / sum over the two lanes l and l ^ 32 (v_permlane32_swap, no LDS traffic)
 __device__ inline float max_across_halves(float x)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
@@ -115,6 +144,11 @@ __device__ inline f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Wait states between the last MFMA writing the accumulator and a read of it
+// inside inline assembly, which the compiler's hazard tracking does not see
+// through (more than the 32x32 XDL write -> VALU read requirement).
+__device__ inline void acc_read_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory"); }
+
 // Buffer resource word 3 for raw (unswizzled, stride 0) dword access on CDNA.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
@@ -126,9 +160,9 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 // physical chunk L % 8.  The buffer descriptor of each tile starts at the
 // tile's first row and covers only the rows below the key length; the
 // hardware returns 0 for reads past that bound, which zero-fills padded rows.
-template <int NW>
+template <int NW, int BN>
 struct TileLoader {
-    static constexpr int kSlices = kBN / 8;                 // 1 KiB slices per K (or V) tile
+    static constexpr int kSlices = BN / 8;                  // 1 KiB slices per K (or V) tile
     static constexpr int kPerWave = (kSlices + NW - 1) / NW;
     uint32_t koff[kPerWave], voff[kPerWave];               // byte offsets within the tile
     int slice0;
@@ -140,19 +174,19 @@ struct TileLoader {
         for (int j = 0; j < kPerWave; ++j) {
             const int pos = 8 * (slice0 + j) + (lane >> 3);   // LDS row filled by this lane
             const int pc = lane & 7;                          // physical chunk
-            const int kr = (pos & 32) | pi32(pos & 31);       // K row stored at LDS row pos
-            koff[j] = (uint32_t)(kr * kD * 2 + ((pc ^ swz(pos)) << 4));
-            voff[j] = (uint32_t)(pos * kD * 2 + ((pc ^ swz_v(pos)) << 4));
+            const int kr = (pos & ~31) | pi32(pos & 31);      // K row stored at LDS row pos
+            koff[j] = (uint32_t)(kr * kRowBytes + ((pc ^ swz(pos)) << 4));
+            voff[j] = (uint32_t)(pos * kRowBytes + ((pc ^ swz_v(pos)) << 4));
         }
     }
 
-    // Issue the asynchronous copies of rows kv0 .. kv0+63 (rows >= valid read 0).
+    // Issue the asynchronous copies of rows kv0 .. kv0+BN-1 (rows >= valid read 0).
     __device__ inline void issue(const uint16_t *Kh, const uint16_t *Vh, int64_t kv0,
                                  int64_t valid, uint16_t *Ks, uint16_t *Vs) const
     {
         int64_t rows = valid - kv0;
-        rows = rows < 0 ? 0 : (rows > kBN ? kBN : rows);
-        const int nbytes = (int)rows * kD * 2;
+        rows = rows < 0 ? 0 : (rows > BN ? BN : rows);
+        const int nbytes = (int)rows * kRowBytes;
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc((void *)(Kh + kv0 * kD), (short)0, nbytes, kBufferRsrcWord3);
         const __amdgpu_buffer_rsrc_t rv =
@@ -174,167 +208,261 @@ struct TileLoader {
 // HBM -> LDS copies have landed.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Per-wave state of the forward pass and the work on one key tile.  The tile
-// step is instantiated once per LDS buffer so that every LDS operand address is
-// a per-lane register plus an immediate offset.
-template <int NW>
+// Per-wave state of the forward pass and the work on one key tile.
+template <int NW, int NB>
 struct Attn {
     static constexpr int BM = 32 * NW;
+    static constexpr int BN = 32 * NB;
+    static constexpr int kTileElems = BN * kD;   // bf16 elements per K (or V) tile
 
     uint16_t *lds;                   // [2 buffers][K, V][kTileElems]
     const uint16_t *Kh, *Vh;
     int64_t len;                     // legal keys of this batch entry (clamped)
     int64_t q0w;                     // first query row of this wave (wave-uniform)
-    int64_t qrow;                    // this lane's query row
+    int l32;                         // this lane's query row is q0w + l32
     int causal;
     int n_tiles;
     float scale_log2;
     int g;                           // lane half
 
-    TileLoader<NW> ld;
+    TileLoader<NW, BN> ld;
     bf16x8_t qf[4];                  // Q^T operand (B of S^T = K Q^T)
-    int koff[2][4];                  // LDS element offsets, K operand reads
-    int voff[2];                     // LDS element offsets, V transposing reads
-    f32x16_t acc[2];                 // O^T: dims 32*db + 8*(r/4) + 4*g + r%4, query qrow
+    int koff[2][4];                  // LDS element offsets of K reads (blocks of even/odd parity)
+    int voff[2];                     // LDS element offsets of V transposing reads
+    f32x16_t acc[2];                 // O^T: dims 32*db + 8*(r/4) + 4*g + r%4, this lane's query row
     float m_run, l_run;
 
-    template <int BUF>
-    __device__ __forceinline__ void tile(int t)
+    // S^T block bk of the tile in buffer Ks.
+    __device__ __forceinline__ f32x16_t scores(const uint16_t *Ks, int bk) const
     {
-        const uint16_t *Ks = lds + BUF * 2 * kTileElems;
-        const uint16_t *Vs = Ks + kTileElems;
-        // Tile t has landed for every wave, and every wave is done with tile
-        // t-1, whose buffer the next copies overwrite.
-        wait_vmem();
-        __syncthreads();
-        const int64_t kv0 = (int64_t)t * kBN;
-        if (t + 1 < n_tiles)
-            ld.issue(Kh, Vh, kv0 + kBN, len, lds + (1 - BUF) * 2 * kTileElems,
-                     lds + (1 - BUF) * 2 * kTileElems + kTileElems);
-
-        // A wave whose rows all precede the tile's first key has nothing to do.
-        if (causal && kv0 > q0w + 31) return;
-
-        // ---- S^T = K Q^T for the tile's two 32-key blocks
-        f32x16_t s[2];
+        f32x16_t s;
 #pragma unroll
-        for (int bk = 0; bk < 2; ++bk) {
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[bk][i] = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const u32x4_t a = *(const u32x4_t *)(Ks + koff[bk][kb]);
-                s[bk] = mfma32(as_bf16x8(a), qf[kb], s[bk]);
-            }
+        for (int kb = 0; kb < 4; ++kb) {
+            const u32x4_t a = *(const u32x4_t *)(Ks + koff[bk & 1][kb] + (bk >> 1) * 64 * kD);
+            s = mfma32(as_bf16x8(a), qf[kb], s);
         }
+        return s;
+    }
 
-        // ---- mask (only where the tile crosses the diagonal or the padding end):
-        // key kv0 + rel is legal iff rel < lim.
-        const bool need_mask = (kv0 + kBN > len) || (causal && kv0 + kBN - 1 > q0w);
-        if (need_mask) {
-            int64_t lim64 = len - kv0;
-            if (causal && qrow + 1 - kv0 < lim64) lim64 = qrow + 1 - kv0;
-            const int lim = (int)(lim64 < 0 ? 0 : (lim64 > kBN ? kBN : lim64));
+    // acc += V^T P^T for block bk (its two 16-key slabs kk = 2*bk, 2*bk + 1).
+    __device__ __forceinline__ void pv(const uint16_t *Vs, int bk, const bf16x8_t *p)
+    {
 #pragma unroll
-            for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rel = 32 * bk + 16 * (r >> 3) + 8 * g + (r & 7);
-                    if (rel >= lim) s[bk][r] = -INFINITY;
-                }
-        }
-
-        // ---- online softmax (base 2) with a lazily moved reference maximum
-        float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-        const float mxs = max_across_halves(mx) * scale_log2;
-        // Each row moves its own reference only (so a row's result depends on its
-        // own legal keys alone); the branch is taken when any row of the wave moves.
-        const bool grow = mxs > m_run + kTau;    // false while mxs is -inf
-        if (__builtin_expect(__any(grow), 0)) {
-            // Keep this a real branch: after the first tiles it is almost never
-            // taken, and if-converted it would cost 34 multiplies on every tile.
-            asm volatile("" ::: "memory");
-            const float m_new = grow ? mxs : m_run;
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) { acc[0][i] *= alpha; acc[1][i] *= alpha; }
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;   // all -inf so far
-
-        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-        bf16x8_t pf[4];              // P^T B operands, k-block kk = 2*bk + (r / 8)
-#pragma unroll
-        for (int bk = 0; bk < 2; ++bk) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                u32x4_t w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i], scale_log2, -m_use));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[bk][8 * h + 2 * i + 1], scale_log2, -m_use));
-                    // The row sum adds the bf16-rounded weights, the ones used in P V.
-                    // (The packed word is summed as a scalar: hipcc 7.2 passed the
-                    // first word to every dot2 when given elements of a vector.)
-                    const uint32_t pk = pack_bf16x2(p0, p1);
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones,
-                                                            l_run, false);
-                    w[i] = pk;
-                }
-                pf[2 * bk + h] = as_bf16x8(w);
-            }
-        }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int h = 0; h < 2; ++h) {
+            const int kk = 2 * bk + h;
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
                 const u32x2_t lo = ds_read_tr16_b64(Vs + voff[db] + (16 * kk) * kD);
                 const u32x2_t hi = ds_read_tr16_b64(Vs + voff[db] + (16 * kk + 4) * kD);
                 const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-                acc[db] = mfma32(as_bf16x8(a), pf[kk], acc[db]);
+                acc[db] = mfma32(as_bf16x8(a), p[h], acc[db]);
             }
         }
     }
+
+    // Row maximum of a block (scaled, log2 units), both lane halves combined.
+    __device__ __forceinline__ float block_max(const f32x16_t &s) const
+    {
+        float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        return max_across_halves(mx) * scale_log2;
+    }
+
+    // Multiply what was accumulated relative to the old reference maximum by
+    // alpha: the accumulator, the row sum and (if given) weights not yet
+    // multiplied by V (re-rounded to bf16).
+    __device__ __forceinline__ void scale_pending(float alpha, bf16x8_t *pending)
+    {
+        l_run *= alpha;
+        // In-place multiplies (tied operands): the accumulator keeps its
+        // registers across this rarely taken path, so the common path needs no
+        // copies where the two paths join.
+        acc_read_fence();
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                asm volatile("v_mul_f32 %0, %0, %1" : "+v"(acc[db][i]) : "v"(alpha));
+        if (pending) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4_t w = as_u32x4(pending[h]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = __builtin_bit_cast(float, w[i] << 16) * alpha;
+                    const float hi = __builtin_bit_cast(float, w[i] & 0xFFFF0000u) * alpha;
+                    w[i] = pack_bf16x2(lo, hi);
+                }
+                pending[h] = as_bf16x8(w);
+            }
+        }
+    }
+
+    // Move the reference maximum of the rows whose block maximum grew by more
+    // than kTau over it, rescaling what was accumulated against the old one.
+    __device__ __forceinline__ void rescale_if_needed(float mxs)
+    {
+        const bool grow = mxs > m_run + kTau;    // false while mxs is -inf
+        if (__builtin_expect(__any(grow), 0)) {
+            // Keep this a real branch: after the first blocks it is rarely taken,
+            // and if-converted it would cost dozens of multiplies per block.
+            asm volatile("" ::: "memory");
+            const float m_new = grow ? mxs : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            scale_pending(alpha, nullptr);
+        }
+    }
+
+    // Weights of one block relative to the reference maximum, packed as the two
+    // B operands of the P.V product.  Returns this lane's sum of the
+    // bf16-rounded weights (the ones used in P.V).
+    __device__ __forceinline__ float weights(const f32x16_t &s, bf16x8_t *p) const
+    {
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;   // all -inf so far
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4_t w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + 2 * i], scale_log2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * h + 2 * i + 1], scale_log2, -m_use));
+                // The packed word is summed as a scalar: hipcc 7.2 passed the
+                // first word to every dot2 when given elements of a vector.
+                const uint32_t pk = pack_bf16x2(p0, p1);
+                sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, sum, false);
+                w[i] = pk;
+            }
+            p[h] = as_bf16x8(w);
+        }
+        return sum;
+    }
+
+    // Tile fully inside the legal region for every row of this wave, every
+    // row already holding a finite reference maximum: no masks, all NB blocks,
+    // software-pipelined, and no block maximum.  A row's weights are computed
+    // against its reference maximum directly; only if they sum past kSumMax
+    // (some score grew by more than log2(kSumMax / 32) over the reference) does
+    // that row move its reference to the block's maximum and recompute them.
+    // The decision is per row, so a row's result depends on its own keys only.
+    __device__ __forceinline__ void tile_fast(const uint16_t *Ks, const uint16_t *Vs)
+    {
+        constexpr float kSumMax = 1048576.0f;   // 2^20
+        f32x16_t s[NB];
+        bf16x8_t p[NB][2];
+        s[0] = scores(Ks, 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            // One straight-line stretch: S of block b+1 and P.V of block b-1 on
+            // the matrix core, the weights of block b on the VALU.
+            if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
+            float bsum = weights(s[b], p[b]);
+            if (b > 0) pv(Vs, b - 1, p[b - 1]);
+            // P.V of block b-1 is already in the accumulator, so moving the
+            // reference maximum only rescales the accumulator and the row sum.
+            const bool grow = !(bsum <= kSumMax);
+            if (__builtin_expect(__any(grow), 0)) {
+                asm volatile("" ::: "memory");   // keep the rare path a real branch
+                const float mxs = block_max(s[b]);
+                if (grow) {
+                    scale_pending(__builtin_amdgcn_exp2f(m_run - mxs), nullptr);
+                    m_run = mxs;
+                }
+                const float redo = weights(s[b], p[b]);
+                bsum = grow ? redo : bsum;
+            }
+            l_run += bsum;
+        }
+        pv(Vs, NB - 1, p[NB - 1]);
+    }
+
+    // Tile crossing the causal diagonal or the padding end: block by block,
+    // masking, skipping blocks with no legal key for any row of the wave.
+    __device__ __forceinline__ void tile_masked(const uint16_t *Ks, const uint16_t *Vs, int64_t kv0)
+    {
+        int64_t lim64 = len - kv0;
+        const int64_t causal_lim = (q0w - kv0) + l32 + 1;   // keys up to this lane's row
+        if (causal && causal_lim < lim64) lim64 = causal_lim;
+        const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));   // key kv0+rel legal iff rel < lim
+        int64_t wave_end = len - kv0;                                        // wave-uniform bound
+        if (causal && q0w + 32 - kv0 < wave_end) wave_end = q0w + 32 - kv0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (32 * b >= wave_end) break;
+            f32x16_t s = scores(Ks, b);
+            // key kv0 + 32*b + 16*(r/8) + 8*g + r%8 is legal iff that offset < lim;
+            // the per-register part is a constant compared with lim - 8*g - 32*b
+            const int lim_g = lim - 8 * g - 32 * b;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (16 * (r >> 3) + (r & 7) >= lim_g) s[r] = -INFINITY;
+            rescale_if_needed(block_max(s));
+            bf16x8_t p[2];
+            l_run += weights(s, p);
+            pv(Vs, b, p);
+        }
+    }
+
+    // Tile t in LDS buffer BUF = t % 2.  Instantiated per buffer so that every
+    // LDS operand address is a per-lane register plus an immediate offset.
+    template <int BUF>
+    __device__ __forceinline__ void tile(int t)
+    {
+        const int cur = BUF * 2 * kTileElems, nxt = 2 * kTileElems - cur;
+        const uint16_t *Ks = lds + cur;
+        const uint16_t *Vs = Ks + kTileElems;
+        // Tile t has landed for every wave, and every wave is done with tile
+        // t-1, whose buffer the next copies overwrite.
+        wait_vmem();
+        __syncthreads();
+        const int64_t kv0 = (int64_t)t * BN;
+        if (t + 1 < n_tiles)
+            ld.issue(Kh, Vh, kv0 + BN, len, lds + nxt, lds + nxt + kTileElems);
+
+        // A wave whose rows all precede the tile's first key has nothing to do.
+        if (causal && kv0 > q0w + 31) return;
+        // The first tile also takes the block-by-block path, which computes
+        // block maxima: afterwards every row has a finite reference maximum
+        // (key 0 is legal for every row when len > 0).
+        const bool need_mask = t == 0 || (kv0 + BN > len) || (causal && kv0 + BN - 1 > q0w);
+        if (need_mask)
+            tile_masked(Ks, Vs, kv0);
+        else
+            tile_fast(Ks, Vs);
+    }
 };
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+// One query tile (BM rows of head bh): load Q, stream the key tiles, store O.
+template <int NW, int NB>
+__device__ __forceinline__ void attend_query_tile(
+    uint16_t *lds, const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
-    uint32_t n_qtiles, uint32_t n_bh)
+    uint32_t bh, uint32_t qt, int wave, int lane)
 {
-    constexpr int BM = 32 * NW;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * kTileElems];
-
-    const int lane = threadIdx.x & 63;
-    // wave index as a scalar (it is uniform across the wave)
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    using A = Attn<NW, NB>;
+    constexpr int BM = A::BM;
+    constexpr int BN = A::BN;
     const int g = lane >> 5;      // lane half
     const int l32 = lane & 31;
-
-    // Work item: head-major within a query-tile index; causal grids run the
-    // longest (last) query tiles first.
-    const uint32_t bh = blockIdx.x % n_bh;
-    uint32_t qt = blockIdx.x / n_bh;
-    if (causal) qt = n_qtiles - 1 - qt;
     const int64_t b = bh / H;
     const int64_t q0 = (int64_t)qt * BM;
 
-    Attn<NW> st;
+    A st;
     st.lds = lds;
     st.causal = causal;
     st.scale_log2 = scale_log2;
     st.g = g;
     st.q0w = q0 + 32 * wave;
-    st.qrow = st.q0w + l32;
+    st.l32 = l32;
+    const bool row_ok = st.q0w + l32 < Lq;
+    // wave-uniform base of the wave's 32 rows; lanes add 32-bit offsets
+    const int64_t tile_base = ((int64_t)bh * Lq + st.q0w) * kD;
 
     int64_t len = Lk;
     if (key_lengths) {
@@ -344,23 +472,24 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
     st.len = len;
     int64_t kv_end = len;                        // keys the workgroup needs
     if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
-    st.n_tiles = (int)((kv_end + kBN - 1) / kBN);
+    st.n_tiles = (int)((kv_end + BN - 1) / BN);
 
     st.Kh = K + (int64_t)bh * Lk * kD;
     st.Vh = V + (int64_t)bh * Lk * kD;
 
-    // Q^T as the B operand of the score MFMA: lane holds query qrow, dims
+    // Q^T as the B operand of the score MFMA: lane holds this lane's query row, dims
     // 16*kb + 8*g .. +7 for kb = 0..3.
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         u32x4_t t = {0u, 0u, 0u, 0u};
-        if (st.qrow < Lq)
-            t = *(const u32x4_t *)(Q + ((int64_t)bh * Lq + st.qrow) * kD + kb * 16 + g * 8);
+        if (row_ok) t = *(const u32x4_t *)(Q + tile_base + (l32 * kD + kb * 16 + g * 8));
         st.qf[kb] = as_bf16x8(t);
     }
 
     // LDS element offsets of this lane's operand reads.
-    //  K (A of S^T): row pos = 32*bk + l32, dims 16*kb + 8*g .. +7.
+    //  K (A of S^T): row pos = 32*bk + l32, dims 16*kb + 8*g .. +7; swz(pos)
+    //  depends on bk only through its parity, so blocks bk and bk + 2 share
+    //  offsets up to a constant.
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
@@ -388,7 +517,7 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
     st.l_run = 0.f;               // this lane's part of the running sum
 
     st.ld.init(wave, lane);
-    if (st.n_tiles > 0) st.ld.issue(st.Kh, st.Vh, 0, len, lds, lds + kTileElems);
+    if (st.n_tiles > 0) st.ld.issue(st.Kh, st.Vh, 0, len, lds, lds + A::kTileElems);
 
     for (int t = 0; t < st.n_tiles; t += 2) {
         st.template tile<0>(t);
@@ -396,10 +525,11 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
     }
 
     // ---- epilogue: O = acc / l, rounded to bf16
+    acc_read_fence();
     const float l_tot = sum_across_halves(st.l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
-    if (st.qrow < Lq) {
-        uint16_t *o = O + ((int64_t)bh * Lq + st.qrow) * kD;
+    if (row_ok) {
+        uint16_t *o = O + tile_base;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -407,8 +537,46 @@ __global__ __launch_bounds__(NW * 64) void sdpa_fwd_mfma_d64_kernel(
                 u32x2_t w;
                 w[0] = pack_bf16x2(st.acc[db][4 * rq + 0] * inv, st.acc[db][4 * rq + 1] * inv);
                 w[1] = pack_bf16x2(st.acc[db][4 * rq + 2] * inv, st.acc[db][4 * rq + 3] * inv);
-                *(u32x2_t *)(o + db * 32 + rq * 8 + g * 4) = w;
+                *(u32x2_t *)(o + (l32 * kD + db * 32 + rq * 8 + g * 4)) = w;
             }
+    }
+}
+
+// Work decomposition.  A workgroup handles one query tile, or, for long causal
+// grids (pair = 1), the two query tiles p and n_qtiles-1-p of one head, whose
+// key ranges add up to the same length for every p.  Workgroups are numbered
+// head-major (all the tiles of a head are consecutive) and the numbering is
+// spread over the 8 XCDs in contiguous runs: the hardware hands workgroup w to
+// XCD w % 8, so workgroup w takes item (w % 8) * (T / 8) + w / 8 when 8 divides
+// the item count T.  Each XCD then works on a few heads at a time, and the
+// workgroups streaming the same K/V rows share that XCD's L2.
+template <int NW, int NB>
+__global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
+    uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
+    uint32_t n_qtiles, uint32_t n_bh, uint32_t items_per_head, int pair)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * Attn<NW, NB>::kTileElems];
+
+    const int lane = threadIdx.x & 63;
+    // wave index as a scalar (it is uniform across the wave)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    const uint32_t n_items = items_per_head * n_bh;
+    uint32_t item = blockIdx.x;
+    if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
+    const uint32_t bh = item / items_per_head;
+    const uint32_t p = item % items_per_head;
+
+    // pair: the long tile n_qtiles-1-p, then (if different) the short tile p;
+    // otherwise one tile, and for causal grids each head's longest tiles first.
+    const uint32_t first = (pair || causal) ? n_qtiles - 1 - p : p;
+    const int n_work = (pair && p != first) ? 2 : 1;
+    for (int w = 0; w < n_work; ++w) {
+        if (w > 0) __syncthreads();   // every wave is done with the previous tile's LDS
+        attend_query_tile<NW, NB>(lds, Q, K, V, key_lengths, causal, O, H, Lq, Lk, scale_log2,
+                                  bh, w == 0 ? first : p, wave, lane);
     }
 }
 
@@ -418,15 +586,20 @@ hipError_t launch_mfma_d64(const void *Q, const void *K, const void *V,
                            const int32_t *key_lengths, int causal, void *out,
                            int64_t B, int64_t H, int64_t Lq, int64_t Lk, hipStream_t stream)
 {
-    constexpr int NW = 4;
+    constexpr int NW = SDPA_MFMA_WAVES;
+    constexpr int NB = SDPA_MFMA_KEY_BLOCKS;
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
+    // Pair the query tiles of long causal grids (balanced work per workgroup);
+    // short grids keep one tile per workgroup for parallelism.
+    const int pair = (causal && n_qtiles >= 16) ? 1 : 0;
+    const uint32_t items_per_head = pair ? (n_qtiles + 1) / 2 : n_qtiles;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
-    hipLaunchKernelGGL((sdpa_fwd_mfma_d64_kernel<NW>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0,
-                       stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                       key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2,
-                       n_qtiles, n_bh);
+    hipLaunchKernelGGL((sdpa_fwd_mfma_d64_kernel<NW, NB>), dim3(items_per_head * n_bh),
+                       dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
+                       (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
+                       scale_log2, n_qtiles, n_bh, items_per_head, pair);
     return hipGetLastError();
 }
 

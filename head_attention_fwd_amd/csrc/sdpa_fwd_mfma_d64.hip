@@ -33,9 +33,9 @@
 //    is read with ds_read_b64_tr_b16, which transposes 16-bit elements across
 //    each group of 16 lanes: lane i receives element i % 4 of the 4-element
 //    rows addressed by lanes 4e + i / 4 (e = 0..3), so two such reads give a
-//    lane 8 consecutive keys of one dim.  Two LDS buffers: tile t+1 is copied
-//    from HBM into LDS (asynchronously, without registers) while tile t is
-//    multiplied, one barrier per tile.
+//    lane 8 consecutive keys of one dim.  A ring of three LDS buffers: tiles
+//    t+1 and t+2 are being copied from HBM into LDS (asynchronously, without
+//    registers) while tile t is multiplied, one barrier per tile.
 //  * Softmax in base 2: p = exp2(s * log2(e)/sqrt(d_k) - m), with m tracked in
 //    the same scaled units; exp2 is v_exp_f32.  A row's reference maximum m
 //    is moved (to the row's current maximum) only when that maximum exceeds m
@@ -49,13 +49,11 @@
 //    wave needs independent matrix work in its instruction stream to keep both
 //    units busy).  P.V of block b-1 is issued before block b's rescale check,
 //    so a rare move of the reference maximum only rescales the accumulator.
-//  * The pipelined path computes no row maximum: a row's weights are taken
-//    against its reference maximum, and only when they sum past 2^20 (rare)
-//    does the row recompute them against the block's maximum.
-//  * Masks are applied only in tiles that cross the causal diagonal or the
-//    padding boundary; those tiles (and the first tile, which sets every
-//    row's reference maximum) take a block-by-block path with block maxima
-//    that also skips blocks entirely above the wave's diagonal.  Tiles entirely beyond the key
+//  * Fully legal tiles after the first compute no row maximum: a row's
+//    weights are taken against its reference maximum, and only when they sum
+//    past 2^20 (rare) does the row recompute them against the block maximum.
+//    The first tile and tiles crossing the causal diagonal or the padding end
+//    compute block maxima; only the latter apply masks.  Tiles entirely beyond the key
 //    length are never loaded.
 //  * Work order: head-major, spread over the 8 XCDs in contiguous runs so
 //    the workgroups streaming one head's K/V share an L2; long causal grids
@@ -87,6 +85,9 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #endif
 #ifndef SDPA_MFMA_KEY_BLOCKS
 #define SDPA_MFMA_KEY_BLOCKS 2    // 32-key blocks per LDS tile
+#endif
+#ifndef SDPA_MFMA_BUFFERS
+#define SDPA_MFMA_BUFFERS 3       // LDS tile buffers (prefetch distance = buffers - 1)
 #endif
 #ifndef SDPA_MFMA_WAVES_PER_SIMD
 #define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget for 3 waves per SIMD (0: no hint)
@@ -152,6 +153,22 @@ __device__ inline void acc_read_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_
 // Buffer resource word 3 for raw (unswizzled, stride 0) dword access on CDNA.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// One wave-wide HBM -> LDS copy: lane L's 16 bytes at byte offset voff of the
+// buffer land at LDS address dst + 16*L (buffer_load_dwordx4 ... lds, LDS base
+// in M0).  Issued as inline assembly so that the compiler does not track it:
+// its conservative tracking of such copies made it wait for every copy in
+// flight before any LDS read, which would serialize the prefetch.  The kernel
+// therefore orders these copies itself (wait_vmem_keep before each barrier).
+// M0 is written here and nowhere else in this kernel (nothing else in it uses
+// M0 on gfx950), so it is not declared clobbered (it is a reserved register).
+__device__ inline void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint16_t *dst, uint32_t voff)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+}
+
 // K/V tile loads go straight from HBM into LDS (buffer_load_dwordx4 ... lds): no
 // staging registers, no LDS store instructions.  One such instruction moves
 // 64 lanes x 16 B = 1 KiB = 8 rows of a tile into LDS at consecutive addresses
@@ -163,7 +180,9 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 template <int NW, int BN>
 struct TileLoader {
     static constexpr int kSlices = BN / 8;                  // 1 KiB slices per K (or V) tile
-    static constexpr int kPerWave = (kSlices + NW - 1) / NW;
+    static constexpr int kPerWave = kSlices / NW;
+    static_assert(kSlices % NW == 0, "every wave issues the same number of copies");
+    static constexpr int kLoadsPerTile = 2 * kPerWave;      // per wave: K and V slices
     uint32_t koff[kPerWave], voff[kPerWave];               // byte offsets within the tile
     int slice0;
 
@@ -191,22 +210,20 @@ struct TileLoader {
             __builtin_amdgcn_make_buffer_rsrc((void *)(Kh + kv0 * kD), (short)0, nbytes, kBufferRsrcWord3);
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void *)(Vh + kv0 * kD), (short)0, nbytes, kBufferRsrcWord3);
-        typedef __attribute__((address_space(3))) void lds_void;
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
-            if (slice0 + j < kSlices) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(Ks + (slice0 + j) * 8 * kD), 16,
-                                                         koff[j], 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(Vs + (slice0 + j) * 8 * kD), 16,
-                                                         voff[j], 0, 0, 0);
-            }
+            copy_to_lds(rk, Ks + (slice0 + j) * 8 * kD, koff[j]);
+            copy_to_lds(rv, Vs + (slice0 + j) * 8 * kD, voff[j]);
         }
     }
 };
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): this wave's
-// HBM -> LDS copies have landed.
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima: at most n
+// of this wave's memory operations are still outstanding (vector memory loads
+// complete in issue order, so the oldest copies have landed).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+template <int N>
+__device__ inline void wait_vmem_keep() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(N)); }
 
 // Per-wave state of the forward pass and the work on one key tile.
 template <int NW, int NB>
@@ -214,8 +231,11 @@ struct Attn {
     static constexpr int BM = 32 * NW;
     static constexpr int BN = 32 * NB;
     static constexpr int kTileElems = BN * kD;   // bf16 elements per K (or V) tile
+    static constexpr int kBuffers = SDPA_MFMA_BUFFERS;
+    static constexpr int kBufStride = 2 * kTileElems;   // K tile, then V tile, per buffer
+    static_assert(kBuffers == 2 || kBuffers == 3, "two or three LDS tile buffers");
 
-    uint16_t *lds;                   // [2 buffers][K, V][kTileElems]
+    uint16_t *kbuf[kBuffers], *vbuf[kBuffers];   // LDS tile buffers
     const uint16_t *Kh, *Vh;
     int64_t len;                     // legal keys of this batch entry (clamped)
     int64_t q0w;                     // first query row of this wave (wave-uniform)
@@ -227,8 +247,8 @@ struct Attn {
 
     TileLoader<NW, BN> ld;
     bf16x8_t qf[4];                  // Q^T operand (B of S^T = K Q^T)
-    int koff[2][4];                  // LDS element offsets of K reads (blocks of even/odd parity)
-    int voff[2];                     // LDS element offsets of V transposing reads
+    int koff[2][4];                  // LDS byte offsets of K reads (blocks of even/odd parity)
+    int voff[2];                     // LDS byte offsets of V transposing reads
     f32x16_t acc[2];                 // O^T: dims 32*db + 8*(r/4) + 4*g + r%4, this lane's query row
     float m_run, l_run;
 
@@ -240,7 +260,7 @@ struct Attn {
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const u32x4_t a = *(const u32x4_t *)(Ks + koff[bk & 1][kb] + (bk >> 1) * 64 * kD);
+            const u32x4_t a = *(const u32x4_t *)((const char *)Ks + koff[bk & 1][kb] + (bk >> 1) * 64 * kRowBytes);
             s = mfma32(as_bf16x8(a), qf[kb], s);
         }
         return s;
@@ -254,8 +274,9 @@ struct Attn {
             const int kk = 2 * bk + h;
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                const u32x2_t lo = ds_read_tr16_b64(Vs + voff[db] + (16 * kk) * kD);
-                const u32x2_t hi = ds_read_tr16_b64(Vs + voff[db] + (16 * kk + 4) * kD);
+                const char *vb = (const char *)Vs + voff[db];
+                const u32x2_t lo = ds_read_tr16_b64((const uint16_t *)(vb + (16 * kk) * kRowBytes));
+                const u32x2_t hi = ds_read_tr16_b64((const uint16_t *)(vb + (16 * kk + 4) * kRowBytes));
                 const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
                 acc[db] = mfma32(as_bf16x8(a), p[h], acc[db]);
             }
@@ -343,104 +364,163 @@ struct Attn {
         return sum;
     }
 
-    // Tile fully inside the legal region for every row of this wave, every
-    // row already holding a finite reference maximum: no masks, all NB blocks,
-    // software-pipelined, and no block maximum.  A row's weights are computed
-    // against its reference maximum directly; only if they sum past kSumMax
-    // (some score grew by more than log2(kSumMax / 32) over the reference) does
-    // that row move its reference to the block's maximum and recompute them.
-    // The decision is per row, so a row's result depends on its own keys only.
-    __device__ __forceinline__ void tile_fast(const uint16_t *Ks, const uint16_t *Vs)
+    // Blocks 0..NBLK-1 of a tile, software-pipelined: in each straight-line
+    // stretch the matrix core has S of block b+1 and/or P.V of block b-1 while
+    // the VALU works on block b.  P.V of block b-1 is always issued before block
+    // b's rescale decision, so moving a reference maximum only rescales the
+    // accumulator and the row sum.  Decisions are per row, so a row's result
+    // depends on its own legal keys only.
+    //
+    //  kMaxFree: no block maximum (the tile is fully legal and every row holds
+    //    a finite reference).  Weights are taken against the reference; only if
+    //    a row's block sum passes kSumMax (a score grew by more than
+    //    log2(kSumMax / 32) over the reference) does that row move its
+    //    reference to the block maximum and recompute the block.
+    //  kBlockMax: block maxima, reference moved when one exceeds it by kTau.
+    //    kMask additionally sets illegal scores to -inf: key
+    //    kv0 + 32*b + 16*(r/8) + 8*g + r%8 is legal iff that offset < lim.
+    enum Mode { kMaxFree, kBlockMax, kMask };
+
+    template <Mode M, int NBLK>
+    __device__ __forceinline__ void tile_blocks(const uint16_t *Ks, const uint16_t *Vs, int lim)
     {
         constexpr float kSumMax = 1048576.0f;   // 2^20
-        f32x16_t s[NB];
-        bf16x8_t p[NB][2];
+        f32x16_t s[NBLK];
+        bf16x8_t p[NBLK][2];
         s[0] = scores(Ks, 0);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            // One straight-line stretch: S of block b+1 and P.V of block b-1 on
-            // the matrix core, the weights of block b on the VALU.
-            if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
-            float bsum = weights(s[b], p[b]);
-            if (b > 0) pv(Vs, b - 1, p[b - 1]);
-            // P.V of block b-1 is already in the accumulator, so moving the
-            // reference maximum only rescales the accumulator and the row sum.
-            const bool grow = !(bsum <= kSumMax);
-            if (__builtin_expect(__any(grow), 0)) {
-                asm volatile("" ::: "memory");   // keep the rare path a real branch
-                const float mxs = block_max(s[b]);
-                if (grow) {
-                    scale_pending(__builtin_amdgcn_exp2f(m_run - mxs), nullptr);
-                    m_run = mxs;
+        for (int b = 0; b < NBLK; ++b) {
+            if constexpr (M == kMaxFree) {
+                if (b + 1 < NBLK) s[b + 1] = scores(Ks, b + 1);
+                float bsum = weights(s[b], p[b]);
+                if (b > 0) pv(Vs, b - 1, p[b - 1]);
+                const bool grow = !(bsum <= kSumMax);
+                if (__builtin_expect(__any(grow), 0)) {
+                    asm volatile("" ::: "memory");   // keep the rare path a real branch
+                    const float mxs = block_max(s[b]);
+                    if (grow) {
+                        scale_pending(__builtin_amdgcn_exp2f(m_run - mxs), nullptr);
+                        m_run = mxs;
+                    }
+                    const float redo = weights(s[b], p[b]);
+                    bsum = grow ? redo : bsum;
                 }
-                const float redo = weights(s[b], p[b]);
-                bsum = grow ? redo : bsum;
+                l_run += bsum;
+            } else {
+                if constexpr (M == kMask) {
+                    // the per-register part is a constant compared with lim - 8g - 32b
+                    const int lim_g = lim - 8 * g - 32 * b;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;
+                }
+                const float mxs = block_max(s[b]);
+                if (b > 0) pv(Vs, b - 1, p[b - 1]);
+                rescale_if_needed(mxs);
+                if (b + 1 < NBLK) s[b + 1] = scores(Ks, b + 1);
+                l_run += weights(s[b], p[b]);
             }
-            l_run += bsum;
         }
-        pv(Vs, NB - 1, p[NB - 1]);
+        pv(Vs, NBLK - 1, p[NBLK - 1]);
     }
 
-    // Tile crossing the causal diagonal or the padding end: block by block,
-    // masking, skipping blocks with no legal key for any row of the wave.
-    __device__ __forceinline__ void tile_masked(const uint16_t *Ks, const uint16_t *Vs, int64_t kv0)
+    // Issue the copies of tile u into buffer u % kBuffers.
+    __device__ __forceinline__ void prefetch(int u, uint16_t *kb, uint16_t *vb)
     {
-        int64_t lim64 = len - kv0;
-        const int64_t causal_lim = (q0w - kv0) + l32 + 1;   // keys up to this lane's row
-        if (causal && causal_lim < lim64) lim64 = causal_lim;
-        const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));   // key kv0+rel legal iff rel < lim
-        int64_t wave_end = len - kv0;                                        // wave-uniform bound
-        if (causal && q0w + 32 - kv0 < wave_end) wave_end = q0w + 32 - kv0;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (32 * b >= wave_end) break;
-            f32x16_t s = scores(Ks, b);
-            // key kv0 + 32*b + 16*(r/8) + 8*g + r%8 is legal iff that offset < lim;
-            // the per-register part is a constant compared with lim - 8*g - 32*b
-            const int lim_g = lim - 8 * g - 32 * b;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (16 * (r >> 3) + (r & 7) >= lim_g) s[r] = -INFINITY;
-            rescale_if_needed(block_max(s));
-            bf16x8_t p[2];
-            l_run += weights(s, p);
-            pv(Vs, b, p);
-        }
+        ld.issue(Kh, Vh, (int64_t)u * BN, len, kb, vb);
     }
 
-    // Tile t in LDS buffer BUF = t % 2.  Instantiated per buffer so that every
-    // LDS operand address is a per-lane register plus an immediate offset.
-    template <int BUF>
-    __device__ __forceinline__ void tile(int t)
+    // Start of tile t, the same for every wave and every kind of tile (one
+    // barrier per tile): tile t has landed once at most the copies of the tiles
+    // after it that were already issued are outstanding; after the barrier every
+    // wave's copies of tile t are in LDS and every wave is done with tile t-1,
+    // whose buffer takes tile t + kBuffers - 1.
+    __device__ __forceinline__ void tile_begin(int t, uint16_t *knext, uint16_t *vnext)
     {
-        const int cur = BUF * 2 * kTileElems, nxt = 2 * kTileElems - cur;
-        const uint16_t *Ks = lds + cur;
-        const uint16_t *Vs = Ks + kTileElems;
-        // Tile t has landed for every wave, and every wave is done with tile
-        // t-1, whose buffer the next copies overwrite.
-        wait_vmem();
+        if (kBuffers == 3 && t + 1 < n_tiles)
+            wait_vmem_keep<TileLoader<NW, BN>::kLoadsPerTile>();
+        else
+            wait_vmem_keep<0>();
         __syncthreads();
-        const int64_t kv0 = (int64_t)t * BN;
-        if (t + 1 < n_tiles)
-            ld.issue(Kh, Vh, kv0 + BN, len, lds + nxt, lds + nxt + kTileElems);
+        // Q arrived with the first tile's copies: tie its registers to the wait.
+        asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
+        if (t + kBuffers - 1 < n_tiles) prefetch(t + kBuffers - 1, knext, vnext);
+    }
 
+    // A fully legal tile after the first, in LDS buffer BUF = t % kBuffers.
+    // Instantiated per buffer so that every LDS operand address is a per-lane
+    // register plus an immediate offset.
+    template <int BUF>
+    __device__ __forceinline__ void tile_full(int t)
+    {
+        constexpr int kNext = (BUF + kBuffers - 1) % kBuffers;
+        tile_begin(t, kbuf[kNext], vbuf[kNext]);
+        tile_blocks<kMaxFree, NB>(kbuf[BUF], vbuf[BUF], BN);
+    }
+
+    // Any other tile (the first, one crossing the causal diagonal or the
+    // padding end, one beyond this wave's rows, or a full one left over from
+    // the unrolled loop), with the buffer chosen at run time.
+    __device__ __forceinline__ void tile_any(int t)
+    {
+        const int buf = t % kBuffers;
+        const int nxt = (t + kBuffers - 1) % kBuffers;
+        tile_begin(t, kbuf[0] + nxt * kBufStride, vbuf[0] + nxt * kBufStride);
+        const int64_t kv0 = (int64_t)t * BN;
         // A wave whose rows all precede the tile's first key has nothing to do.
         if (causal && kv0 > q0w + 31) return;
-        // The first tile also takes the block-by-block path, which computes
-        // block maxima: afterwards every row has a finite reference maximum
-        // (key 0 is legal for every row when len > 0).
-        const bool need_mask = t == 0 || (kv0 + BN > len) || (causal && kv0 + BN - 1 > q0w);
-        if (need_mask)
-            tile_masked(Ks, Vs, kv0);
-        else
-            tile_fast(Ks, Vs);
+        // Keys this lane may use in the tile: below the key length and, if
+        // causal, up to its own row.  (A block with no legal key for any row
+        // of the wave is computed and contributes exactly 0.)  On the first
+        // tile the block maxima set every row's reference maximum (key 0 is
+        // legal for every row when len > 0).
+        int64_t lim64 = len - kv0;
+        const int64_t causal_lim = (q0w - kv0) + l32 + 1;
+        if (causal && causal_lim < lim64) lim64 = causal_lim;
+        const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));
+        tile_blocks<kMask, NB>(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim);
+    }
+
+    // All key tiles: the first, then the fully legal ones in a loop unrolled
+    // over the buffer ring (no per-tile branches on the tile kind), then the
+    // rest.  Every wave passes the same number of barriers (one per tile).
+    __device__ __forceinline__ void run()
+    {
+        if (n_tiles == 0) return;
+        // Tiles 1 .. n_full-1 are fully legal for every row of this wave.
+        int64_t n_full = len / BN;
+        if (causal) {
+            const int64_t diag = (q0w + 1) / BN;   // (t+1)*BN - 1 <= q0w
+            if (diag < n_full) n_full = diag;
+        }
+        for (int t = 0; t < n_tiles;) {
+            if (t == 1 && n_full > 1) {
+                if constexpr (kBuffers == 3) {
+                    for (; t + 2 < n_full; t += 3) {
+                        tile_full<1>(t);
+                        tile_full<2>(t + 1);
+                        tile_full<0>(t + 2);
+                    }
+                    if (t < n_full) tile_full<1>(t++);
+                    if (t < n_full) tile_full<2>(t++);
+                } else {
+                    for (; t + 1 < n_full; t += 2) {
+                        tile_full<1>(t);
+                        tile_full<0>(t + 1);
+                    }
+                    if (t < n_full) tile_full<1>(t++);
+                }
+            } else {
+                tile_any(t++);
+            }
+        }
     }
 };
 
 // One query tile (BM rows of head bh): load Q, stream the key tiles, store O.
 template <int NW, int NB>
 __device__ __forceinline__ void attend_query_tile(
-    uint16_t *lds, const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    uint16_t *const *kbuf, uint16_t *const *vbuf, const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
     uint32_t bh, uint32_t qt, int wave, int lane)
@@ -454,16 +534,13 @@ __device__ __forceinline__ void attend_query_tile(
     const int64_t q0 = (int64_t)qt * BM;
 
     A st;
-    st.lds = lds;
+#pragma unroll
+    for (int i = 0; i < A::kBuffers; ++i) { st.kbuf[i] = kbuf[i]; st.vbuf[i] = vbuf[i]; }
     st.causal = causal;
     st.scale_log2 = scale_log2;
     st.g = g;
     st.q0w = q0 + 32 * wave;
     st.l32 = l32;
-    const bool row_ok = st.q0w + l32 < Lq;
-    // wave-uniform base of the wave's 32 rows; lanes add 32-bit offsets
-    const int64_t tile_base = ((int64_t)bh * Lq + st.q0w) * kD;
-
     int64_t len = Lk;
     if (key_lengths) {
         const int64_t l = key_lengths[b];
@@ -477,16 +554,28 @@ __device__ __forceinline__ void attend_query_tile(
     st.Kh = K + (int64_t)bh * Lk * kD;
     st.Vh = V + (int64_t)bh * Lk * kD;
 
-    // Q^T as the B operand of the score MFMA: lane holds this lane's query row, dims
-    // 16*kb + 8*g .. +7 for kb = 0..3.
+    // Rows of this wave present in Q / O; buffer descriptors bounded to them make
+    // reads past Lq return 0 and writes past Lq vanish.
+    int64_t rows_here = Lq - st.q0w;
+    rows_here = rows_here < 0 ? 0 : (rows_here > 32 ? 32 : rows_here);
+    const int64_t tile_base = ((int64_t)bh * Lq + st.q0w) * kD;   // wave-uniform
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Q + tile_base), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
+
+    // Q^T as the B operand of the score MFMA: lane holds its query row, dims
+    // 16*kb + 8*g .. +7 for kb = 0..3.  Loaded by inline assembly so that the
+    // compiler does not wait for these loads with vmcnt(0) inside the tile loop
+    // (which would also drain the tile copies in flight); the first tile's
+    // wait covers them, and Attn::tile re-defines qf after each wait.
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        u32x4_t t = {0u, 0u, 0u, 0u};
-        if (row_ok) t = *(const u32x4_t *)(Q + tile_base + (l32 * kD + kb * 16 + g * 8));
+        u32x4_t t;
+        const uint32_t voff = (uint32_t)(l32 * kRowBytes + (kb * 16 + g * 8) * 2);
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(t) : "v"(voff), "s"(rq) : "memory");
         st.qf[kb] = as_bf16x8(t);
     }
 
-    // LDS element offsets of this lane's operand reads.
+    // LDS byte offsets of this lane's operand reads.
     //  K (A of S^T): row pos = 32*bk + l32, dims 16*kb + 8*g .. +7; swz(pos)
     //  depends on bk only through its parity, so blocks bk and bk + 2 share
     //  offsets up to a constant.
@@ -495,7 +584,7 @@ __device__ __forceinline__ void attend_query_tile(
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int pos = bk * 32 + l32;
-            st.koff[bk][kb] = pos * kD + (((2 * kb + g) ^ swz(pos)) << 3);
+            st.koff[bk][kb] = 2 * (pos * kD + (((2 * kb + g) ^ swz(pos)) << 3));
         }
     //  V (A of O^T, transposing read): in 16-lane group G, lane i addresses row
     //  i/4 of a 4-row slab and dims 4*(i%4) .. +3 of the 16-dim slab
@@ -507,7 +596,7 @@ __device__ __forceinline__ void attend_query_tile(
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
             const int col = 32 * db + 16 * G1 + 4 * (i & 3);
-            st.voff[db] = row * kD + ((((col >> 3) ^ swz_v(row))) << 3) + (col & 7);
+            st.voff[db] = 2 * (row * kD + ((((col >> 3) ^ swz_v(row))) << 3) + (col & 7));
         }
     }
 
@@ -517,29 +606,27 @@ __device__ __forceinline__ void attend_query_tile(
     st.l_run = 0.f;               // this lane's part of the running sum
 
     st.ld.init(wave, lane);
-    if (st.n_tiles > 0) st.ld.issue(st.Kh, st.Vh, 0, len, lds, lds + A::kTileElems);
+    if (st.n_tiles > 0) st.prefetch(0, st.kbuf[0], st.vbuf[0]);
+    if (A::kBuffers == 3 && st.n_tiles > 1) st.prefetch(1, st.kbuf[1], st.vbuf[1]);
 
-    for (int t = 0; t < st.n_tiles; t += 2) {
-        st.template tile<0>(t);
-        if (t + 1 < st.n_tiles) st.template tile<1>(t + 1);
-    }
+    st.run();
 
     // ---- epilogue: O = acc / l, rounded to bf16
     acc_read_fence();
     const float l_tot = sum_across_halves(st.l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
-    if (row_ok) {
-        uint16_t *o = O + tile_base;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(O + tile_base), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                u32x2_t w;
-                w[0] = pack_bf16x2(st.acc[db][4 * rq + 0] * inv, st.acc[db][4 * rq + 1] * inv);
-                w[1] = pack_bf16x2(st.acc[db][4 * rq + 2] * inv, st.acc[db][4 * rq + 3] * inv);
-                *(u32x2_t *)(o + (l32 * kD + db * 32 + rq * 8 + g * 4)) = w;
-            }
-    }
+        for (int rq4 = 0; rq4 < 4; ++rq4) {
+            u32x2_t w;
+            w[0] = pack_bf16x2(st.acc[db][4 * rq4 + 0] * inv, st.acc[db][4 * rq4 + 1] * inv);
+            w[1] = pack_bf16x2(st.acc[db][4 * rq4 + 2] * inv, st.acc[db][4 * rq4 + 3] * inv);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                w, ro, (uint32_t)(l32 * kRowBytes + (db * 32 + rq4 * 8 + g * 4) * 2), 0, 0);
+        }
 }
 
 // Work decomposition.  A workgroup handles one query tile, or, for long causal
@@ -557,7 +644,14 @@ __global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kern
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
     uint32_t n_qtiles, uint32_t n_bh, uint32_t items_per_head, int pair)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * Attn<NW, NB>::kTileElems];
+    using A = Attn<NW, NB>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
+    uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
+#pragma unroll
+    for (int i = 0; i < A::kBuffers; ++i) {
+        kbuf[i] = lds + i * A::kBufStride;
+        vbuf[i] = kbuf[i] + A::kTileElems;
+    }
 
     const int lane = threadIdx.x & 63;
     // wave index as a scalar (it is uniform across the wave)
@@ -575,7 +669,7 @@ __global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kern
     const int n_work = (pair && p != first) ? 2 : 1;
     for (int w = 0; w < n_work; ++w) {
         if (w > 0) __syncthreads();   // every wave is done with the previous tile's LDS
-        attend_query_tile<NW, NB>(lds, Q, K, V, key_lengths, causal, O, H, Lq, Lk, scale_log2,
+        attend_query_tile<NW, NB>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk, scale_log2,
                                   bh, w == 0 ? first : p, wave, lane);
     }
 }

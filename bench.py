@@ -10,7 +10,10 @@ workloads (--config) are available for profiling; they are parity cases, not
 headline lines.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
-                  [--no-cpu-baseline] [--rotate R]
+                  [--no-cpu-baseline] [--rotate R] [--settle-ms MS]
+
+After the W warmup steps, untimed steps continue until the GPU has been busy for
+--settle-ms (default 150 ms), so that the K timed steps see the settled clock.
 
 FLOPs are algorithmic: (2*d_k + 2*d_v) per (query, key) pair the mask allows
 (page "Attention Is All You Need/paper/es", §4, Table 1: O(n^2 d) per layer),
@@ -137,8 +140,11 @@ def copy_calibration(torch, dev, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="after the warmup steps, keep launching untimed steps until the "
+                         "GPU has been busy this long (its clock settles within ~50 ms)")
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -206,6 +212,16 @@ def main():
     for n in range(args.warmup):
         step(n)
     torch.cuda.synchronize()
+    # MI355X raises its clock over the first tens of milliseconds of sustained
+    # work; launches in that window run up to ~30% slower.  Keep the GPU busy
+    # (untimed) until it has run for settle_ms, in batches of launches.
+    settle_steps = 0
+    t_busy = time.perf_counter()
+    while (time.perf_counter() - t_busy) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -245,7 +261,8 @@ def main():
 
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": settle_steps,
+        "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": c.dtype, "data": "synthetic",
         "config": {"workload": c.name, "description": c.description, "B": c.B, "h": c.H,

@@ -86,9 +86,6 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #ifndef SDPA_MFMA_KEY_BLOCKS
 #define SDPA_MFMA_KEY_BLOCKS 2    // 32-key blocks per LDS tile
 #endif
-#ifndef SDPA_MFMA_BUFFERS
-#define SDPA_MFMA_BUFFERS 3       // LDS tile buffers (prefetch distance = buffers - 1)
-#endif
 #ifndef SDPA_MFMA_WAVES_PER_SIMD
 #define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget for 3 waves per SIMD (0: no hint)
 #endif
@@ -224,6 +221,8 @@ struct TileLoader {
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 template <int N>
 __device__ inline void wait_vmem_keep() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(N)); }
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima.
+constexpr int kWaitLds0 = 15 | (3 << 14) | (7 << 4);
 
 // Per-wave state of the forward pass and the work on one key tile.
 template <int NW, int NB>
@@ -231,9 +230,11 @@ struct Attn {
     static constexpr int BM = 32 * NW;
     static constexpr int BN = 32 * NB;
     static constexpr int kTileElems = BN * kD;   // bf16 elements per K (or V) tile
-    static constexpr int kBuffers = SDPA_MFMA_BUFFERS;
+    static constexpr int kBuffers = 3;                  // LDS ring: tiles t, t+1 read, t+2 landing
     static constexpr int kBufStride = 2 * kTileElems;   // K tile, then V tile, per buffer
-    static_assert(kBuffers == 2 || kBuffers == 3, "two or three LDS tile buffers");
+    // Q is staged in buffer 2 before tile 2 arrives: each wave's 32 Q rows sit
+    // exactly where its own share of tile 2's copies will land.
+    static_assert(2 * BN / NW == 32, "a wave's share of one tile's K and V rows holds its Q rows");
 
     uint16_t *kbuf[kBuffers], *vbuf[kBuffers];   // LDS tile buffers
     const uint16_t *Kh, *Vh;
@@ -247,6 +248,7 @@ struct Attn {
 
     TileLoader<NW, BN> ld;
     bf16x8_t qf[4];                  // Q^T operand (B of S^T = K Q^T)
+    int wave;                        // wave index in the workgroup (uniform)
     int koff[2][4];                  // LDS byte offsets of K reads (blocks of even/odd parity)
     int voff[2];                     // LDS byte offsets of V transposing reads
     f32x16_t acc[2];                 // O^T: dims 32*db + 8*(r/4) + 4*g + r%4, this lane's query row
@@ -364,64 +366,110 @@ struct Attn {
         return sum;
     }
 
-    // Blocks 0..NBLK-1 of a tile, software-pipelined: in each straight-line
-    // stretch the matrix core has S of block b+1 and/or P.V of block b-1 while
-    // the VALU works on block b.  P.V of block b-1 is always issued before block
-    // b's rescale decision, so moving a reference maximum only rescales the
-    // accumulator and the row sum.  Decisions are per row, so a row's result
-    // depends on its own legal keys only.
-    //
-    //  kMaxFree: no block maximum (the tile is fully legal and every row holds
-    //    a finite reference).  Weights are taken against the reference; only if
-    //    a row's block sum passes kSumMax (a score grew by more than
-    //    log2(kSumMax / 32) over the reference) does that row move its
-    //    reference to the block maximum and recompute the block.
-    //  kBlockMax: block maxima, reference moved when one exceeds it by kTau.
-    //    kMask additionally sets illegal scores to -inf: key
-    //    kv0 + 32*b + 16*(r/8) + 8*g + r%8 is legal iff that offset < lim.
-    enum Mode { kMaxFree, kBlockMax, kMask };
+    // Scheduling of one straight-line stretch of a fully legal tile (block b's
+    // weights on the VALU; S of block b+1 or of the next tile's block 0, and
+    // P.V of block b-1, on the matrix core): the compiler would otherwise issue
+    // the stretch's MFMAs back to back and leave the wave without matrix work
+    // while its VALU runs.  The LDS reads go first, then each MFMA is followed
+    // by a group of VALU instructions.  Masks: 0x100 LDS read, 0x008 MFMA,
+    // 0x002 VALU.
+    __device__ __forceinline__ static void mfma_then_valu(int n)
+    {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < n) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+    }
 
-    template <Mode M, int NBLK>
-    __device__ __forceinline__ void tile_blocks(const uint16_t *Ks, const uint16_t *Vs, int lim)
+    __device__ __forceinline__ static void interleave_stretch(int b)
+    {
+        if (b == 0) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // K reads of S
+            mfma_then_valu(4);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // V reads of P.V, K reads of S
+            mfma_then_valu(8);
+        }
+    }
+
+    // Block b of a fully legal tile (every row holds a finite reference
+    // maximum), after its weights were taken against the reference (bsum = the
+    // row's block sum): only if a row's block sum passes kSumMax (a score grew
+    // by more than log2(kSumMax / 32) over the reference) does that row move its
+    // reference to the block maximum and recompute the block.  P.V of block b-1
+    // is already issued, so moving a reference only rescales the accumulator
+    // and the row sum.
+    __device__ __forceinline__ void finish_max_free(const f32x16_t &s, bf16x8_t *p, float bsum)
     {
         constexpr float kSumMax = 1048576.0f;   // 2^20
-        f32x16_t s[NBLK];
-        bf16x8_t p[NBLK][2];
+        const bool grow = !(bsum <= kSumMax);
+        if (__builtin_expect(__any(grow), 0)) {
+            asm volatile("" ::: "memory");   // keep the rare path a real branch
+            const float mxs = block_max(s);
+            if (grow) {
+                scale_pending(__builtin_amdgcn_exp2f(m_run - mxs), nullptr);
+                m_run = mxs;
+            }
+            const float redo = weights(s, p);
+            bsum = grow ? redo : bsum;
+        }
+        l_run += bsum;
+    }
+
+    // A fully legal tile after the first, software-pipelined across tiles: S of
+    // its block 0 was computed by the previous tile (s_io in); while block b's
+    // weights run on the VALU, the matrix core has S of block b+1 (for the last
+    // block: S of the next tile's block 0, from Knext, into s_io) and P.V of
+    // block b-1.  The next tile's K is in LDS: every wave waited for all its
+    // copies before this tile's barrier.  When there is no next tile the buffer
+    // holds older data and that result is not used.
+    __device__ __forceinline__ void tile_blocks_full(const uint16_t *Ks, const uint16_t *Vs,
+                                                     const uint16_t *Knext, f32x16_t &s_io)
+    {
+        f32x16_t s[NB];
+        bf16x8_t p[NB][2];
+        s[0] = s_io;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
+            else s_io = scores(Knext, 0);
+            const float bsum = weights(s[b], p[b]);   // no block maximum
+            if (b > 0) pv(Vs, b - 1, p[b - 1]);
+            interleave_stretch(b);   // in the same straight-line stretch as the above
+            finish_max_free(s[b], p[b], bsum);
+        }
+        pv(Vs, NB - 1, p[NB - 1]);
+    }
+
+    // Any other tile (the first, one crossing the causal diagonal or the
+    // padding end, one beyond this wave's rows) block by block, with block
+    // maxima and masks: key kv0 + 32*b + 16*(r/8) + 8*g + r%8 is legal iff
+    // that offset < lim.  On the first tile the block maxima set every row's
+    // reference maximum (key 0 is legal for every row when len > 0).  A block
+    // with no legal key for any row of the wave contributes exactly 0.
+    // Decisions are per row, so a row's result depends on its own legal keys
+    // only.
+    __device__ __forceinline__ void tile_blocks_masked(const uint16_t *Ks, const uint16_t *Vs, int lim)
+    {
+        f32x16_t s[NB];
+        bf16x8_t p[NB][2];
         s[0] = scores(Ks, 0);
 #pragma unroll
-        for (int b = 0; b < NBLK; ++b) {
-            if constexpr (M == kMaxFree) {
-                if (b + 1 < NBLK) s[b + 1] = scores(Ks, b + 1);
-                float bsum = weights(s[b], p[b]);
-                if (b > 0) pv(Vs, b - 1, p[b - 1]);
-                const bool grow = !(bsum <= kSumMax);
-                if (__builtin_expect(__any(grow), 0)) {
-                    asm volatile("" ::: "memory");   // keep the rare path a real branch
-                    const float mxs = block_max(s[b]);
-                    if (grow) {
-                        scale_pending(__builtin_amdgcn_exp2f(m_run - mxs), nullptr);
-                        m_run = mxs;
-                    }
-                    const float redo = weights(s[b], p[b]);
-                    bsum = grow ? redo : bsum;
-                }
-                l_run += bsum;
-            } else {
-                if constexpr (M == kMask) {
-                    // the per-register part is a constant compared with lim - 8g - 32b
-                    const int lim_g = lim - 8 * g - 32 * b;
+        for (int b = 0; b < NB; ++b) {
+            // the per-register part is a constant compared with lim - 8g - 32b
+            const int lim_g = lim - 8 * g - 32 * b;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;
-                }
-                const float mxs = block_max(s[b]);
-                if (b > 0) pv(Vs, b - 1, p[b - 1]);
-                rescale_if_needed(mxs);
-                if (b + 1 < NBLK) s[b + 1] = scores(Ks, b + 1);
-                l_run += weights(s[b], p[b]);
-            }
+            for (int r = 0; r < 16; ++r)
+                if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;
+            const float mxs = block_max(s[b]);
+            if (b > 0) pv(Vs, b - 1, p[b - 1]);
+            rescale_if_needed(mxs);
+            if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
+            l_run += weights(s[b], p[b]);
         }
-        pv(Vs, NBLK - 1, p[NBLK - 1]);
+        pv(Vs, NB - 1, p[NB - 1]);
     }
 
     // Issue the copies of tile u into buffer u % kBuffers.
@@ -430,60 +478,66 @@ struct Attn {
         ld.issue(Kh, Vh, (int64_t)u * BN, len, kb, vb);
     }
 
-    // Start of tile t, the same for every wave and every kind of tile (one
-    // barrier per tile): tile t has landed once at most the copies of the tiles
-    // after it that were already issued are outstanding; after the barrier every
-    // wave's copies of tile t are in LDS and every wave is done with tile t-1,
-    // whose buffer takes tile t + kBuffers - 1.
-    __device__ __forceinline__ void tile_begin(int t, uint16_t *knext, uint16_t *vnext)
+    // Q^T as the B operand of the score MFMA, from where the prologue staged it
+    // in buffer 2: the lane's query row l32, dims 16*kb + 8*g .. +7 (logical
+    // chunk 2*kb + g, stored at chunk (2*kb + g) ^ swz(l32)).
+    __device__ __forceinline__ void read_q()
     {
-        if (kBuffers == 3 && t + 1 < n_tiles)
-            wait_vmem_keep<TileLoader<NW, BN>::kLoadsPerTile>();
-        else
-            wait_vmem_keep<0>();
-        __syncthreads();
-        // Q arrived with the first tile's copies: tie its registers to the wait.
-        asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]));
-        if (t + kBuffers - 1 < n_tiles) prefetch(t + kBuffers - 1, knext, vnext);
+        const uint16_t *row = (l32 < 16 ? kbuf[2] : vbuf[2]) + (16 * wave + (l32 & 15)) * kD;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            qf[kb] = *(const bf16x8_t *)(row + (((2 * kb + g) ^ swz(l32)) << 3));
     }
 
-    // A fully legal tile after the first, in LDS buffer BUF = t % kBuffers.
+    // Start of tile t, the same for every wave and every kind of tile (one
+    // barrier per tile).  Before the barrier each wave waits for all its copies
+    // in flight, tiles t and t+1 (and Q at t = 0); after it, tiles t and t+1
+    // are in LDS for every wave and every wave is done with tile t-1, whose
+    // buffer takes tile t+2.  At t = 0 the wave first reads its Q rows, which
+    // lie where its own copies of tile 2 land.
+    __device__ __forceinline__ void tile_begin(int t, uint16_t *knext, uint16_t *vnext)
+    {
+        wait_vmem_keep<0>();
+        __syncthreads();
+        if (t == 0) {
+            read_q();
+            __builtin_amdgcn_s_waitcnt(kWaitLds0);
+        }
+        if (t + 2 < n_tiles) prefetch(t + 2, knext, vnext);
+    }
+
+    // A fully legal tile after the first, in LDS buffer BUF = t % 3.
     // Instantiated per buffer so that every LDS operand address is a per-lane
     // register plus an immediate offset.
     template <int BUF>
-    __device__ __forceinline__ void tile_full(int t)
+    __device__ __forceinline__ void tile_full(int t, f32x16_t &s_io)
     {
-        constexpr int kNext = (BUF + kBuffers - 1) % kBuffers;
-        tile_begin(t, kbuf[kNext], vbuf[kNext]);
-        tile_blocks<kMaxFree, NB>(kbuf[BUF], vbuf[BUF], BN);
+        tile_begin(t, kbuf[(BUF + 2) % 3], vbuf[(BUF + 2) % 3]);
+        tile_blocks_full(kbuf[BUF], vbuf[BUF], kbuf[(BUF + 1) % 3], s_io);
     }
 
-    // Any other tile (the first, one crossing the causal diagonal or the
-    // padding end, one beyond this wave's rows, or a full one left over from
-    // the unrolled loop), with the buffer chosen at run time.
+    // Any other tile, with the buffer chosen at run time.
     __device__ __forceinline__ void tile_any(int t)
     {
-        const int buf = t % kBuffers;
-        const int nxt = (t + kBuffers - 1) % kBuffers;
+        const int buf = t % 3;
+        const int nxt = (t + 2) % 3;
         tile_begin(t, kbuf[0] + nxt * kBufStride, vbuf[0] + nxt * kBufStride);
         const int64_t kv0 = (int64_t)t * BN;
         // A wave whose rows all precede the tile's first key has nothing to do.
         if (causal && kv0 > q0w + 31) return;
         // Keys this lane may use in the tile: below the key length and, if
-        // causal, up to its own row.  (A block with no legal key for any row
-        // of the wave is computed and contributes exactly 0.)  On the first
-        // tile the block maxima set every row's reference maximum (key 0 is
-        // legal for every row when len > 0).
+        // causal, up to its own row.
         int64_t lim64 = len - kv0;
         const int64_t causal_lim = (q0w - kv0) + l32 + 1;
         if (causal && causal_lim < lim64) lim64 = causal_lim;
         const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));
-        tile_blocks<kMask, NB>(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim);
+        tile_blocks_masked(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim);
     }
 
     // All key tiles: the first, then the fully legal ones in a loop unrolled
-    // over the buffer ring (no per-tile branches on the tile kind), then the
-    // rest.  Every wave passes the same number of barriers (one per tile).
+    // over the buffer ring (no per-tile branch on the tile kind), then the
+    // rest.  Every wave passes the same number of barriers (one per tile); the
+    // waves of a workgroup may switch between the phases at different tiles.
     __device__ __forceinline__ void run()
     {
         if (n_tiles == 0) return;
@@ -495,21 +549,14 @@ struct Attn {
         }
         for (int t = 0; t < n_tiles;) {
             if (t == 1 && n_full > 1) {
-                if constexpr (kBuffers == 3) {
-                    for (; t + 2 < n_full; t += 3) {
-                        tile_full<1>(t);
-                        tile_full<2>(t + 1);
-                        tile_full<0>(t + 2);
-                    }
-                    if (t < n_full) tile_full<1>(t++);
-                    if (t < n_full) tile_full<2>(t++);
-                } else {
-                    for (; t + 1 < n_full; t += 2) {
-                        tile_full<1>(t);
-                        tile_full<0>(t + 1);
-                    }
-                    if (t < n_full) tile_full<1>(t++);
+                f32x16_t s_io = scores(kbuf[1], 0);   // tile 1 landed before tile 0's barrier
+                for (; t + 2 < n_full; t += 3) {
+                    tile_full<1>(t, s_io);
+                    tile_full<2>(t + 1, s_io);
+                    tile_full<0>(t + 2, s_io);
                 }
+                if (t < n_full) tile_full<1>(t++, s_io);
+                if (t < n_full) tile_full<2>(t++, s_io);
             } else {
                 tile_any(t++);
             }
@@ -562,18 +609,7 @@ __device__ __forceinline__ void attend_query_tile(
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(Q + tile_base), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
 
-    // Q^T as the B operand of the score MFMA: lane holds its query row, dims
-    // 16*kb + 8*g .. +7 for kb = 0..3.  Loaded by inline assembly so that the
-    // compiler does not wait for these loads with vmcnt(0) inside the tile loop
-    // (which would also drain the tile copies in flight); the first tile's
-    // wait covers them, and Attn::tile re-defines qf after each wait.
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        u32x4_t t;
-        const uint32_t voff = (uint32_t)(l32 * kRowBytes + (kb * 16 + g * 8) * 2);
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(t) : "v"(voff), "s"(rq) : "memory");
-        st.qf[kb] = as_bf16x8(t);
-    }
+    st.wave = wave;
 
     // LDS byte offsets of this lane's operand reads.
     //  K (A of S^T): row pos = 32*bk + l32, dims 16*kb + 8*g .. +7; swz(pos)
@@ -606,8 +642,19 @@ __device__ __forceinline__ void attend_query_tile(
     st.l_run = 0.f;               // this lane's part of the running sum
 
     st.ld.init(wave, lane);
-    if (st.n_tiles > 0) st.prefetch(0, st.kbuf[0], st.vbuf[0]);
-    if (A::kBuffers == 3 && st.n_tiles > 1) st.prefetch(1, st.kbuf[1], st.vbuf[1]);
+    if (st.n_tiles > 0) {
+        // This wave's 32 Q rows into buffer 2 (rows 0-15 where its share of
+        // tile 2's K rows lands, rows 16-31 where its V rows land), 8 rows per
+        // copy, chunks swizzled by the row; then tiles 0 and 1.
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            const int qrow = 8 * sl + (lane >> 3);
+            const uint16_t *dst = (sl < 2 ? st.kbuf[2] : st.vbuf[2]) + (16 * wave + 8 * (sl & 1)) * kD;
+            copy_to_lds(rq, dst, (uint32_t)(qrow * kRowBytes + (((lane & 7) ^ swz(qrow)) << 4)));
+        }
+        st.prefetch(0, st.kbuf[0], st.vbuf[0]);
+    }
+    if (st.n_tiles > 1) st.prefetch(1, st.kbuf[1], st.vbuf[1]);
 
     st.run();
 

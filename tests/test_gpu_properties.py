@@ -196,3 +196,36 @@ def test_stream_ordering_on_side_stream():
         out = sdpa.forward(dq, dk, dv, key_lengths=kl)
     s.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lds_left_by_earlier_launches_never_reaches_result(causal):
+    """Launches whose K/V are all NaN (and an fp32 launch) leave NaN bit patterns in
+    LDS; a following ragged launch must still match the oracle exactly as it does
+    from a clean state: rows past the key length are zero-filled, and no operand
+    is read before its copy has landed."""
+    dev = require_gpu()
+    B, H, Lq, Lk = 16, 4, 256, 256
+    q, k, v, _ = workloads.draw(B, H, Lq, Lk, 64, 64, dtype="bf16", seed=81)
+    lengths = [100, 130, 200, 250, 256, 64, 65, 191] * 2
+    ref = oracle.attention(q, k, v, key_lengths=lengths, causal=causal)
+    nan = torch.full((B, H, Lk, 64), float("nan"), device=dev, dtype=torch.bfloat16)
+    zq = torch.zeros((B, H, Lq, 64), device=dev, dtype=torch.bfloat16)
+    t = workloads.generate("tiny_causal_f32")
+    tq, tk, tv = (to_dev(a, torch.float32) for a in (t.q, t.k, t.v))
+    dq, dk, dv = (to_dev(a, torch.bfloat16) for a in (q, k, v))
+    kl = torch.as_tensor(np.asarray(lengths, np.int32)).to(dev)
+    announce("stale LDS causal=%d" % causal)
+    first = None
+    for rep in range(4):
+        sdpa.forward(zq, nan, nan)
+        sdpa.forward(tq, tk, tv, causal=True)
+        out = sdpa.forward(dq, dk, dv, key_lengths=kl, causal=causal)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), "repetition %d" % rep
+        if first is None:
+            first = got
+            assert_parity(got, ref, v, "bf16", "after NaN-filled launches")
+        else:
+            assert np.array_equal(got, first)

@@ -55,10 +55,10 @@
 //    The first tile and tiles crossing the causal diagonal or the padding end
 //    compute block maxima; only the latter apply masks.  Tiles entirely beyond the key
 //    length are never loaded.
-//  * Work order: head-major, spread over the 8 XCDs in contiguous runs so
-//    the workgroups streaming one head's K/V share an L2; long causal grids
-//    pair query tiles p and n-1-p in one workgroup (equal work per
-//    workgroup), short ones run each head's longest tiles first.
+//  * Work order: one query tile per workgroup, each XCD on its own run of
+//    heads so the workgroups streaming one head's K/V share an L2; causal
+//    grids dispatch the longest query tiles first (greedy longest-first over
+//    the workgroup slots, which the hardware dispatcher fills in order).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -676,20 +676,22 @@ __device__ __forceinline__ void attend_query_tile(
         }
 }
 
-// Work decomposition.  A workgroup handles one query tile, or, for long causal
-// grids (pair = 1), the two query tiles p and n_qtiles-1-p of one head, whose
-// key ranges add up to the same length for every p.  Workgroups are numbered
-// head-major (all the tiles of a head are consecutive) and the numbering is
-// spread over the 8 XCDs in contiguous runs: the hardware hands workgroup w to
-// XCD w % 8, so workgroup w takes item (w % 8) * (T / 8) + w / 8 when 8 divides
-// the item count T.  Each XCD then works on a few heads at a time, and the
-// workgroups streaming the same K/V rows share that XCD's L2.
+// Work decomposition: one query tile (qt, head bh) per workgroup.  The
+// hardware hands workgroup w to XCD w % 8 and, within an XCD, starts
+// workgroups in order of w as slots free up.
+//  * Non-causal: item (w % 8) * (T / 8) + w / 8 when 8 divides the item count
+//    T, numbered head-major: each XCD works on a contiguous run of heads, and
+//    the workgroups streaming the same K/V rows share that XCD's L2.
+//  * Causal: a query tile's work grows with qt, so the tiles go out longest
+//    first (qt descending), which fills the slots greedily longest-first and
+//    leaves only short tiles for the end of the grid; when 8 divides the head
+//    count each XCD still takes its own run of heads.
 template <int NW, int NB>
 __global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
-    uint32_t n_qtiles, uint32_t n_bh, uint32_t items_per_head, int pair)
+    uint32_t n_qtiles, uint32_t n_bh)
 {
     using A = Attn<NW, NB>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
@@ -704,21 +706,25 @@ __global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kern
     // wave index as a scalar (it is uniform across the wave)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    const uint32_t n_items = items_per_head * n_bh;
-    uint32_t item = blockIdx.x;
-    if ((n_items & 7) == 0) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
-    const uint32_t bh = item / items_per_head;
-    const uint32_t p = item % items_per_head;
-
-    // pair: the long tile n_qtiles-1-p, then (if different) the short tile p;
-    // otherwise one tile, and for causal grids each head's longest tiles first.
-    const uint32_t first = (pair || causal) ? n_qtiles - 1 - p : p;
-    const int n_work = (pair && p != first) ? 2 : 1;
-    for (int w = 0; w < n_work; ++w) {
-        if (w > 0) __syncthreads();   // every wave is done with the previous tile's LDS
-        attend_query_tile<NW, NB>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk, scale_log2,
-                                  bh, w == 0 ? first : p, wave, lane);
+    const uint32_t w = blockIdx.x;
+    uint32_t bh, qt;
+    if (causal) {
+        if ((n_bh & 7) == 0) {
+            const uint32_t hx = n_bh >> 3, j = w >> 3;   // heads per XCD, position in the XCD
+            bh = (w & 7) * hx + j % hx;
+            qt = n_qtiles - 1 - j / hx;
+        } else {
+            bh = w % n_bh;
+            qt = n_qtiles - 1 - w / n_bh;
+        }
+    } else {
+        const uint32_t n_items = n_qtiles * n_bh;
+        const uint32_t item = (n_items & 7) == 0 ? (w & 7) * (n_items >> 3) + (w >> 3) : w;
+        bh = item / n_qtiles;
+        qt = item % n_qtiles;
     }
+    attend_query_tile<NW, NB>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk, scale_log2,
+                              bh, qt, wave, lane);
 }
 
 }  // namespace
@@ -732,15 +738,11 @@ hipError_t launch_mfma_d64(const void *Q, const void *K, const void *V,
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
-    // Pair the query tiles of long causal grids (balanced work per workgroup);
-    // short grids keep one tile per workgroup for parallelism.
-    const int pair = (causal && n_qtiles >= 16) ? 1 : 0;
-    const uint32_t items_per_head = pair ? (n_qtiles + 1) / 2 : n_qtiles;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
-    hipLaunchKernelGGL((sdpa_fwd_mfma_d64_kernel<NW, NB>), dim3(items_per_head * n_bh),
+    hipLaunchKernelGGL((sdpa_fwd_mfma_d64_kernel<NW, NB>), dim3(n_qtiles * n_bh),
                        dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
                        (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
-                       scale_log2, n_qtiles, n_bh, items_per_head, pair);
+                       scale_log2, n_qtiles, n_bh);
     return hipGetLastError();
 }
 

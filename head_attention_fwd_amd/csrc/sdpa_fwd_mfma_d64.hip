@@ -86,6 +86,9 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #ifndef SDPA_MFMA_KEY_BLOCKS
 #define SDPA_MFMA_KEY_BLOCKS 2    // 32-key blocks per LDS tile
 #endif
+#ifndef SDPA_STORE_LDS
+#define SDPA_STORE_LDS 1
+#endif
 #ifndef SDPA_MFMA_WAVES_PER_SIMD
 #define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget for 3 waves per SIMD (0: no hint)
 #endif
@@ -664,6 +667,32 @@ __device__ __forceinline__ void attend_query_tile(
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(O + tile_base), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
+#if SDPA_STORE_LDS
+    // The wave's 32 x 64 output tile goes through LDS so that every store
+    // instruction writes 8 whole rows (1 KiB contiguous): written in the
+    // accumulator layout (lane: row l32, 8-byte pieces of 16-byte chunk
+    // 4*db + rq4), read back as row 8*i + lane/8, chunk lane%8.  Chunks are
+    // XOR-swizzled by the row.  The barrier makes sure every wave is done with
+    // the tile buffers this reuses (no copies are in flight after the last tile).
+    __syncthreads();
+    uint16_t *stage = kbuf[0] + wave * 32 * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int rq4 = 0; rq4 < 4; ++rq4) {
+            u32x2_t w;
+            w[0] = pack_bf16x2(st.acc[db][4 * rq4 + 0] * inv, st.acc[db][4 * rq4 + 1] * inv);
+            w[1] = pack_bf16x2(st.acc[db][4 * rq4 + 2] * inv, st.acc[db][4 * rq4 + 3] * inv);
+            const int c = 4 * db + rq4;
+            *(u32x2_t *)((char *)stage + l32 * kRowBytes + ((c ^ (l32 & 7)) << 4) + 8 * g) = w;
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * i + (lane >> 3), c = lane & 7;
+        const u32x4_t w = *(const u32x4_t *)((const char *)stage + r * kRowBytes + ((c ^ (r & 7)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(r * kRowBytes + c * 16), 0, 0);
+    }
+#else
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -674,6 +703,7 @@ __device__ __forceinline__ void attend_query_tile(
             __builtin_amdgcn_raw_buffer_store_b64(
                 w, ro, (uint32_t)(l32 * kRowBytes + (db * 32 + rq4 * 8 + g * 4) * 2), 0, 0);
         }
+#endif
 }
 
 // Work decomposition: one query tile (qt, head bh) per workgroup.  The

@@ -15,11 +15,15 @@ from ._binding import (  # noqa: F401
     SDPA_ERR_HIP,
     SDPA_ERR_NULL_POINTER,
     SDPA_ERR_UNSUPPORTED,
+    SDPA_ERR_WORKSPACE,
     SDPA_F32,
     SDPA_OK,
     SdpaError,
+    decode,
     forward,
     load_library,
+    sdpa_decode,
+    sdpa_decode_workspace_bytes,
     sdpa_forward,
     sdpa_last_hip_error,
     sdpa_status_str,

@@ -18,12 +18,14 @@ SDPA_ERR_BAD_SHAPE = 2
 SDPA_ERR_UNSUPPORTED = 3
 SDPA_ERR_ALIAS = 4
 SDPA_ERR_HIP = 5
+SDPA_ERR_WORKSPACE = 6
 
 SDPA_F32 = 0
 SDPA_BF16 = 1
 
 #: Symbols include/sdpa.h declares.
-EXPORTED = ("sdpa_forward", "sdpa_status_str", "sdpa_last_hip_error")
+EXPORTED = ("sdpa_decode", "sdpa_decode_workspace_bytes", "sdpa_forward", "sdpa_last_hip_error",
+            "sdpa_status_str")
 
 _lib = None
 
@@ -31,8 +33,8 @@ _lib = None
 class SdpaError(RuntimeError):
     """A non-zero sdpa_status returned by the library."""
 
-    def __init__(self, status: int, message: str):
-        super().__init__("sdpa_forward failed (%d): %s" % (status, message))
+    def __init__(self, status: int, message: str, entry: str = "sdpa_forward"):
+        super().__init__("%s failed (%d): %s" % (entry, status, message))
         self.status = status
 
 
@@ -49,6 +51,11 @@ def load_library(path: str = LIBRARY):
     lib.sdpa_forward.restype = ctypes.c_int
     lib.sdpa_forward.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64,
                                  i64, ctypes.c_int, vp]
+    lib.sdpa_decode.restype = ctypes.c_int
+    lib.sdpa_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                vp, i64, vp]
+    lib.sdpa_decode_workspace_bytes.restype = i64
+    lib.sdpa_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.sdpa_status_str.restype = ctypes.c_char_p
     lib.sdpa_status_str.argtypes = [ctypes.c_int]
     lib.sdpa_last_hip_error.restype = ctypes.c_int
@@ -66,6 +73,20 @@ def sdpa_forward(Q: int, K: int, V: int, key_lengths: int, causal: int, out: int
                                        int(dtype), stream or None)
 
 
+def sdpa_decode(Q: int, K: int, V: int, key_lengths: int, out: int, B: int, H: int, Lq: int,
+                Lk: int, d_k: int, d_v: int, dtype: int, workspace: int, workspace_bytes: int,
+                stream: int) -> int:
+    """Raw C call; pointers and the stream are integers (0 = NULL).  Returns the status."""
+    return load_library().sdpa_decode(Q or None, K or None, V or None, key_lengths or None,
+                                      out or None, B, H, Lq, Lk, d_k, d_v, int(dtype),
+                                      workspace or None, workspace_bytes, stream or None)
+
+
+def sdpa_decode_workspace_bytes(B: int, H: int, Lq: int, Lk: int, d_k: int, d_v: int,
+                                dtype: int) -> int:
+    return load_library().sdpa_decode_workspace_bytes(B, H, Lq, Lk, d_k, d_v, int(dtype))
+
+
 def sdpa_status_str(status: int) -> str:
     return load_library().sdpa_status_str(int(status)).decode()
 
@@ -74,15 +95,8 @@ def sdpa_last_hip_error() -> int:
     return load_library().sdpa_last_hip_error()
 
 
-def forward(q, k, v, key_lengths=None, causal: bool = False, out=None):
-    """Attention forward on torch CUDA tensors (HIP on ROCm).
-
-    q [B,H,Lq,d_k], k [B,H,Lk,d_k], v [B,H,Lk,d_v]: contiguous, one dtype
-    (torch.float32 or torch.bfloat16), one device.  key_lengths: None, or an
-    int32 tensor [B] on that device (other integer sequences are copied there).
-    out: optional preallocated contiguous [B,H,Lq,d_v] tensor of the same dtype.
-    The kernel is enqueued on the device's current stream; returns out.
-    """
+def _check(q, k, v, key_lengths, out):
+    """Validate torch tensors for the calls below; returns (sizes, dtype code, key_lengths, out)."""
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -119,14 +133,62 @@ def forward(q, k, v, key_lengths=None, causal: bool = False, out=None):
     elif tuple(out.shape) != (B, H, Lq, d_v) or out.dtype != q.dtype or out.device != dev or \
             not out.is_contiguous():
         raise ValueError("out must be a contiguous [B,H,Lq,d_v] tensor like q")
+    return (B, H, Lq, Lk, d_k, d_v), dtype, key_lengths, out
+
+
+def _raise(st, entry):
+    if st != SDPA_OK:
+        msg = sdpa_status_str(st)
+        if st == SDPA_ERR_HIP:
+            msg += " (hipError %d)" % sdpa_last_hip_error()
+        raise SdpaError(st, msg, entry)
+
+
+def forward(q, k, v, key_lengths=None, causal: bool = False, out=None):
+    """Attention forward on torch CUDA tensors (HIP on ROCm).
+
+    q [B,H,Lq,d_k], k [B,H,Lk,d_k], v [B,H,Lk,d_v]: contiguous, one dtype
+    (torch.float32 or torch.bfloat16), one device.  key_lengths: None, or an
+    int32 tensor [B] on that device (other integer sequences are copied there).
+    out: optional preallocated contiguous [B,H,Lq,d_v] tensor of the same dtype.
+    The kernel is enqueued on the device's current stream; returns out.
+    """
+    import torch
+
+    (B, H, Lq, Lk, d_k, d_v), dtype, key_lengths, out = _check(q, k, v, key_lengths, out)
+    dev = q.device
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = sdpa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                           0 if key_lengths is None else key_lengths.data_ptr(), int(bool(causal)),
                           out.data_ptr(), B, H, Lq, Lk, d_k, d_v, dtype, stream)
-    if st != SDPA_OK:
-        msg = sdpa_status_str(st)
-        if st == SDPA_ERR_HIP:
-            msg += " (hipError %d)" % sdpa_last_hip_error()
-        raise SdpaError(st, msg)
+    _raise(st, "sdpa_forward")
+    return out
+
+
+def decode(q, k, v, key_lengths=None, out=None, workspace=None):
+    """Decode-step attention (sdpa_decode): the result of forward(..., causal=False)
+    for a few query rows per head against a long key/value cache.
+
+    Tensors as for forward().  workspace: optional uint8 tensor on the device of
+    at least sdpa_decode_workspace_bytes(...) bytes; allocated here when None.
+    Returns out.
+    """
+    import torch
+
+    (B, H, Lq, Lk, d_k, d_v), dtype, key_lengths, out = _check(q, k, v, key_lengths, out)
+    dev = q.device
+    need = sdpa_decode_workspace_bytes(B, H, Lq, Lk, d_k, d_v, dtype)
+    if need < 0:
+        raise SdpaError(SDPA_ERR_BAD_SHAPE, "sizes rejected", "sdpa_decode")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = sdpa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                         0 if key_lengths is None else key_lengths.data_ptr(), out.data_ptr(),
+                         B, H, Lq, Lk, d_k, d_v, dtype, ws_ptr, ws_bytes, stream)
+    _raise(st, "sdpa_decode")
     return out

@@ -38,6 +38,105 @@ bool mul_ok(int64_t &n, std::initializer_list<int64_t> f)
     return true;
 }
 
+sdpa_status hip_status(hipError_t err)
+{
+    if (err == hipSuccess) return SDPA_OK;
+    g_last_hip_error = (int)err;
+    return SDPA_ERR_HIP;
+}
+
+// Size checks shared by every entry point (no pointers involved).
+sdpa_status check_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_k, int64_t d_v,
+                        sdpa_dtype dtype)
+{
+    if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1) return SDPA_ERR_BAD_SHAPE;
+    if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+    if (d_k > kMaxHeadDim || d_v > kMaxHeadDim) return SDPA_ERR_UNSUPPORTED;
+    if (B > kMaxDim || H > kMaxDim || Lq > kMaxDim || Lk > kMaxDim) return SDPA_ERR_BAD_SHAPE;
+    if (B == 0 || H == 0 || Lq == 0) return SDPA_OK;   // empty output: nothing to write
+    const int64_t elem = dtype == SDPA_BF16 ? 2 : 4;
+    int64_t n;
+    if (!mul_ok(n, {B, H, Lq, d_k, elem}) || !mul_ok(n, {B, H, Lk, d_k, elem}) ||
+        !mul_ok(n, {B, H, Lk, d_v, elem}) || !mul_ok(n, {B, H, Lq, d_v, elem}))
+        return SDPA_ERR_BAD_SHAPE;
+    if (B * H > kMaxDim) return SDPA_ERR_BAD_SHAPE;
+    // Both kernels use at most ceil(Lq / 64) workgroups per head.
+    if (((Lq + 63) / 64) > kMaxWorkgroups / (B * H)) return SDPA_ERR_BAD_SHAPE;
+    return SDPA_OK;
+}
+
+struct Sizes {
+    int64_t nq = 0, nk = 0, nv = 0, no = 0;   // bytes of Q, K, V, out
+    bool empty = false;
+};
+
+// Everything sdpa_forward checks before any HIP call.
+sdpa_status validate(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                     const void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_k,
+                     int64_t d_v, sdpa_dtype dtype, Sizes &z)
+{
+    const sdpa_status st = check_sizes(B, H, Lq, Lk, d_k, d_v, dtype);
+    if (st != SDPA_OK) return st;
+    if (B == 0 || H == 0 || Lq == 0) {
+        z.empty = true;
+        return SDPA_OK;
+    }
+    const int64_t elem = dtype == SDPA_BF16 ? 2 : 4;
+    mul_ok(z.nq, {B, H, Lq, d_k, elem});
+    mul_ok(z.nk, {B, H, Lk, d_k, elem});
+    mul_ok(z.nv, {B, H, Lk, d_v, elem});
+    mul_ok(z.no, {B, H, Lq, d_v, elem});
+    if (!Q || !out || (Lk > 0 && (!K || !V))) return SDPA_ERR_NULL_POINTER;
+    if (overlaps(out, z.no, Q, z.nq) || overlaps(out, z.no, K, z.nk) || overlaps(out, z.no, V, z.nv) ||
+        overlaps(out, z.no, key_lengths, 4 * B))
+        return SDPA_ERR_ALIAS;
+    return SDPA_OK;
+}
+
+sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                            int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                            int64_t d_k, int64_t d_v, sdpa_dtype dtype, hipStream_t s)
+{
+    // Lk == 0 needs no special case: both kernels then stage no key tile and
+    // write 0 for every row (no legal connection).
+    if (dtype == SDPA_BF16 && d_k == 64 && d_v == 64)
+        return hip_status(sdpa::launch_mfma_d64(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq,
+                                                Lk, s));
+    return hip_status(sdpa::launch_generic(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
+                                           (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
+}
+
+// The key-split path of sdpa_decode: bf16, d = 64, one 32-row wave per chunk.
+bool split_applies(int64_t Lq, int64_t d_k, int64_t d_v, sdpa_dtype dtype)
+{
+    return dtype == SDPA_BF16 && d_k == 64 && d_v == 64 && Lq >= 1 && Lq <= 32;
+}
+
+// Chunks per head: enough workgroups to fill the chip (about 1536: three
+// one-wave workgroups per CU, two rounds) but at least two 64-key tiles per
+// chunk.  chunk is a multiple of 64; n_split * chunk >= Lk; n_split >= 1.
+struct SplitPlan {
+    int64_t chunk, n_split;
+};
+SplitPlan split_plan(int64_t n_bh, int64_t Lk)
+{
+    constexpr int64_t kTarget = 1536, kTile = 64, kMinChunk = 2 * kTile;
+    int64_t want = (kTarget + n_bh - 1) / n_bh;
+    const int64_t most = (Lk + kMinChunk - 1) / kMinChunk;
+    if (want > most) want = most;
+    if (want < 1) want = 1;
+    int64_t chunk = (Lk + want - 1) / want;
+    chunk = (chunk + kTile - 1) / kTile * kTile;
+    if (chunk < kTile) chunk = kTile;
+    return SplitPlan{chunk, (Lk + chunk - 1) / chunk > 0 ? (Lk + chunk - 1) / chunk : 1};
+}
+
+// fp32 acc [d_v = 64] plus m and l per (split, query row).
+int64_t split_workspace_bytes(int64_t n_bh, int64_t Lq, const SplitPlan &sp)
+{
+    return 4 * (64 + 2) * n_bh * sp.n_split * Lq;
+}
+
 }  // namespace
 
 extern "C" {
@@ -51,6 +150,7 @@ const char *sdpa_status_str(sdpa_status s)
     case SDPA_ERR_UNSUPPORTED: return "unsupported dtype or head dimension";
     case SDPA_ERR_ALIAS: return "out overlaps an input buffer";
     case SDPA_ERR_HIP: return "a HIP runtime call failed (see sdpa_last_hip_error)";
+    case SDPA_ERR_WORKSPACE: return "the workspace is missing, too small, or overlaps another buffer";
     }
     return "unknown sdpa_status";
 }
@@ -62,41 +162,47 @@ sdpa_status sdpa_forward(const void *Q, const void *K, const void *V,
                          int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                          int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream)
 {
-    if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1) return SDPA_ERR_BAD_SHAPE;
-    if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
-    if (d_k > kMaxHeadDim || d_v > kMaxHeadDim) return SDPA_ERR_UNSUPPORTED;
-    if (B > kMaxDim || H > kMaxDim || Lq > kMaxDim || Lk > kMaxDim) return SDPA_ERR_BAD_SHAPE;
-    if (B == 0 || H == 0 || Lq == 0) return SDPA_OK;   // empty output: nothing to write
+    Sizes z;
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    if (st != SDPA_OK || z.empty) return st;
+    return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dtype,
+                           (hipStream_t)stream);
+}
 
-    const int64_t elem = dtype == SDPA_BF16 ? 2 : 4;
-    int64_t nq, nk, nv, no;
-    if (!mul_ok(nq, {B, H, Lq, d_k, elem}) || !mul_ok(nk, {B, H, Lk, d_k, elem}) ||
-        !mul_ok(nv, {B, H, Lk, d_v, elem}) || !mul_ok(no, {B, H, Lq, d_v, elem}))
-        return SDPA_ERR_BAD_SHAPE;
-    if (B * H > kMaxDim) return SDPA_ERR_BAD_SHAPE;
-    // Both kernels use at most ceil(Lq / 64) workgroups per head.
-    if (((Lq + 63) / 64) > kMaxWorkgroups / (B * H)) return SDPA_ERR_BAD_SHAPE;
+int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                    int64_t d_k, int64_t d_v, sdpa_dtype dtype)
+{
+    const sdpa_status st = check_sizes(B, H, Lq, Lk, d_k, d_v, dtype);
+    if (st != SDPA_OK) return -1;
+    if (B == 0 || H == 0 || Lq == 0) return 0;
+    if (!split_applies(Lq, d_k, d_v, dtype)) return 0;
+    const SplitPlan sp = split_plan(B * H, Lk);
+    return split_workspace_bytes(B * H, Lq, sp);
+}
 
-    if (!Q || !out || (Lk > 0 && (!K || !V))) return SDPA_ERR_NULL_POINTER;
-    if (overlaps(out, no, Q, nq) || overlaps(out, no, K, nk) || overlaps(out, no, V, nv) ||
-        overlaps(out, no, key_lengths, 4 * B))
-        return SDPA_ERR_ALIAS;
-
+sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
+                        const int32_t *key_lengths, void *out,
+                        int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                        int64_t d_k, int64_t d_v, sdpa_dtype dtype,
+                        void *workspace, int64_t workspace_bytes, void *stream)
+{
+    Sizes z;
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    if (st != SDPA_OK || z.empty) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t err;
-    // Lk == 0 needs no special case: both kernels then stage no key tile and
-    // write 0 for every row (no legal connection).
-    if (dtype == SDPA_BF16 && d_k == 64 && d_v == 64) {
-        err = sdpa::launch_mfma_d64(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk, s);
-    } else {
-        err = sdpa::launch_generic(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
-                                   (int)d_k, (int)d_v, dtype == SDPA_BF16, s);
-    }
-    if (err != hipSuccess) {
-        g_last_hip_error = (int)err;
-        return SDPA_ERR_HIP;
-    }
-    return SDPA_OK;
+    if (!split_applies(Lq, d_k, d_v, dtype))
+        return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dtype, s);
+
+    const SplitPlan sp = split_plan(B * H, Lk);
+    const int64_t need = split_workspace_bytes(B * H, Lq, sp);
+    if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+    if (overlaps(workspace, need, Q, z.nq) || overlaps(workspace, need, K, z.nk) ||
+        overlaps(workspace, need, V, z.nv) || overlaps(workspace, need, out, z.no) ||
+        overlaps(workspace, need, key_lengths, 4 * B))
+        return SDPA_ERR_WORKSPACE;
+    if (B * H * sp.n_split > kMaxWorkgroups || B * H * Lq > kMaxWorkgroups) return SDPA_ERR_BAD_SHAPE;
+    return hip_status(sdpa::launch_split_mfma_d64(Q, K, V, key_lengths, out, B, H, Lq, Lk, sp.chunk,
+                                                  sp.n_split, workspace, s));
 }
 
 }  // extern "C"

@@ -70,6 +70,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -237,7 +238,7 @@ struct Attn {
     static constexpr int kBufStride = 2 * kTileElems;   // K tile, then V tile, per buffer
     // Q is staged in buffer 2 before tile 2 arrives: each wave's 32 Q rows sit
     // exactly where its own share of tile 2's copies will land.
-    static_assert(2 * BN / NW == 32, "a wave's share of one tile's K and V rows holds its Q rows");
+    static_assert(2 * BN / NW >= 32, "a wave's share of one tile's K and V rows holds its Q rows");
 
     uint16_t *kbuf[kBuffers], *vbuf[kBuffers];   // LDS tile buffers
     const uint16_t *Kh, *Vh;
@@ -567,13 +568,27 @@ struct Attn {
     }
 };
 
-// One query tile (BM rows of head bh): load Q, stream the key tiles, store O.
-template <int NW, int NB>
+// Key-split mode (several query rows against a long key range, split over
+// workgroups): the workgroup takes keys [kv_lo, kv_lo + chunk) of its head and,
+// instead of O, writes its partial result for each query row i of split u =
+// bh * n_split + s: acc[u][i][0..63] = sum_j w_ij v_j, m[u][i] = the reference
+// maximum m_i (log2 units of the scaled scores), l[u][i] = sum_j w_ij, with
+// w_ij = exp2(s_ij - m_i) rounded to bf16 (the weights used in the product).
+// Partial results for any reference combine exactly (log-sum-exp merge).
+struct SplitOut {
+    float *acc, *m, *l;
+    int64_t chunk;       // keys per split, a multiple of the key tile
+    uint32_t n_split;    // splits per head
+};
+
+// One query tile (BM rows of head bh) against keys [kv_lo, kv_hi): load Q,
+// stream the key tiles, store O (or, with SPLIT, the partial result).
+template <int NW, int NB, bool SPLIT>
 __device__ __forceinline__ void attend_query_tile(
     uint16_t *const *kbuf, uint16_t *const *vbuf, const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
-    uint32_t bh, uint32_t qt, int wave, int lane)
+    uint32_t bh, uint32_t qt, int wave, int lane, int64_t kv_lo, int64_t kv_hi, const SplitOut &so, uint32_t u)
 {
     using A = Attn<NW, NB>;
     constexpr int BM = A::BM;
@@ -596,13 +611,17 @@ __device__ __forceinline__ void attend_query_tile(
         const int64_t l = key_lengths[b];
         len = l < 0 ? 0 : (l > Lk ? Lk : l);
     }
+    // Legal keys of this workgroup's range, counted from kv_lo (the causal
+    // mask is only used with kv_lo = 0).
+    len = (len < kv_hi ? len : kv_hi) - kv_lo;
+    len = len < 0 ? 0 : len;
     st.len = len;
     int64_t kv_end = len;                        // keys the workgroup needs
     if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
     st.n_tiles = (int)((kv_end + BN - 1) / BN);
 
-    st.Kh = K + (int64_t)bh * Lk * kD;
-    st.Vh = V + (int64_t)bh * Lk * kD;
+    st.Kh = K + ((int64_t)bh * Lk + kv_lo) * kD;
+    st.Vh = V + ((int64_t)bh * Lk + kv_lo) * kD;
 
     // Rows of this wave present in Q / O; buffer descriptors bounded to them make
     // reads past Lq return 0 and writes past Lq vanish.
@@ -664,6 +683,34 @@ __device__ __forceinline__ void attend_query_tile(
     // ---- epilogue: O = acc / l, rounded to bf16
     acc_read_fence();
     const float l_tot = sum_across_halves(st.l_run);
+    if constexpr (SPLIT) {
+        // The partial result, rows below Lq only (bounded descriptors drop the rest).
+        const int64_t row0 = (int64_t)u * Lq + st.q0w;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(so.acc + row0 * kD), (short)0, (int)rows_here * kD * 4, kBufferRsrcWord3);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int rq4 = 0; rq4 < 4; ++rq4) {
+                // Built as a float vector first: hipcc 7.2 stored the first
+                // slice for every rq4 when given bit-cast elements directly.
+                const f32x4_t w = {st.acc[db][4 * rq4 + 0], st.acc[db][4 * rq4 + 1],
+                                   st.acc[db][4 * rq4 + 2], st.acc[db][4 * rq4 + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4_t, w), ra, (uint32_t)((l32 * kD + db * 32 + rq4 * 8 + g * 4) * 4), 0, 0);
+            }
+        if (g == 0) {
+            const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(so.m + row0), (short)0, (int)rows_here * 4, kBufferRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(so.l + row0), (short)0, (int)rows_here * 4, kBufferRsrcWord3);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, st.m_run), rm,
+                                                  (uint32_t)(l32 * 4), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_tot), rl,
+                                                  (uint32_t)(l32 * 4), 0, 0);
+        }
+        return;
+    }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(O + tile_base), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
@@ -753,8 +800,64 @@ __global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kern
         bh = item / n_qtiles;
         qt = item % n_qtiles;
     }
-    attend_query_tile<NW, NB>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk, scale_log2,
-                              bh, qt, wave, lane);
+    attend_query_tile<NW, NB, false>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk,
+                                     scale_log2, bh, qt, wave, lane, 0, Lk, SplitOut{}, 0);
+}
+
+
+// Key-split kernel: one wave per workgroup, 32 query rows (Lq <= 32) against
+// one chunk of keys; workgroup w takes split s = w % n_split of head
+// bh = w / n_split and writes its partial result (SplitOut).  No causal mask.
+__global__ __launch_bounds__(64) SDPA_OCCUPANCY void sdpa_split_mfma_d64_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths,
+    int H, int64_t Lq, int64_t Lk, float scale_log2, SplitOut so)
+{
+    constexpr int NW = 1, NB = SDPA_MFMA_KEY_BLOCKS;
+    using A = Attn<NW, NB>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
+    uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
+#pragma unroll
+    for (int i = 0; i < A::kBuffers; ++i) {
+        kbuf[i] = lds + i * A::kBufStride;
+        vbuf[i] = kbuf[i] + A::kTileElems;
+    }
+    const int lane = threadIdx.x & 63;
+    const uint32_t u = blockIdx.x;
+    const uint32_t bh = u / so.n_split;
+    const int64_t kv_lo = (int64_t)(u % so.n_split) * so.chunk;
+    int64_t kv_hi = kv_lo + so.chunk;
+    kv_hi = kv_hi < Lk ? kv_hi : Lk;
+    attend_query_tile<NW, NB, true>(kbuf, vbuf, Q, K, V, key_lengths, 0, nullptr, H, Lq, Lk,
+                                    scale_log2, bh, 0, 0, lane, kv_lo, kv_hi, so, u);
+}
+
+// Merge of the split partial results: block = 64 lanes = the 64 output dims of
+// row i of head bh (block bh * Lq + i).  With M = max_s m_s:
+//   O = sum_s exp2(m_s - M) acc_s / sum_s exp2(m_s - M) l_s   (0 if no split has a key).
+__global__ __launch_bounds__(64) void sdpa_split_merge_d64_kernel(
+    const float *__restrict__ acc, const float *__restrict__ m, const float *__restrict__ l,
+    uint16_t *__restrict__ O, int64_t Lq, uint32_t n_split)
+{
+    const int d = threadIdx.x;
+    const int64_t row = blockIdx.x;                 // bh * Lq + i
+    const int64_t bh = row / Lq, i = row % Lq;
+    const int64_t u0 = bh * n_split;
+    float M = -INFINITY;
+    for (uint32_t s = 0; s < n_split; ++s) M = fmaxf(M, m[(u0 + s) * Lq + i]);
+    float num = 0.f, den = 0.f;
+    if (M > -INFINITY) {
+        for (uint32_t s = 0; s < n_split; ++s) {
+            const int64_t r = (u0 + s) * Lq + i;
+            const float ms = m[r];
+            if (ms == -INFINITY) continue;          // a split without legal keys
+            const float w = __builtin_amdgcn_exp2f(ms - M);
+            num += w * acc[r * kD + d];
+            den += w * l[r];
+        }
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    O[row * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
 }
 
 }  // namespace
@@ -773,6 +876,26 @@ hipError_t launch_mfma_d64(const void *Q, const void *K, const void *V,
                        dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
                        (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
                        scale_log2, n_qtiles, n_bh);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
+                                 const int32_t *key_lengths, void *out, int64_t B, int64_t H,
+                                 int64_t Lq, int64_t Lk, int64_t chunk, int64_t n_split,
+                                 void *workspace, hipStream_t stream)
+{
+    const int64_t n_bh = B * H, n_rows = n_bh * n_split * Lq;
+    float *ws = (float *)workspace;
+    const SplitOut so{ws, ws + n_rows * kD, ws + n_rows * (kD + 1), chunk, (uint32_t)n_split};
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
+    hipLaunchKernelGGL(sdpa_split_mfma_d64_kernel, dim3((uint32_t)(n_bh * n_split)), dim3(64), 0, stream,
+                       (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths,
+                       (int)H, Lq, Lk, scale_log2, so);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(sdpa_split_merge_d64_kernel, dim3((uint32_t)(n_bh * Lq)), dim3(64), 0, stream,
+                       (const float *)so.acc, (const float *)so.m, (const float *)so.l, (uint16_t *)out,
+                       Lq, (uint32_t)n_split);
     return hipGetLastError();
 }
 

@@ -23,4 +23,13 @@ hipError_t launch_mfma_d64(const void *Q, const void *K, const void *V,
                            int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                            hipStream_t stream);
 
+// bf16, d_k = d_v = 64, Lq <= 32, no causal mask: keys split into n_split chunks
+// of `chunk` keys per head (chunk a multiple of 64, n_split * chunk >= Lk),
+// partial results in `workspace` (4 * 66 * B * H * n_split * Lq bytes), then
+// merged into out.  Two kernels on `stream`.
+hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
+                                 const int32_t *key_lengths, void *out, int64_t B, int64_t H,
+                                 int64_t Lq, int64_t Lk, int64_t chunk, int64_t n_split,
+                                 void *workspace, hipStream_t stream);
+
 }  // namespace sdpa

@@ -64,7 +64,8 @@ typedef enum sdpa_status {
     SDPA_ERR_BAD_SHAPE = 2,      /* a size is negative, or a product overflows the limits */
     SDPA_ERR_UNSUPPORTED = 3,    /* (dtype, d_k, d_v) combination not built */
     SDPA_ERR_ALIAS = 4,          /* out overlaps Q, K, V or key_lengths */
-    SDPA_ERR_HIP = 5             /* a HIP call failed; see sdpa_last_hip_error() */
+    SDPA_ERR_HIP = 5,            /* a HIP call failed; see sdpa_last_hip_error() */
+    SDPA_ERR_WORKSPACE = 6       /* sdpa_decode: workspace NULL, too small, or overlapping */
 } sdpa_status;
 
 typedef enum sdpa_dtype {
@@ -88,6 +89,50 @@ sdpa_status sdpa_forward(const void *Q, const void *K, const void *V,
                          const int32_t *key_lengths, int causal, void *out,
                          int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                          int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream);
+
+/*
+ * Decode-step attention: the same result as sdpa_forward with causal = 0, for
+ * the case of a few query rows per head against a long key/value cache (the
+ * new positions of an autoregressive decoder, page "Attention Is All You
+ * Need/paper/es" §3.1 and §3.2.3: each output position attends to all the
+ * positions generated so far, given by key_lengths[b], the cache length
+ * including the new positions).
+ *
+ * For bf16 with d_k = d_v = 64 and 1 <= Lq <= 32 the keys of every (b, h) are
+ * split into chunks that run in parallel on the matrix cores; each chunk writes
+ * its partial result (per query row: reference maximum m, weight sum l and the
+ * unnormalised weighted sum of V) to `workspace`, and a second kernel merges
+ * the chunks: O = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c with
+ * M = max_c m_c (base 2 in the kernel; a chunk without legal keys contributes
+ * nothing; no legal key at all gives 0).  Any other (dtype, d_k, d_v, Lq) runs
+ * the sdpa_forward kernels and needs no workspace.
+ *
+ * Arguments as for sdpa_forward (no causal flag), plus
+ *   workspace        device scratch of at least sdpa_decode_workspace_bytes()
+ *                    bytes (may be NULL when that is 0); owned by the caller,
+ *                    contents on entry irrelevant, overwritten; must not
+ *                    overlap Q, K, V, key_lengths or out;
+ *   workspace_bytes  its size.
+ * Two calls may share a workspace only if they run in stream order.
+ * Returns SDPA_OK after the enqueue (two kernels on `stream`), or an error code;
+ * SDPA_ERR_WORKSPACE if the workspace is needed and is NULL, too small or
+ * overlapping.  Arithmetic and rounding as for sdpa_forward (the merge is fp32);
+ * results are deterministic run to run.
+ */
+sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
+                        const int32_t *key_lengths, void *out,
+                        int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                        int64_t d_k, int64_t d_v, sdpa_dtype dtype,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace sdpa_decode needs for these sizes: 0 when it runs the
+ * sdpa_forward kernels, otherwise 4 * (d_v + 2) * B * H * Lq * n_chunks, where
+ * n_chunks depends on B * H and Lk only.  Returns -1 for sizes sdpa_decode
+ * would reject with SDPA_ERR_BAD_SHAPE or SDPA_ERR_UNSUPPORTED.
+ */
+int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                    int64_t d_k, int64_t d_v, sdpa_dtype dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *sdpa_status_str(sdpa_status status);

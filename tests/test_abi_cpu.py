@@ -98,3 +98,53 @@ def test_python_forward_rejects_bad_arguments_without_gpu():
         sdpa.forward(q[0], q, q)
     with pytest.raises(TypeError):
         sdpa.forward(q.half(), q.half(), q.half())
+
+
+# ---- sdpa_decode: the same host-side checks, plus the workspace
+
+def dcall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=2, H=2, Lq=1, Lk=128,
+          dk=64, dv=64, dtype=sdpa.SDPA_BF16, ws=0x1000000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = sdpa.sdpa_decode_workspace_bytes(B, H, Lq, Lk, dk, dv, dtype)
+    return sdpa.sdpa_decode(Q, K, V, kl, O, B, H, Lq, Lk, dk, dv, dtype, ws, ws_bytes, 0)
+
+
+def test_decode_workspace_bytes():
+    ws = sdpa.sdpa_decode_workspace_bytes
+    bf, f32 = sdpa.SDPA_BF16, sdpa.SDPA_F32
+    one = ws(4, 16, 1, 8192, 64, 64, bf)
+    assert one > 0 and one % (4 * 66 * 64) == 0        # 4 * (d_v + 2) * B * H * Lq * chunks
+    assert ws(4, 16, 5, 8192, 64, 64, bf) == 5 * one    # linear in Lq
+    assert ws(4, 16, 32, 8192, 64, 64, bf) == 32 * one
+    # the split path is bf16, d = 64, Lq <= 32 only; otherwise no workspace
+    assert ws(4, 16, 33, 8192, 64, 64, bf) == 0
+    assert ws(4, 16, 1, 8192, 64, 64, f32) == 0
+    assert ws(4, 16, 1, 8192, 32, 32, bf) == 0
+    assert ws(0, 16, 1, 8192, 64, 64, bf) == 0          # empty call
+    assert ws(4, 16, 1, 0, 64, 64, bf) == 4 * 66 * 64   # no keys: one (empty) chunk
+    # sizes the entry point rejects
+    assert ws(-1, 16, 1, 8192, 64, 64, bf) == -1
+    assert ws(4, 16, 1, 8192, 129, 64, bf) == -1
+    assert ws(4, 16, 1, 8192, 64, 64, 9) == -1
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(Q=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(O=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(B=-1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(dk=129), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(O=FAKE_Q), sdpa.SDPA_ERR_ALIAS),
+    (dict(ws=0), sdpa.SDPA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), sdpa.SDPA_ERR_WORKSPACE),
+    (dict(ws=FAKE_V + 64), sdpa.SDPA_ERR_WORKSPACE),     # overlaps V
+    (dict(ws=FAKE_O - 64), sdpa.SDPA_ERR_WORKSPACE),     # overlaps out
+])
+def test_decode_prelaunch_validation(kw, expected):
+    assert dcall(**kw) == expected
+
+
+def test_decode_empty_calls():
+    assert dcall(B=0) == sdpa.SDPA_OK
+    assert dcall(Lq=0, ws=0) == sdpa.SDPA_OK
+    assert dcall(Q=0, K=0, V=0, O=0, H=0, ws=0) == sdpa.SDPA_OK
+    assert sdpa.sdpa_status_str(sdpa.SDPA_ERR_WORKSPACE).startswith("the workspace")

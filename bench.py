@@ -150,6 +150,10 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(calibrates the HBM byte counters of rocprofv3)")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="time the K steps as one replay of a captured HIP graph (no host "
+                         "launch cost between steps); auto: on for the decode workloads, whose "
+                         "steps are two short launches")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through (0: enough for >= 1 GiB on HBM-bound "
                          "workloads, 1 otherwise)")
@@ -195,19 +199,29 @@ def main():
     # Validate the binding once, then time pre-marshalled C-ABI calls so that the
     # host cost per step stays far below the kernel time.
     (q0, k0, v0), o0 = sets[0]
-    sdpa.forward(q0, k0, v0, key_lengths=kl, causal=c.causal, out=o0)
     stream = torch.cuda.current_stream(dev)
     lib = sdpa.load_library()
     dcode = sdpa.SDPA_BF16 if c.dtype == "bf16" else sdpa.SDPA_F32
-    calls = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), None if kl is None else kl.data_ptr(),
-              int(c.causal), o.data_ptr(), c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dcode,
-              stream.cuda_stream) for (q, k, v), o in sets]
-    fwd = lib.sdpa_forward
+    klp = None if kl is None else kl.data_ptr()
+    if c.entry == "decode":
+        ws_bytes = sdpa.sdpa_decode_workspace_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dcode)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        sdpa.decode(q0, k0, v0, key_lengths=kl, out=o0, workspace=ws)
+        calls = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), klp, o.data_ptr(), c.B, c.H, c.Lq,
+                  c.Lk, c.d_k, c.d_v, dcode, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+                 for (q, k, v), o in sets]
+        fn, fn_name = lib.sdpa_decode, "sdpa_decode"
+    else:
+        sdpa.forward(q0, k0, v0, key_lengths=kl, causal=c.causal, out=o0)
+        calls = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), klp, int(c.causal), o.data_ptr(),
+                  c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dcode, stream.cuda_stream)
+                 for (q, k, v), o in sets]
+        fn, fn_name = lib.sdpa_forward, "sdpa_forward"
 
     def step(n):
-        st = fwd(*calls[n % rotate])
+        st = fn(*calls[n % rotate])
         if st != 0:
-            raise RuntimeError("sdpa_forward: %s" % sdpa.sdpa_status_str(st))
+            raise RuntimeError("%s: %s" % (fn_name, sdpa.sdpa_status_str(st)))
 
     for n in range(args.warmup):
         step(n)
@@ -223,19 +237,57 @@ def main():
             settle_steps += 1
         torch.cuda.synchronize()
 
+    use_graph = args.graph == "on" or (args.graph == "auto" and c.entry == "decode")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()        # barrier (one rank) + synchronize
-    t0 = time.perf_counter()
-    start.record(stream)
-    for n in range(args.steps):
-        step(n)
-    end.record(stream)
-    torch.cuda.synchronize()
+    if use_graph:
+        # The same K calls captured on a side stream (default priority) and
+        # replayed as one graph.  The library's kernels take the stream handle
+        # they are given; the calls are re-marshalled with the capture stream.
+        gs = torch.cuda.Stream(device=dev)
+        gs.wait_stream(stream)
+        gcalls = [cl[:-1] + (gs.cuda_stream,) for cl in calls]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            for n in range(args.steps):
+                st = fn(*gcalls[n % rotate])
+                if st != 0:
+                    raise RuntimeError("%s: %s" % (fn_name, sdpa.sdpa_status_str(st)))
+        # replays must reproduce the eager result bit for bit (deterministic kernels)
+        for n in range(rotate):
+            step(n)
+        torch.cuda.synchronize()
+        eager = [o.clone() for _, o in sets]
+        for o in (o for _, o in sets):
+            o.zero_()
+        for _ in range(2):
+            with torch.cuda.stream(gs):     # replay() launches on the current stream
+                graph.replay()
+            torch.cuda.synchronize()
+            for (_, o), e in zip(sets, eager):
+                if not torch.equal(o.view(torch.int16) if o.dtype == torch.bfloat16 else o,
+                                   e.view(torch.int16) if e.dtype == torch.bfloat16 else e):
+                    raise RuntimeError("graph replay differs from the eager result")
+        torch.cuda.synchronize()        # barrier (one rank) + synchronize
+        t0 = time.perf_counter()
+        with torch.cuda.stream(gs):
+            start.record(gs)
+            graph.replay()
+            end.record(gs)
+        torch.cuda.synchronize()
+    else:
+        torch.cuda.synchronize()        # barrier (one rank) + synchronize
+        t0 = time.perf_counter()
+        start.record(stream)
+        for n in range(args.steps):
+            step(n)
+        end.record(stream)
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
-    # One kernel launch per step, launched back to back on this stream: the
-    # average launch duration is the event window over the launch count.
+    # One kernel launch per step (decode: the split kernel and its merge),
+    # launched back to back on this stream: the average launch duration is the
+    # event window over the launch count.
     kern_ms = ms_per_step
 
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -249,8 +301,11 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_TFLOPS[c.dtype],
                 "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_TFLOPS[c.dtype],
                 "traffic": traffic}
-    roof["kernel"] = ("sdpa_fwd_mfma_d64_kernel" if (c.dtype == "bf16" and c.d_k == 64 and
-                                                      c.d_v == 64) else "sdpa_fwd_generic_kernel")
+    if c.entry == "decode":
+        roof["kernel"] = "sdpa_split_mfma_d64_kernel + sdpa_split_merge_d64_kernel"
+    else:
+        roof["kernel"] = ("sdpa_fwd_mfma_d64_kernel" if (c.dtype == "bf16" and c.d_k == 64 and
+                                                          c.d_v == 64) else "sdpa_fwd_generic_kernel")
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
     roof["kernel_ms"] = kern_ms
@@ -262,10 +317,12 @@ def main():
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settle_steps,
+        "timing": "hip graph of the timed steps" if use_graph else "back-to-back launches",
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": c.dtype, "data": "synthetic",
-        "config": {"workload": c.name, "description": c.description, "B": c.B, "h": c.H,
+        "config": {"workload": c.name, "description": c.description, "entry": fn_name,
+                   "B": c.B, "h": c.H,
                    "Lq": c.Lq, "Lk": c.Lk, "d_k": c.d_k, "d_v": c.d_v, "causal": c.causal,
                    "key_lengths": None if x.key_lengths is None else "U{%d..%d} seed %d" % (
                        c.key_len_range[0], c.key_len_range[1], c.seed),

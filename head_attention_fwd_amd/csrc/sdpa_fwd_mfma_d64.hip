@@ -90,6 +90,9 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #ifndef SDPA_STORE_LDS
 #define SDPA_STORE_LDS 1
 #endif
+#ifndef SDPA_SPLIT_KEY_BLOCKS
+#define SDPA_SPLIT_KEY_BLOCKS 1   // 32-key blocks per LDS tile of the key-split kernel
+#endif
 #ifndef SDPA_MFMA_WAVES_PER_SIMD
 #define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget for 3 waves per SIMD (0: no hint)
 #endif
@@ -808,12 +811,14 @@ __global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kern
 // Key-split kernel: one wave per workgroup, 32 query rows (Lq <= 32) against
 // one chunk of keys; workgroup w takes split s = w % n_split of head
 // bh = w / n_split and writes its partial result (SplitOut).  No causal mask.
-__global__ __launch_bounds__(64) SDPA_OCCUPANCY void sdpa_split_mfma_d64_kernel(
+__global__ __launch_bounds__(64) void sdpa_split_mfma_d64_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths,
     int H, int64_t Lq, int64_t Lk, float scale_log2, SplitOut so)
 {
-    constexpr int NW = 1, NB = SDPA_MFMA_KEY_BLOCKS;
+    // One wave, 32-key tiles: 24 KiB of LDS, so 6 workgroups (waves) per CU
+    // keep the cache streaming.
+    constexpr int NW = 1, NB = SDPA_SPLIT_KEY_BLOCKS;
     using A = Attn<NW, NB>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
@@ -832,9 +837,24 @@ __global__ __launch_bounds__(64) SDPA_OCCUPANCY void sdpa_split_mfma_d64_kernel(
                                     scale_log2, bh, 0, 0, lane, kv_lo, kv_hi, so, u);
 }
 
-// Merge of the split partial results: block = 64 lanes = the 64 output dims of
-// row i of head bh (block bh * Lq + i).  With M = max_s m_s:
-//   O = sum_s exp2(m_s - M) acc_s / sum_s exp2(m_s - M) l_s   (0 if no split has a key).
+// Merge of the split partial results: block = one wave, lane d = output dim d
+// of row i of head bh (block bh * Lq + i).  Lane s of each group of 64 splits
+// loads that split's m and l (all loads of a group at once); with
+// M = max_s m_s and w_s = exp2(m_s - M) (0 for a split without legal keys):
+//   O = sum_s w_s acc_s / sum_s w_s l_s   (0 if no split has a key).
+__device__ inline float wave_max(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ inline float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
 __global__ __launch_bounds__(64) void sdpa_split_merge_d64_kernel(
     const float *__restrict__ acc, const float *__restrict__ m, const float *__restrict__ l,
     uint16_t *__restrict__ O, int64_t Lq, uint32_t n_split)
@@ -844,17 +864,34 @@ __global__ __launch_bounds__(64) void sdpa_split_merge_d64_kernel(
     const int64_t bh = row / Lq, i = row % Lq;
     const int64_t u0 = bh * n_split;
     float M = -INFINITY;
-    for (uint32_t s = 0; s < n_split; ++s) M = fmaxf(M, m[(u0 + s) * Lq + i]);
+    for (uint32_t s0 = 0; s0 < n_split; s0 += 64)
+        if (s0 + d < n_split) M = fmaxf(M, m[(u0 + s0 + d) * Lq + i]);
+    M = wave_max(M);
     float num = 0.f, den = 0.f;
     if (M > -INFINITY) {
-        for (uint32_t s = 0; s < n_split; ++s) {
-            const int64_t r = (u0 + s) * Lq + i;
-            const float ms = m[r];
-            if (ms == -INFINITY) continue;          // a split without legal keys
-            const float w = __builtin_amdgcn_exp2f(ms - M);
-            num += w * acc[r * kD + d];
-            den += w * l[r];
+        for (uint32_t s0 = 0; s0 < n_split; s0 += 64) {
+            float w = 0.f;
+            if (s0 + d < n_split) {
+                const int64_t r = (u0 + s0 + d) * Lq + i;
+                const float ms = m[r];
+                if (ms > -INFINITY) {
+                    w = __builtin_amdgcn_exp2f(ms - M);
+                    den += w * l[r];
+                }
+            }
+            const uint32_t n = n_split - s0 < 64 ? n_split - s0 : 64;
+            const float *a = acc + ((u0 + s0) * Lq + i) * kD + d;
+            for (uint32_t t0 = 0; t0 < n; t0 += 8) {   // 8 independent loads in flight
+                float x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = t0 + j < n ? a[(int64_t)(t0 + j) * Lq * kD] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    num += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w),
+                                                                               (t0 + j) & 63)) * x[j];
+            }
         }
+        den = wave_sum(den);
     }
     const float o = den > 0.f ? num / den : 0.f;
     O[row * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)o);

@@ -44,6 +44,7 @@ class Config:
     key_len_range: Optional[tuple]   # inclusive (lo, hi) or None for "no padding"
     scale: float
     seed: int
+    entry: str = "forward"   # "forward": sdpa_forward; "decode": sdpa_decode (causal = False)
 
 
 CONFIGS = {
@@ -67,11 +68,24 @@ CONFIGS = {
         "long_causal_bf16", "long-sequence causal self-attention, inputs scaled by 0.5", "bf16",
         B=4, H=16, Lq=8192, Lk=8192, d_k=64, d_v=64, causal=True, key_len_range=None,
         scale=0.5, seed=4),
+    # Decode steps (sdpa_decode): the new position of an autoregressive decoder
+    # against the cache of the positions generated so far (§3.1, §3.2.3).
+    "decode_long_bf16": Config(
+        "decode_long_bf16", "decode step after the long sequence: one new position per head "
+        "against an 8192-key cache, inputs scaled by 0.5", "bf16",
+        B=4, H=16, Lq=1, Lk=8192, d_k=64, d_v=64, causal=False, key_len_range=None,
+        scale=0.5, seed=5, entry="decode"),
+    "decode_base_bf16": Config(
+        "decode_base_bf16", "base-model decode step: 64 sequences (e.g. 16 sentences x 4 beams), "
+        "one new position against caches of up to 256 positions", "bf16",
+        B=64, H=8, Lq=1, Lk=256, d_k=64, d_v=64, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=6, entry="decode"),
 }
 
-#: Configuration order used by tests and reports (smallest first).
+#: Configuration order used by tests and reports (smallest first): the five
+#: forward configurations, then the decode steps.
 ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
-         "big_cross_bf16", "long_causal_bf16"]
+         "big_cross_bf16", "long_causal_bf16", "decode_base_bf16", "decode_long_bf16"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:

@@ -41,7 +41,7 @@ METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak (h=8/16, d_k=64) on 1 MI
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense peaks (matrix bf16; fp32 vector)
 PEAK_HBM_GBS = 8000.0
 DEFAULT_CONFIG = "long_causal_bf16"
-KERNEL_SOURCES = ["head_attention_fwd_amd/csrc/sdpa_fwd_mfma_d64.hip",
+KERNEL_SOURCES = ["head_attention_fwd_amd/csrc/sdpa_fwd_mfma.hip",
                   "head_attention_fwd_amd/csrc/sdpa_api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -304,8 +304,8 @@ def main():
     if c.entry == "decode":
         roof["kernel"] = "sdpa_split_mfma_d64_kernel + sdpa_split_merge_d64_kernel"
     else:
-        roof["kernel"] = ("sdpa_fwd_mfma_d64_kernel" if (c.dtype == "bf16" and c.d_k == 64 and
-                                                          c.d_v == 64) else "sdpa_fwd_generic_kernel")
+        roof["kernel"] = ("sdpa_fwd_mfma_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
+                                                      c.d_k in (32, 64, 128)) else "sdpa_fwd_generic_kernel")
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
     roof["kernel_ms"] = kern_ms

@@ -99,9 +99,9 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
 {
     // Lk == 0 needs no special case: both kernels then stage no key tile and
     // write 0 for every row (no legal connection).
-    if (dtype == SDPA_BF16 && d_k == 64 && d_v == 64)
-        return hip_status(sdpa::launch_mfma_d64(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq,
-                                                Lk, s));
+    if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128))
+        return hip_status(sdpa::launch_mfma(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
+                                            (int)d_k, s));
     return hip_status(sdpa::launch_generic(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
                                            (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
 }

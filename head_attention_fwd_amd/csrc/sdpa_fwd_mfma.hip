@@ -1,9 +1,11 @@
-// Scaled dot-product attention forward for bf16 inputs with d_k = d_v = 64 on
-// the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// Scaled dot-product attention forward for bf16 inputs with d_k = d_v = D,
+// D in {32, 64, 128}, on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation).
 //
 // What it computes: Eq. (1) of page "Attention Is All You Need/paper/es"
 // (§3.2.1), softmax(Q K^T / sqrt(d_k)) V per head (§3.2.2: d_k = d_v = 64 in
-// the base and big models), with -inf for illegal connections before the
+// the base and big models; Table 3 row (A) varies the head count at fixed
+// d_model = 512, i.e. d_k = 128, 32 and 16), with -inf for illegal connections before the
 // softmax (§3.2.3): keys j >= len_b (padding) and, when causal, keys j > i.
 // Both products are dense contractions ("highly optimised matrix multiplication
 // code", §3.2.1), so they run on the matrix cores; the Lq x Lk score matrix
@@ -76,8 +78,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kD = 64;                // d_k = d_v
-constexpr int kRowBytes = kD * 2;     // one K or V row in HBM and LDS
 constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 
 // Build-time shape of the kernel (tuned on MI355X; see the launcher).
@@ -94,21 +94,28 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #define SDPA_SPLIT_KEY_BLOCKS 1   // 32-key blocks per LDS tile of the key-split kernel
 #endif
 #ifndef SDPA_MFMA_WAVES_PER_SIMD
-#define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget for 3 waves per SIMD (0: no hint)
+#define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget at D = 64: 3 waves per SIMD
 #endif
-#if SDPA_MFMA_WAVES_PER_SIMD > 0
-#define SDPA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(SDPA_MFMA_WAVES_PER_SIMD, SDPA_MFMA_WAVES_PER_SIMD)))
-#else
-#define SDPA_OCCUPANCY
-#endif
+// Waves per SIMD the register budget is set for, by head size: D = 128 needs
+// 64 accumulator and 32 Q-operand registers (2 waves), D = 32 fits 4.
+template <int D>
+struct Occupancy {
+    static constexpr int kWaves = D >= 128 ? 2 : (D >= 64 ? SDPA_MFMA_WAVES_PER_SIMD : 4);
+};
 
-// 16-byte chunk swizzle: rows r and r' that a wave reads in the same LDS cycle
-// get different chunk positions (injective on any 8 consecutive rows and on the
-// 8 even or 8 odd rows of any 16 consecutive rows).
-__device__ inline int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte chunk swizzles of a row of D bf16 values (D/8 chunks), XORed into
+// the chunk index (for D = 128 only its low three bits, within each half row).
+// K (and Q) rows: rows r and r' that a wave reads in the same LDS cycle get
+// different chunk positions (D >= 64: injective on any 8 consecutive rows and
+// on the 8 even or 8 odd rows of any 16 consecutive rows; D = 32, four rows per
+// 256 bytes: rows r and r + 4 differ).
+template <int D>
+__device__ inline int swz(int row) { return D >= 64 ? (row ^ (row >> 3)) & 7 : (row >> 2) & 3; }
 
-// V rows: the 4 rows one ds_read_b64_tr_b16 group touches get disjoint chunk pairs.
-__device__ inline int swz_v(int row) { return (row & 3) << 1; }
+// V rows: the 4 rows one ds_read_b64_tr_b16 group touches get disjoint chunk
+// pairs (D = 32: the two 16-dim halves of a row stay apart).
+template <int D>
+__device__ inline int swz_v(int row) { return D >= 64 ? (row & 3) << 1 : (row & 1) << 1; }
 
 // Key row order fed to the score MFMA: swap bits 2 and 3 (an involution).
 __device__ inline int pi32(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -175,15 +182,19 @@ __device__ inline void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint16_t *
 
 // K/V tile loads go straight from HBM into LDS (buffer_load_dwordx4 ... lds): no
 // staging registers, no LDS store instructions.  One such instruction moves
-// 64 lanes x 16 B = 1 KiB = 8 rows of a tile into LDS at consecutive addresses
-// (lane L -> byte 16*L of the slice), so the LDS layout is chosen by which
-// global 16-byte chunk each lane fetches: lane L fills LDS row 8*slice + L/8,
-// physical chunk L % 8.  The buffer descriptor of each tile starts at the
-// tile's first row and covers only the rows below the key length; the
-// hardware returns 0 for reads past that bound, which zero-fills padded rows.
-template <int NW, int BN>
+// 64 lanes x 16 B = 1 KiB = 512/D rows of a tile into LDS at consecutive
+// addresses (lane L -> byte 16*L of the slice), so the LDS layout is chosen by
+// which global 16-byte chunk each lane fetches: with C = D/8 chunks per row,
+// lane L fills LDS row (512/D)*slice + L/C, physical chunk L % C.  The buffer
+// descriptor of each tile starts at the tile's first row and covers only the
+// rows below the key length; the hardware returns 0 for reads past that bound,
+// which zero-fills padded rows.
+template <int NW, int BN, int D>
 struct TileLoader {
-    static constexpr int kSlices = BN / 8;                  // 1 KiB slices per K (or V) tile
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
+    static constexpr int kRowsPerSlice = 512 / D;           // rows per 1 KiB copy
+    static constexpr int kSlices = BN * D / 512;            // 1 KiB slices per K (or V) tile
     static constexpr int kPerWave = kSlices / NW;
     static_assert(kSlices % NW == 0, "every wave issues the same number of copies");
     static constexpr int kLoadsPerTile = 2 * kPerWave;      // per wave: K and V slices
@@ -195,11 +206,11 @@ struct TileLoader {
         slice0 = wave * kPerWave;
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
-            const int pos = 8 * (slice0 + j) + (lane >> 3);   // LDS row filled by this lane
-            const int pc = lane & 7;                          // physical chunk
+            const int pos = kRowsPerSlice * (slice0 + j) + lane / kChunks;   // LDS row filled by this lane
+            const int pc = lane % kChunks;                    // physical chunk
             const int kr = (pos & ~31) | pi32(pos & 31);      // K row stored at LDS row pos
-            koff[j] = (uint32_t)(kr * kRowBytes + ((pc ^ swz(pos)) << 4));
-            voff[j] = (uint32_t)(pos * kRowBytes + ((pc ^ swz_v(pos)) << 4));
+            koff[j] = (uint32_t)(kr * kRowBytes + ((pc ^ swz<D>(pos)) << 4));
+            voff[j] = (uint32_t)(pos * kRowBytes + ((pc ^ swz_v<D>(pos)) << 4));
         }
     }
 
@@ -211,13 +222,13 @@ struct TileLoader {
         rows = rows < 0 ? 0 : (rows > BN ? BN : rows);
         const int nbytes = (int)rows * kRowBytes;
         const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(Kh + kv0 * kD), (short)0, nbytes, kBufferRsrcWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void *)(Kh + kv0 * D), (short)0, nbytes, kBufferRsrcWord3);
         const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(Vh + kv0 * kD), (short)0, nbytes, kBufferRsrcWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void *)(Vh + kv0 * D), (short)0, nbytes, kBufferRsrcWord3);
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
-            copy_to_lds(rk, Ks + (slice0 + j) * 8 * kD, koff[j]);
-            copy_to_lds(rv, Vs + (slice0 + j) * 8 * kD, voff[j]);
+            copy_to_lds(rk, Ks + (slice0 + j) * 512, koff[j]);
+            copy_to_lds(rv, Vs + (slice0 + j) * 512, voff[j]);
         }
     }
 };
@@ -232,16 +243,23 @@ __device__ inline void wait_vmem_keep() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(
 constexpr int kWaitLds0 = 15 | (3 << 14) | (7 << 4);
 
 // Per-wave state of the forward pass and the work on one key tile.
-template <int NW, int NB>
+template <int NW, int NB, int D>
 struct Attn {
+    static constexpr int kD = D;                 // d_k = d_v
+    static constexpr int kRowBytes = 2 * D;      // one K or V row in HBM and LDS
+    static constexpr int kKB = D / 16;           // 16-dim chunks of the score contraction
+    static constexpr int kDB = D / 32;           // 32-dim blocks of the output
     static constexpr int BM = 32 * NW;
     static constexpr int BN = 32 * NB;
     static constexpr int kTileElems = BN * kD;   // bf16 elements per K (or V) tile
     static constexpr int kBuffers = 3;                  // LDS ring: tiles t, t+1 read, t+2 landing
     static constexpr int kBufStride = 2 * kTileElems;   // K tile, then V tile, per buffer
-    // Q is staged in buffer 2 before tile 2 arrives: each wave's 32 Q rows sit
-    // exactly where its own share of tile 2's copies will land.
-    static_assert(2 * BN / NW >= 32, "a wave's share of one tile's K and V rows holds its Q rows");
+    // Q is staged in buffer 2 before tile 2 arrives when each wave's 32 Q rows
+    // fit exactly where its own share of tile 2's copies will land; otherwise
+    // (D = 128 with 32-key tiles) the Q operand is loaded straight into
+    // registers.
+    static constexpr bool kQViaLds = 2 * BN / NW >= 32;
+    static_assert(D == 32 || D == 64 || D == 128, "head sizes with a matrix-core layout");
 
     uint16_t *kbuf[kBuffers], *vbuf[kBuffers];   // LDS tile buffers
     const uint16_t *Kh, *Vh;
@@ -253,12 +271,12 @@ struct Attn {
     float scale_log2;
     int g;                           // lane half
 
-    TileLoader<NW, BN> ld;
-    bf16x8_t qf[4];                  // Q^T operand (B of S^T = K Q^T)
+    TileLoader<NW, BN, D> ld;
+    bf16x8_t qf[kKB];                // Q^T operand (B of S^T = K Q^T)
     int wave;                        // wave index in the workgroup (uniform)
-    int koff[2][4];                  // LDS byte offsets of K reads (blocks of even/odd parity)
-    int voff[2];                     // LDS byte offsets of V transposing reads
-    f32x16_t acc[2];                 // O^T: dims 32*db + 8*(r/4) + 4*g + r%4, this lane's query row
+    int koff[2][kKB];                // LDS byte offsets of K reads (blocks of even/odd parity)
+    int voff[kDB];                   // LDS byte offsets of V transposing reads
+    f32x16_t acc[kDB];               // O^T: dims 32*db + 8*(r/4) + 4*g + r%4, this lane's query row
     float m_run, l_run;
 
     // S^T block bk of the tile in buffer Ks.
@@ -268,7 +286,7 @@ struct Attn {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < kKB; ++kb) {
             const u32x4_t a = *(const u32x4_t *)((const char *)Ks + koff[bk & 1][kb] + (bk >> 1) * 64 * kRowBytes);
             s = mfma32(as_bf16x8(a), qf[kb], s);
         }
@@ -282,7 +300,7 @@ struct Attn {
         for (int h = 0; h < 2; ++h) {
             const int kk = 2 * bk + h;
 #pragma unroll
-            for (int db = 0; db < 2; ++db) {
+            for (int db = 0; db < kDB; ++db) {
                 const char *vb = (const char *)Vs + voff[db];
                 const u32x2_t lo = ds_read_tr16_b64((const uint16_t *)(vb + (16 * kk) * kRowBytes));
                 const u32x2_t hi = ds_read_tr16_b64((const uint16_t *)(vb + (16 * kk + 4) * kRowBytes));
@@ -312,7 +330,7 @@ struct Attn {
         // copies where the two paths join.
         acc_read_fence();
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 asm volatile("v_mul_f32 %0, %0, %1" : "+v"(acc[db][i]) : "v"(alpha));
@@ -487,13 +505,16 @@ struct Attn {
 
     // Q^T as the B operand of the score MFMA, from where the prologue staged it
     // in buffer 2: the lane's query row l32, dims 16*kb + 8*g .. +7 (logical
-    // chunk 2*kb + g, stored at chunk (2*kb + g) ^ swz(l32)).
+    // chunk 2*kb + g, stored at chunk (2*kb + g) ^ swz(l32)).  Without LDS
+    // staging the prologue has loaded qf straight from HBM.
     __device__ __forceinline__ void read_q()
     {
-        const uint16_t *row = (l32 < 16 ? kbuf[2] : vbuf[2]) + (16 * wave + (l32 & 15)) * kD;
+        if constexpr (kQViaLds) {
+            const uint16_t *row = (l32 < 16 ? kbuf[2] : vbuf[2]) + (16 * wave + (l32 & 15)) * kD;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-            qf[kb] = *(const bf16x8_t *)(row + (((2 * kb + g) ^ swz(l32)) << 3));
+            for (int kb = 0; kb < kKB; ++kb)
+                qf[kb] = *(const bf16x8_t *)(row + (((2 * kb + g) ^ swz<D>(l32)) << 3));
+        }
     }
 
     // Start of tile t, the same for every wave and every kind of tile (one
@@ -586,16 +607,17 @@ struct SplitOut {
 
 // One query tile (BM rows of head bh) against keys [kv_lo, kv_hi): load Q,
 // stream the key tiles, store O (or, with SPLIT, the partial result).
-template <int NW, int NB, bool SPLIT>
+template <int NW, int NB, int D, bool SPLIT>
 __device__ __forceinline__ void attend_query_tile(
     uint16_t *const *kbuf, uint16_t *const *vbuf, const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
     uint32_t bh, uint32_t qt, int wave, int lane, int64_t kv_lo, int64_t kv_hi, const SplitOut &so, uint32_t u)
 {
-    using A = Attn<NW, NB>;
+    using A = Attn<NW, NB, D>;
     constexpr int BM = A::BM;
     constexpr int BN = A::BN;
+    constexpr int kD = D, kRowBytes = A::kRowBytes, kKB = A::kKB, kDB = A::kDB;
     const int g = lane >> 5;      // lane half
     const int l32 = lane & 31;
     const int64_t b = bh / H;
@@ -643,9 +665,9 @@ __device__ __forceinline__ void attend_query_tile(
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < kKB; ++kb) {
             const int pos = bk * 32 + l32;
-            st.koff[bk][kb] = 2 * (pos * kD + (((2 * kb + g) ^ swz(pos)) << 3));
+            st.koff[bk][kb] = 2 * (pos * kD + (((2 * kb + g) ^ swz<D>(pos)) << 3));
         }
     //  V (A of O^T, transposing read): in 16-lane group G, lane i addresses row
     //  i/4 of a 4-row slab and dims 4*(i%4) .. +3 of the 16-dim slab
@@ -655,31 +677,57 @@ __device__ __forceinline__ void attend_query_tile(
         const int G1 = (lane >> 4) & 1;
         const int row = 8 * g + (i >> 2);
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
+        for (int db = 0; db < kDB; ++db) {
             const int col = 32 * db + 16 * G1 + 4 * (i & 3);
-            st.voff[db] = 2 * (row * kD + ((((col >> 3) ^ swz_v(row))) << 3) + (col & 7));
+            st.voff[db] = 2 * (row * kD + ((((col >> 3) ^ swz_v<D>(row))) << 3) + (col & 7));
         }
     }
 
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { st.acc[0][i] = 0.f; st.acc[1][i] = 0.f; }
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.f;
     st.m_run = -INFINITY;         // reference max of scaled scores (log2 units)
     st.l_run = 0.f;               // this lane's part of the running sum
 
     st.ld.init(wave, lane);
     if (st.n_tiles > 0) {
-        // This wave's 32 Q rows into buffer 2 (rows 0-15 where its share of
-        // tile 2's K rows lands, rows 16-31 where its V rows land), 8 rows per
-        // copy, chunks swizzled by the row; then tiles 0 and 1.
+        if constexpr (A::kQViaLds) {
+            // This wave's 32 Q rows into buffer 2 (rows 0-15 where its share of
+            // tile 2's K rows lands, rows 16-31 where its V rows land), 512/D
+            // rows per copy, chunks swizzled by the row.
+            constexpr int kRps = 512 / D, kC = D / 8;
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            const int qrow = 8 * sl + (lane >> 3);
-            const uint16_t *dst = (sl < 2 ? st.kbuf[2] : st.vbuf[2]) + (16 * wave + 8 * (sl & 1)) * kD;
-            copy_to_lds(rq, dst, (uint32_t)(qrow * kRowBytes + (((lane & 7) ^ swz(qrow)) << 4)));
+            for (int sl = 0; sl < 32 / kRps; ++sl) {
+                const int qrow = kRps * sl + lane / kC;
+                const int r0 = kRps * sl;                    // first Q row of this copy
+                const uint16_t *dst = (r0 < 16 ? st.kbuf[2] : st.vbuf[2]) + (16 * wave + (r0 & 15)) * kD;
+                copy_to_lds(rq, dst, (uint32_t)(qrow * kRowBytes + (((lane % kC) ^ swz<D>(qrow)) << 4)));
+            }
+        } else {
+            // Q^T operand straight into registers: lane (l32, g) holds row l32,
+            // dims 16*kb + 8*g .. +7.  Compiler-visible loads, so the compiler
+            // puts a wait for them before the first read of qf (the register
+            // file has no interlock on a load's destination); the tile copies
+            // it does not see are issued after them and complete later, so
+            // that wait never ends early.
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb)
+                st.qf[kb] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
+                    rq, (uint32_t)(l32 * kRowBytes + (kb * 16 + g * 8) * 2), 0, 0));
         }
+        // then the first tiles
         st.prefetch(0, st.kbuf[0], st.vbuf[0]);
     }
     if (st.n_tiles > 1) st.prefetch(1, st.kbuf[1], st.vbuf[1]);
+    if constexpr (!A::kQViaLds) {
+        // Read qf once here so that the compiler's wait for the Q loads sits
+        // before the tile loop: it waits for the first tiles too, which the
+        // first barrier waits for anyway, instead of draining the copies in
+        // flight on every tile.
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) asm volatile("" ::"v"(st.qf[kb]));
+    }
 
     st.run();
 
@@ -692,7 +740,7 @@ __device__ __forceinline__ void attend_query_tile(
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(so.acc + row0 * kD), (short)0, (int)rows_here * kD * 4, kBufferRsrcWord3);
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < kDB; ++db)
 #pragma unroll
             for (int rq4 = 0; rq4 < 4; ++rq4) {
                 // Built as a float vector first: hipcc 7.2 stored the first
@@ -718,33 +766,38 @@ __device__ __forceinline__ void attend_query_tile(
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(O + tile_base), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
 #if SDPA_STORE_LDS
-    // The wave's 32 x 64 output tile goes through LDS so that every store
-    // instruction writes 8 whole rows (1 KiB contiguous): written in the
+    // The wave's 32 x D output tile goes through LDS so that every store
+    // instruction writes 512/D whole rows (1 KiB contiguous): written in the
     // accumulator layout (lane: row l32, 8-byte pieces of 16-byte chunk
-    // 4*db + rq4), read back as row 8*i + lane/8, chunk lane%8.  Chunks are
-    // XOR-swizzled by the row.  The barrier makes sure every wave is done with
-    // the tile buffers this reuses (no copies are in flight after the last tile).
+    // 4*db + rq4), read back as row (512/D)*i + lane/(D/8), chunk lane%(D/8).
+    // Chunks are XOR-swizzled by the row (D = 32: rows r and r + 4 share banks,
+    // so by r/4).  The barrier makes sure every wave is done with the tile
+    // buffers this reuses (no copies are in flight after the last tile); the
+    // waves' stages (32 * D elements each) fit in the three buffers.
+    static_assert(NW * 32 * kD <= A::kBuffers * A::kBufStride, "output stage fits in LDS");
     __syncthreads();
     uint16_t *stage = kbuf[0] + wave * 32 * kD;
+    constexpr int kC = kD / 8, kRps = 512 / kD;
+    auto oswz = [](int r) { return kD >= 64 ? r & 7 : (r >> 2) & 3; };
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int rq4 = 0; rq4 < 4; ++rq4) {
             u32x2_t w;
             w[0] = pack_bf16x2(st.acc[db][4 * rq4 + 0] * inv, st.acc[db][4 * rq4 + 1] * inv);
             w[1] = pack_bf16x2(st.acc[db][4 * rq4 + 2] * inv, st.acc[db][4 * rq4 + 3] * inv);
             const int c = 4 * db + rq4;
-            *(u32x2_t *)((char *)stage + l32 * kRowBytes + ((c ^ (l32 & 7)) << 4) + 8 * g) = w;
+            *(u32x2_t *)((char *)stage + l32 * kRowBytes + ((c ^ oswz(l32)) << 4) + 8 * g) = w;
         }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * i + (lane >> 3), c = lane & 7;
-        const u32x4_t w = *(const u32x4_t *)((const char *)stage + r * kRowBytes + ((c ^ (r & 7)) << 4));
+    for (int i = 0; i < 32 / kRps; ++i) {
+        const int r = kRps * i + lane / kC, c = lane % kC;
+        const u32x4_t w = *(const u32x4_t *)((const char *)stage + r * kRowBytes + ((c ^ oswz(r)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(r * kRowBytes + c * 16), 0, 0);
     }
 #else
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int rq4 = 0; rq4 < 4; ++rq4) {
             u32x2_t w;
@@ -766,14 +819,15 @@ __device__ __forceinline__ void attend_query_tile(
 //    first (qt descending), which fills the slots greedily longest-first and
 //    leaves only short tiles for the end of the grid; when 8 divides the head
 //    count each XCD still takes its own run of heads.
-template <int NW, int NB>
-__global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kernel(
+template <int NW, int NB, int D>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves))) void sdpa_fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
     uint32_t n_qtiles, uint32_t n_bh)
 {
-    using A = Attn<NW, NB>;
+    using A = Attn<NW, NB, D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
 #pragma unroll
@@ -803,7 +857,7 @@ __global__ __launch_bounds__(NW * 64) SDPA_OCCUPANCY void sdpa_fwd_mfma_d64_kern
         bh = item / n_qtiles;
         qt = item % n_qtiles;
     }
-    attend_query_tile<NW, NB, false>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk,
+    attend_query_tile<NW, NB, D, false>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk,
                                      scale_log2, bh, qt, wave, lane, 0, Lk, SplitOut{}, 0);
 }
 
@@ -818,8 +872,8 @@ __global__ __launch_bounds__(64) void sdpa_split_mfma_d64_kernel(
 {
     // One wave, 32-key tiles: 24 KiB of LDS, so 6 workgroups (waves) per CU
     // keep the cache streaming.
-    constexpr int NW = 1, NB = SDPA_SPLIT_KEY_BLOCKS;
-    using A = Attn<NW, NB>;
+    constexpr int NW = 1, NB = SDPA_SPLIT_KEY_BLOCKS, D = 64;
+    using A = Attn<NW, NB, D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
 #pragma unroll
@@ -833,7 +887,7 @@ __global__ __launch_bounds__(64) void sdpa_split_mfma_d64_kernel(
     const int64_t kv_lo = (int64_t)(u % so.n_split) * so.chunk;
     int64_t kv_hi = kv_lo + so.chunk;
     kv_hi = kv_hi < Lk ? kv_hi : Lk;
-    attend_query_tile<NW, NB, true>(kbuf, vbuf, Q, K, V, key_lengths, 0, nullptr, H, Lq, Lk,
+    attend_query_tile<NW, NB, D, true>(kbuf, vbuf, Q, K, V, key_lengths, 0, nullptr, H, Lq, Lk,
                                     scale_log2, bh, 0, 0, lane, kv_lo, kv_hi, so, u);
 }
 
@@ -859,6 +913,7 @@ __global__ __launch_bounds__(64) void sdpa_split_merge_d64_kernel(
     const float *__restrict__ acc, const float *__restrict__ m, const float *__restrict__ l,
     uint16_t *__restrict__ O, int64_t Lq, uint32_t n_split)
 {
+    constexpr int kD = 64;
     const int d = threadIdx.x;
     const int64_t row = blockIdx.x;                 // bh * Lq + i
     const int64_t bh = row / Lq, i = row % Lq;
@@ -897,23 +952,37 @@ __global__ __launch_bounds__(64) void sdpa_split_merge_d64_kernel(
     O[row * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
 }
 
-}  // namespace
-
-hipError_t launch_mfma_d64(const void *Q, const void *K, const void *V,
-                           const int32_t *key_lengths, int causal, void *out,
-                           int64_t B, int64_t H, int64_t Lq, int64_t Lk, hipStream_t stream)
+template <int D>
+hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                         int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                         hipStream_t stream)
 {
     constexpr int NW = SDPA_MFMA_WAVES;
-    constexpr int NB = SDPA_MFMA_KEY_BLOCKS;
+    // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB.
+    constexpr int NB = D >= 128 ? 1 : SDPA_MFMA_KEY_BLOCKS;
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
-    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
-    hipLaunchKernelGGL((sdpa_fwd_mfma_d64_kernel<NW, NB>), dim3(n_qtiles * n_bh),
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D>), dim3(n_qtiles * n_bh),
                        dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
                        (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
                        scale_log2, n_qtiles, n_bh);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mfma(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                       int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
+                       hipStream_t stream)
+{
+    switch (d) {
+    case 32: return launch_mfma_d<32>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
+    case 64: return launch_mfma_d<64>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
+    case 128: return launch_mfma_d<128>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
@@ -923,6 +992,7 @@ hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
 {
     const int64_t n_bh = B * H, n_rows = n_bh * n_split * Lq;
     float *ws = (float *)workspace;
+    constexpr int kD = 64;
     const SplitOut so{ws, ws + n_rows * kD, ws + n_rows * (kD + 1), chunk, (uint32_t)n_split};
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
     hipLaunchKernelGGL(sdpa_split_mfma_d64_kernel, dim3((uint32_t)(n_bh * n_split)), dim3(64), 0, stream,

@@ -28,13 +28,17 @@
  * (the same type for all four).  key_lengths: device pointer to int32[B], or
  * NULL.  Offsets are computed in 64 bits.
  *
- * Arithmetic.  SDPA_BF16: bf16 inputs, bf16 matrix-core products with fp32
- * accumulation, fp32 softmax, the weights rounded to bf16 (nearest even)
- * before the product with V, output rounded to bf16 (nearest even).
- * SDPA_F32: fp32 throughout.  Results are deterministic run to run.
+ * Arithmetic.  SDPA_BF16 on the matrix cores (head sizes below): bf16
+ * products with fp32 accumulation, fp32 softmax, the weights rounded to bf16
+ * (nearest even) before the product with V, output rounded to bf16 (nearest
+ * even).  Other SDPA_BF16 head sizes: fp32 arithmetic on the bf16 inputs,
+ * output rounded to bf16.  SDPA_F32: fp32 throughout.  Results are
+ * deterministic run to run.
  *
- * Supported sizes.  SDPA_BF16: 1 <= d_k, d_v <= 128 (d_k = d_v = 64 runs on the
- * matrix cores).  SDPA_F32: 1 <= d_k, d_v <= 128.  B*H <= 2^31 - 1,
+ * Supported sizes.  SDPA_BF16: 1 <= d_k, d_v <= 128 (d_k = d_v in {32, 64, 128}
+ * runs on the matrix cores: the head sizes of the base and big models, §3.2.2,
+ * and of Table 3 row (A) at d_model = 512).  SDPA_F32: 1 <= d_k, d_v <= 128.
+ * B*H <= 2^31 - 1,
  * Lq, Lk <= 2^31 - 1.  B, H, Lq or Lk equal to 0 is an empty call (SDPA_OK,
  * nothing launched).
  *

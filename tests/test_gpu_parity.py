@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name", ["tiny_causal_f32", "base_encoder_bf16",
-                                  "base_decoder_causal_bf16", "big_cross_bf16"])
+                                  "base_decoder_causal_bf16", "big_cross_bf16",
+                                  "rowA_h4_d128_encoder_bf16", "rowA_h16_d32_encoder_bf16"])
 def test_config_full(name):
     x = workloads.generate(name)
     c = x.config
@@ -41,10 +42,10 @@ def _sample_rows(B, H, Lq, n_random, seed):
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
-def test_long_causal_sampled_rows():
-    """The long causal configuration at full size, in the launch configuration the
+@pytest.mark.parametrize("name", ["long_causal_bf16", "long_causal_d128_bf16"])
+def test_long_causal_sampled_rows(name):
+    """The long causal configurations at full size, in the launch configuration the
     benchmark times; the oracle recomputes a sample of rows one by one."""
-    name = "long_causal_bf16"
     x = workloads.generate(name)
     c = x.config
     announce("config %s (full size)" % name)
@@ -68,9 +69,17 @@ RAGGED = [
     (1, 1, 1, 300, 64, 64, False, None),
     (1, 1, 200, 1, 64, 64, True, None),
     (3, 1, 257, 511, 64, 64, True, [511, 200, 7]),
-    (2, 2, 70, 90, 32, 32, True, [50, 90]),    # bf16 generic path
+    (2, 2, 70, 90, 16, 48, True, None),        # bf16 generic path
+    (1, 1, 5, 7, 16, 16, False, None),
+]
+# The same shapes on the matrix-core kernel's other head sizes (d = 128 uses
+# 32-key tiles and loads Q straight into registers; d = 32 packs 4 rows per 256 B).
+for _d in (32, 128):
+    RAGGED += [(B, H, Lq, Lk, _d, _d, c, ln) for (B, H, Lq, Lk, dk, dv, c, ln) in RAGGED[:10]]
+RAGGED += [
+    (2, 2, 70, 90, 32, 32, True, [50, 90]),
     (2, 2, 70, 90, 128, 128, False, [90, 3]),
-    (2, 2, 70, 90, 16, 48, True, None),
+    (2, 3, 160, 97, 128, 128, True, [97, 33]),   # several 32-key tiles, ragged tail
 ]
 
 
@@ -107,11 +116,12 @@ def test_ragged_f32(case):
     assert_parity(got, ref, v, "f32", str(case))
 
 
-def test_long_keys_sampled_rows():
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_long_keys_sampled_rows(d):
     """A long key sequence (32768 keys) on the matrix-core kernel, non-causal with
     padding, rows sampled for the oracle."""
     B, H, Lq, Lk = 2, 2, 256, 32768
-    q, k, v, _ = workloads.draw(B, H, Lq, Lk, 64, 64, dtype="bf16", seed=21)
+    q, k, v, _ = workloads.draw(B, H, Lq, Lk, d, d, dtype="bf16", seed=21 + d)
     lengths = [32768, 20001]
     announce("long keys %d" % Lk)
     got = run(q, k, v, lengths, False, "bf16")

@@ -68,6 +68,23 @@ CONFIGS = {
         "long_causal_bf16", "long-sequence causal self-attention, inputs scaled by 0.5", "bf16",
         B=4, H=16, Lq=8192, Lk=8192, d_k=64, d_v=64, causal=True, key_len_range=None,
         scale=0.5, seed=4),
+    # Table 3, row (A): d_model = 512 split into other head counts, d_k = d_v =
+    # 512 / h, on the base encoder's batch shape.
+    "rowA_h4_d128_encoder_bf16": Config(
+        "rowA_h4_d128_encoder_bf16", "encoder self-attention with key padding, "
+        "h = 4 heads of d_k = d_v = 128 (Table 3 row A)", "bf16",
+        B=64, H=4, Lq=256, Lk=256, d_k=128, d_v=128, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=7),
+    "rowA_h16_d32_encoder_bf16": Config(
+        "rowA_h16_d32_encoder_bf16", "encoder self-attention with key padding, "
+        "h = 16 heads of d_k = d_v = 32 (Table 3 row A)", "bf16",
+        B=64, H=16, Lq=256, Lk=256, d_k=32, d_v=32, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=8),
+    "long_causal_d128_bf16": Config(
+        "long_causal_d128_bf16", "long-sequence causal self-attention, d_model = 1024 as "
+        "h = 8 heads of d_k = d_v = 128, inputs scaled by 0.5", "bf16",
+        B=4, H=8, Lq=8192, Lk=8192, d_k=128, d_v=128, causal=True, key_len_range=None,
+        scale=0.5, seed=9),
     # Decode steps (sdpa_decode): the new position of an autoregressive decoder
     # against the cache of the positions generated so far (§3.1, §3.2.3).
     "decode_long_bf16": Config(
@@ -83,9 +100,11 @@ CONFIGS = {
 }
 
 #: Configuration order used by tests and reports (smallest first): the five
-#: forward configurations, then the decode steps.
+#: forward configurations, the other head sizes, then the decode steps.
 ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
-         "big_cross_bf16", "long_causal_bf16", "decode_base_bf16", "decode_long_bf16"]
+         "big_cross_bf16", "long_causal_bf16", "rowA_h4_d128_encoder_bf16",
+         "rowA_h16_d32_encoder_bf16", "long_causal_d128_bf16", "decode_base_bf16",
+         "decode_long_bf16"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:

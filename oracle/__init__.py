@@ -13,7 +13,10 @@ Computes, for every batch entry b, head h and query row i
 (page "Attention Is All You Need/paper/es", §3.2.1, Eq. (1) and §3.2.3):
     O[b,h,i,:] = sum_j softmax_j( Q[b,h,i,:].K[b,h,j,:] / sqrt(d_k) + mask ) V[b,h,j,:]
 with mask = -inf where j >= len_b (key padding, len_b = clamp(key_lengths[b],
-0, Lk)) or, for causal attention, where j > i.  A row with no legal key is 0.
+0, Lk)), for causal attention where j > i, and for restricted self-attention
+with radius w (same page, §4 and Table 1: a neighbourhood of size r = 2w + 1
+centred on the output position) where |i - j| > w.  A row with no legal key
+is 0.
 """
 from __future__ import annotations
 
@@ -73,6 +76,14 @@ def _lengths(key_lengths, B):
     return kl
 
 
+def _radius(radius):
+    if radius is None:
+        return -1
+    if int(radius) < 0:
+        raise ValueError("radius must be None or >= 0")
+    return int(radius)
+
+
 class Oracle:
     """ctypes front end of one compiled oracle library."""
 
@@ -83,18 +94,19 @@ class Oracle:
         i64 = ctypes.c_int64
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_attention.argtypes = [dp, dp, dp, ip, ctypes.c_int, i64, i64, i64, i64,
-                                         i64, i64, dp, dp, dp, ctypes.c_int]
+                                         i64, i64, i64, dp, dp, dp, ctypes.c_int]
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = [dp, dp, dp, ip, ctypes.c_int, i64, i64, i64,
-                                              i64, i64, i64,
+                                              i64, i64, i64, i64,
                                               ctypes.POINTER(ctypes.c_int64), i64, dp, dp,
                                               ctypes.c_int]
         self.lib = lib
         self.path = path
 
     def attention(self, q, k, v, key_lengths=None, causal=False, return_weights=False,
-                  nthreads=0):
-        """Full attention in fp64.  Returns O, or (O, P, LSE) if return_weights."""
+                  nthreads=0, radius=None):
+        """Full attention in fp64.  Returns O, or (O, P, LSE) if return_weights.
+        radius: None (no restriction) or w >= 0 (keys with |i - j| <= w only)."""
         B, H, Lq, Lk, dk, dv = _shapes(q, k, v)
         q, k, v = _f64(q), _f64(k), _f64(v)
         kl = _lengths(key_lengths, B)
@@ -102,13 +114,14 @@ class Oracle:
         P = np.empty((B, H, Lq, Lk), dtype=np.float64) if return_weights else None
         LSE = np.empty((B, H, Lq), dtype=np.float64) if return_weights else None
         rc = self.lib.oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(kl, ctypes.c_int32),
-                                       int(bool(causal)), B, H, Lq, Lk, dk, dv,
+                                       int(bool(causal)), _radius(radius), B, H, Lq, Lk, dk, dv,
                                        _ptr(O), _ptr(P), _ptr(LSE), int(nthreads))
         if rc != 0:
             raise RuntimeError("oracle_attention failed with code %d" % rc)
         return (O, P, LSE) if return_weights else O
 
-    def attention_rows(self, q, k, v, rows, key_lengths=None, causal=False, nthreads=0):
+    def attention_rows(self, q, k, v, rows, key_lengths=None, causal=False, nthreads=0,
+                       radius=None):
         """Attention for selected rows only.
 
         ``rows`` is an int array of (b, head, i) triples, shape [n, 3].  Returns
@@ -135,7 +148,7 @@ class Oracle:
             l = np.empty((len(idx),), dtype=np.float64)
             rc = self.lib.oracle_attention_rows(_ptr(qh), _ptr(kh), _ptr(vh),
                                                 _ptr(klh, ctypes.c_int32), int(bool(causal)),
-                                                1, 1, Lq, Lk, dk, dv,
+                                                _radius(radius), 1, 1, Lq, Lk, dk, dv,
                                                 _ptr(sel, ctypes.c_int64), len(idx),
                                                 _ptr(o), _ptr(l), int(nthreads))
             if rc != 0:
@@ -158,11 +171,12 @@ def default() -> Oracle:
     return _default
 
 
-def attention(q, k, v, key_lengths=None, causal=False, return_weights=False, nthreads=0):
+def attention(q, k, v, key_lengths=None, causal=False, return_weights=False, nthreads=0,
+              radius=None):
     """Full fp64 attention; see Oracle.attention."""
-    return default().attention(q, k, v, key_lengths, causal, return_weights, nthreads)
+    return default().attention(q, k, v, key_lengths, causal, return_weights, nthreads, radius)
 
 
-def attention_rows(q, k, v, rows, key_lengths=None, causal=False, nthreads=0):
+def attention_rows(q, k, v, rows, key_lengths=None, causal=False, nthreads=0, radius=None):
     """fp64 attention for selected (b, head, i) rows; see Oracle.attention_rows."""
-    return default().attention_rows(q, k, v, rows, key_lengths, causal, nthreads)
+    return default().attention_rows(q, k, v, rows, key_lengths, causal, nthreads, radius)

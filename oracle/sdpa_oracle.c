@@ -22,6 +22,14 @@
  *        triangular mask keeps the current and earlier positions, rows being
  *        queries and columns keys.
  *
+ *   Restricted self-attention: each output position considers only a
+ *     neighbourhood of size r of the input sequence centred on it -- same
+ *     page, §4 and Table 1 (work O(r n d), path length O(n / r)).  Reading
+ *     taken: the neighbourhood is given by its radius w >= 0, key j being
+ *     legal for query i only when |i - j| <= w (r = 2w + 1 positions, fewer at
+ *     the ends of the sequence); a negative radius means no restriction.  It
+ *     combines with the two masks below.
+ *
  *   Key padding (readings stated where the pages are silent):
  *     key j is illegal for every query of sequence b when j >= len_b, with
  *     len_b = clamp(key_lengths[b], 0, Lk) (Lk when key_lengths is NULL);
@@ -50,10 +58,11 @@
 #endif
 
 /* Is key j a legal connection for query i of a sequence with len keys? */
-static int is_legal(int64_t i, int64_t j, int64_t len, int causal)
+static int is_legal(int64_t i, int64_t j, int64_t len, int causal, int64_t radius)
 {
     if (j >= len) return 0;             /* key padding */
     if (causal && j > i) return 0;      /* future position */
+    if (radius >= 0 && (j < i - radius || j > i + radius)) return 0;   /* outside the neighbourhood */
     return 1;
 }
 
@@ -77,12 +86,12 @@ static int64_t clamp_len(const int32_t *key_lengths, int64_t b, int64_t Lk)
  */
 static void attention_row(const double *q, const double *K, const double *V,
                           int64_t Lk, int64_t d_k, int64_t d_v, int64_t len,
-                          int causal, int64_t i, double *s, double *w,
+                          int causal, int64_t radius, int64_t i, double *s, double *w,
                           double *o, double *p_out, double *lse)
 {
     const double root_dk = sqrt((double)d_k);
     for (int64_t j = 0; j < Lk; ++j) {
-        if (!is_legal(i, j, len, causal)) {
+        if (!is_legal(i, j, len, causal, radius)) {
             s[j] = -INFINITY;
             continue;
         }
@@ -126,14 +135,15 @@ static int bad_shape(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_k, 
 }
 
 /*
- * Full attention over every (b, head, i).
+ * Full attention over every (b, head, i); radius < 0: no neighbourhood
+ * restriction.
  *   O   [B,H,Lq,d_v]  required
  *   P   [B,H,Lq,Lk]   optional (NULL): the softmax weights
  *   LSE [B,H,Lq]      optional (NULL)
  * Returns 0 on success, 1 on a bad shape, 2 on allocation failure.
  */
 int oracle_attention(const double *Q, const double *K, const double *V,
-                     const int32_t *key_lengths, int causal,
+                     const int32_t *key_lengths, int causal, int64_t radius,
                      int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                      int64_t d_k, int64_t d_v,
                      double *O, double *P, double *LSE, int nthreads)
@@ -162,7 +172,7 @@ int oracle_attention(const double *Q, const double *K, const double *V,
                 const double *Kh = K + bh * Lk * d_k;
                 const double *Vh = V + bh * Lk * d_v;
                 attention_row(Q + r * d_k, Kh, Vh, Lk, d_k, d_v,
-                              clamp_len(key_lengths, b, Lk), causal, i, s, w,
+                              clamp_len(key_lengths, b, Lk), causal, radius, i, s, w,
                               O + r * d_v, P ? P + r * Lk : NULL,
                               LSE ? LSE + r : NULL);
             }
@@ -179,7 +189,7 @@ int oracle_attention(const double *Q, const double *K, const double *V,
  * Same definition as oracle_attention, row by row.
  */
 int oracle_attention_rows(const double *Q, const double *K, const double *V,
-                          const int32_t *key_lengths, int causal,
+                          const int32_t *key_lengths, int causal, int64_t radius,
                           int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                           int64_t d_k, int64_t d_v,
                           const int64_t *rows, int64_t nrows,
@@ -209,7 +219,7 @@ int oracle_attention_rows(const double *Q, const double *K, const double *V,
                 const int64_t bh = r / Lq;
                 const int64_t b = bh / H;
                 attention_row(Q + r * d_k, K + bh * Lk * d_k, V + bh * Lk * d_v,
-                              Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, i,
+                              Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, radius, i,
                               s, w, O_rows + n * d_v, NULL,
                               LSE_rows ? LSE_rows + n : NULL);
             }

@@ -9,16 +9,23 @@ Used only to pin the oracle.  It differs from the oracle on purpose:
 Definition followed: page "Attention Is All You Need/paper/es", §3.2.1,
 Eq. (1) -- dot product of the query with each key, divided by sqrt(d_k),
 softmax over keys, weighted sum of the values; §3.2.3 -- a decoder position
-may use every position up to and including its own.
+may use every position up to and including its own; §4 and Table 1 -- restricted
+self-attention looks only at a neighbourhood centred on the output position
+(here: the positions within ``radius`` of it, when a radius is given).
 """
 import math
 
 
-def _legal_keys(i, Lk, length, causal):
-    return [j for j in range(Lk) if j < length and (not causal or j <= i)]
+def _legal_keys(i, Lk, length, causal, radius):
+    if radius is None:
+        lo, hi = 0, Lk - 1
+    else:
+        lo, hi = i - radius, i + radius
+    return [j for j in range(max(lo, 0), min(hi, Lk - 1) + 1)
+            if j < length and (not causal or j <= i)]
 
 
-def attention(q, k, v, key_lengths=None, causal=False):
+def attention(q, k, v, key_lengths=None, causal=False, radius=None):
     """q [B][H][Lq][d_k], k [B][H][Lk][d_k], v [B][H][Lk][d_v] (nested sequences
     or numpy arrays).  Returns nested lists O [B][H][Lq][d_v]."""
     B, H = len(q), len(q[0])
@@ -32,7 +39,7 @@ def attention(q, k, v, key_lengths=None, causal=False):
         for h in range(H):
             out_h = []
             for i in range(Lq):
-                legal = _legal_keys(i, Lk, length, causal)
+                legal = _legal_keys(i, Lk, length, causal, radius)
                 if not legal:
                     out_h.append([0.0] * dv)
                     continue

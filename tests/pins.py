@@ -261,9 +261,99 @@ def check_rows_api(orc):
             _close(one[0, 0], full[b, h], 0.0, "head (%d,%d) alone" % (b, h))
 
 
+# ---------------------------------------------------------------- restricted
+
+def check_restricted_radius0(orc):
+    """Radius 0 leaves only key j = i: the weight is exactly 1 and O[i] = V[i]
+    (0 where position i is padding or beyond the keys)."""
+    q, k, v = _rand(21, Lq=7, Lk=5)
+    lens = [5, 3]
+    for causal in (False, True):
+        O = orc.attention(q, k, v, key_lengths=lens, causal=causal, radius=0)
+        for b in range(2):
+            for i in range(7):
+                want = v[b, :, i] if i < lens[b] else np.zeros((3, 3))
+                _close(O[b, :, i], want, 0.0, "radius 0 b=%d i=%d causal=%d" % (b, i, causal))
+
+
+def check_restricted_toy(orc):
+    """Page "Self-Attention คืออะไร (แบบจับต้องได้)", Fig. 1/2 weights with the
+    neighbourhood of §4 of the paper page: the printed weights of the positions
+    within the radius, renormalised (softmax restricted to those keys); e.g. row
+    0 at radius 1 keeps 18 % and 12 % -> (0.18*10 + 0.12*20) / 0.30 = 14."""
+    g = read_golden("self_attention_toy.txt")
+    vals = g["values"]
+    n = len(vals)
+    for wk in ("row0_weights", "row1_weights"):
+        w = g[wk]
+        for radius in (1, 2):
+            O, P, _ = _toy_r(orc, w, radius)
+            for i in range(n):
+                keep = [j for j in range(n) if abs(i - j) <= radius]
+                z = sum(w[j] for j in keep)
+                want_p = [w[j] / z if j in keep else 0.0 for j in range(n)]
+                _close(P[0, 0, i], want_p, 1e-12, "restricted toy %s r=%d weights row %d" % (wk, radius, i))
+                _close(O[0, 0, i], [sum(w[j] * vals[j] for j in keep) / z], 1e-9,
+                       "restricted toy %s r=%d output row %d" % (wk, radius, i))
+    O, _, _ = _toy_r(orc, g["row0_weights"], 1)
+    _close(O[0, 0, 0], [14.0], 1e-9, "restricted toy row 0 radius 1 = 14")
+
+
+def _toy_r(orc, weights, radius):
+    g = read_golden("self_attention_toy.txt")
+    n = len(g["values"])
+    q = t4([[1.0]] * n)
+    k = t4([[math.log(w)] for w in weights])
+    v = t4([[x] for x in g["values"]])
+    return orc.attention(q, k, v, return_weights=True, radius=radius)
+
+
+def check_restricted_bruteforce(orc):
+    """Agreement with the brute force for several radii, masks and shapes."""
+    for seed, causal, lens, radius in ((31, False, [3, 9], 1), (32, True, [9, 5], 2),
+                                       (33, False, None, 3), (34, True, [0, 12], 1),
+                                       (35, False, [7, 9], 4), (36, True, None, 0)):
+        q, k, v = _rand(seed)
+        ref = np.array(bruteforce.attention(q, k, v, lens, causal, radius))
+        _close(orc.attention(q, k, v, key_lengths=lens, causal=causal, radius=radius), ref, 1e-12,
+               "restricted brute force seed=%d" % seed)
+    q, k, v = _rand(37, B=1, H=2, Lq=9, Lk=4, dk=2, dv=4)
+    for radius in (0, 2, 5):
+        _close(orc.attention(q, k, v, radius=radius),
+               np.array(bruteforce.attention(q, k, v, None, False, radius)), 1e-12,
+               "restricted brute force Lq > Lk r=%d" % radius)
+    o, _ = orc.attention_rows(q, k, v, [(0, 1, 6), (0, 0, 2)], radius=2)
+    _close(o, np.array(bruteforce.attention(q, k, v, None, False, 2))[0, [1, 0], [6, 2]], 1e-12,
+           "restricted rows api")
+
+
+def check_restricted_locality(orc):
+    """Keys and values outside row i's neighbourhood do not change row i; a change
+    inside it does."""
+    q, k, v = _rand(38, Lq=9, Lk=9)
+    radius = 2
+    base = orc.attention(q, k, v, radius=radius)
+    rng = np.random.default_rng(39)
+    for i in range(9):
+        k2, v2 = k.copy(), v.copy()
+        out = [j for j in range(9) if abs(i - j) > radius]
+        k2[:, :, out] = rng.standard_normal(k2[:, :, out].shape) * 5
+        v2[:, :, out] = rng.standard_normal(v2[:, :, out].shape) * 5
+        _close(orc.attention(q, k2, v2, radius=radius)[:, :, i], base[:, :, i], 0.0,
+               "restricted locality row %d" % i)
+        v3 = v.copy()
+        v3[:, :, min(i + radius, 8)] += 1.0
+        assert np.all(np.abs(orc.attention(q, k, v3, radius=radius)[:, :, i] - base[:, :, i]) > 1e-6), \
+            "row %d must see its neighbourhood's edge" % i
+    wide = orc.attention(q, k, v, radius=8)
+    _close(wide, orc.attention(q, k, v), 0.0, "radius >= L - 1 is unrestricted")
+
+
 ALL_CHECKS = [
     check_worked_example, check_worked_example_masked, check_toy_rows, check_toy_causal_row0,
     check_scale_dk64, check_uniform_prefix_means, check_special_cases,
     check_rows_sum_to_one_and_masked_zero, check_bruteforce_random, check_shift_invariance,
     check_permutation, check_locality, check_rows_api,
+    check_restricted_radius0, check_restricted_toy, check_restricted_bruteforce,
+    check_restricted_locality,
 ]

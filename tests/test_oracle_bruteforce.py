@@ -29,3 +29,21 @@ def test_exhaustive_tiny(Lq, Lk, dk, dv):
     got = oracle.attention(q, k, v, causal=True)
     ref = np.array(bruteforce.attention(q, k, v, None, True))
     assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (1, 4), (3, 2), (4, 4), (6, 5), (2, 6), (7, 7)])
+def test_exhaustive_tiny_restricted(Lq, Lk):
+    """Every radius from 0 to beyond both lengths, with and without the causal
+    mask and with every key length."""
+    rng = np.random.default_rng(7000 + 10 * Lq + Lk)
+    B, H, dk, dv = 2, 1, 3, 2
+    q = rng.standard_normal((B, H, Lq, dk))
+    k = rng.standard_normal((B, H, Lk, dk))
+    v = rng.standard_normal((B, H, Lk, dv))
+    lengths = list(range(0, Lk + 1))
+    for radius in range(0, max(Lq, Lk) + 1):
+        for causal, (l0, l1) in itertools.product((False, True), zip(lengths, reversed(lengths))):
+            kl = [l0, l1]
+            got = oracle.attention(q, k, v, key_lengths=kl, causal=causal, radius=radius)
+            ref = np.array(bruteforce.attention(q, k, v, kl, causal, radius))
+            assert np.max(np.abs(got - ref)) <= 1e-12, (radius, causal, kl)

@@ -36,8 +36,15 @@ MUTATIONS = {
     "empty_row_nan": ("for (int64_t t = 0; t < d_v; ++t) o[t] = 0.0;\n        if (p_out)",
                       "for (int64_t t = 0; t < d_v; ++t) o[t] = NAN;\n        if (p_out)"),
     "lse_without_max": ("if (lse) *lse = m + log(Z);", "if (lse) *lse = log(Z);"),
-    "rows_api_causal_dropped": ("Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, i,",
-                                "Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), 0, i,"),
+    "rows_api_causal_dropped": ("Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, radius, i,",
+                                "Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), 0, radius, i,"),
+    "rows_api_radius_dropped": ("Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, radius, i,",
+                                "Lk, d_k, d_v, clamp_len(key_lengths, b, Lk), causal, -1, i,"),
+    "band_lower_off_by_one": ("j < i - radius ||", "j <= i - radius ||"),
+    "band_upper_off_by_one": ("|| j > i + radius)", "|| j >= i + radius)"),
+    "band_upper_dropped": ("|| j > i + radius)", ")"),
+    "band_lower_dropped": ("(j < i - radius || j > i + radius)", "(j > i + radius)"),
+    "band_radius_doubled": ("j < i - radius || j > i + radius", "j < i - 2 * radius || j > i + 2 * radius"),
 }
 
 

@@ -88,8 +88,12 @@ def cpu_baseline(x, target_seconds=15.0):
         tot = 0
         for b, h, i in rows:
             lb = c.Lk if x.key_lengths is None else perfmodel.clamp_length(x.key_lengths[b], c.Lk)
-            n = min(lb, i + 1) if c.causal else lb
-            tot += (2 * c.d_k + 2 * c.d_v) * n
+            hi = min(lb, i + 1) if c.causal else lb          # one past the last legal key
+            lo = 0
+            if c.radius is not None:
+                hi = min(hi, i + c.radius + 1)
+                lo = max(0, i - c.radius)
+            tot += (2 * c.d_k + 2 * c.d_v) * max(hi - lo, 0)
         return tot
 
     oracle.default()   # build/load outside the timed region
@@ -102,7 +106,7 @@ def cpu_baseline(x, target_seconds=15.0):
         rows = sample(n)
         t0 = time.perf_counter()
         oracle.attention_rows(q64, k64, v64, rows, key_lengths=x.key_lengths, causal=c.causal,
-                              nthreads=threads)
+                              nthreads=threads, radius=c.radius)
         dt = time.perf_counter() - t0
         if budget == target_seconds:
             break
@@ -114,7 +118,8 @@ def cpu_baseline(x, target_seconds=15.0):
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d uniformly drawn query rows (%.3g of the workload's FLOPs, %.1f s), "
                       "fp64 C oracle with OpenMP" % (n, f / perfmodel.flops(
-                          c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths), dt)}
+                          c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
+                          radius=c.radius), dt)}
 
 
 def copy_calibration(torch, dev, args):
@@ -175,9 +180,10 @@ def main():
     x = workloads.generate(args.config)
     c = x.config
     tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
-    flops = perfmodel.flops(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths)
+    flops = perfmodel.flops(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
+                            radius=c.radius)
     nbytes = perfmodel.min_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
-                                 elem=2 if c.dtype == "bf16" else 4)
+                                 elem=2 if c.dtype == "bf16" else 4, radius=c.radius)
     hbm_bound = flops / nbytes < (PEAK_TFLOPS[c.dtype] * 1e12) / (PEAK_HBM_GBS * 1e9)
 
     rotate = args.rotate
@@ -211,6 +217,12 @@ def main():
                   c.Lk, c.d_k, c.d_v, dcode, ws.data_ptr(), ws_bytes, stream.cuda_stream)
                  for (q, k, v), o in sets]
         fn, fn_name = lib.sdpa_decode, "sdpa_decode"
+    elif c.entry == "restricted":
+        sdpa.restricted(q0, k0, v0, c.radius, key_lengths=kl, causal=c.causal, out=o0)
+        calls = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), klp, int(c.causal), c.radius,
+                  o.data_ptr(), c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dcode, stream.cuda_stream)
+                 for (q, k, v), o in sets]
+        fn, fn_name = lib.sdpa_forward_restricted, "sdpa_forward_restricted"
     else:
         sdpa.forward(q0, k0, v0, key_lengths=kl, causal=c.causal, out=o0)
         calls = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), klp, int(c.causal), o.data_ptr(),
@@ -303,6 +315,9 @@ def main():
                 "traffic": traffic}
     if c.entry == "decode":
         roof["kernel"] = "sdpa_split_mfma_d64_kernel + sdpa_split_merge_d64_kernel"
+    elif c.entry == "restricted":
+        roof["kernel"] = ("sdpa_fwd_mfma_band_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
+                                                           c.d_k in (32, 64, 128)) else "sdpa_fwd_generic_kernel")
     else:
         roof["kernel"] = ("sdpa_fwd_mfma_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
                                                       c.d_k in (32, 64, 128)) else "sdpa_fwd_generic_kernel")
@@ -326,7 +341,7 @@ def main():
                    "Lq": c.Lq, "Lk": c.Lk, "d_k": c.d_k, "d_v": c.d_v, "causal": c.causal,
                    "key_lengths": None if x.key_lengths is None else "U{%d..%d} seed %d" % (
                        c.key_len_range[0], c.key_len_range[1], c.seed),
-                   "input_sets": rotate},
+                   "radius": c.radius, "input_sets": rotate},
         "frac_of_peak": value / PEAK_TFLOPS[c.dtype],
         "roofline": roof,
         "cpu_baseline": cpu,

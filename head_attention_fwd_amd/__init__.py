@@ -24,7 +24,9 @@ from ._binding import (  # noqa: F401
     load_library,
     sdpa_decode,
     sdpa_decode_workspace_bytes,
+    restricted,
     sdpa_forward,
+    sdpa_forward_restricted,
     sdpa_last_hip_error,
     sdpa_status_str,
 )

@@ -24,8 +24,8 @@ SDPA_F32 = 0
 SDPA_BF16 = 1
 
 #: Symbols include/sdpa.h declares.
-EXPORTED = ("sdpa_decode", "sdpa_decode_workspace_bytes", "sdpa_forward", "sdpa_last_hip_error",
-            "sdpa_status_str")
+EXPORTED = ("sdpa_decode", "sdpa_decode_workspace_bytes", "sdpa_forward",
+            "sdpa_forward_restricted", "sdpa_last_hip_error", "sdpa_status_str")
 
 _lib = None
 
@@ -51,6 +51,9 @@ def load_library(path: str = LIBRARY):
     lib.sdpa_forward.restype = ctypes.c_int
     lib.sdpa_forward.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64,
                                  i64, ctypes.c_int, vp]
+    lib.sdpa_forward_restricted.restype = ctypes.c_int
+    lib.sdpa_forward_restricted.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, vp, i64, i64, i64,
+                                            i64, i64, i64, ctypes.c_int, vp]
     lib.sdpa_decode.restype = ctypes.c_int
     lib.sdpa_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                 vp, i64, vp]
@@ -71,6 +74,16 @@ def sdpa_forward(Q: int, K: int, V: int, key_lengths: int, causal: int, out: int
     return load_library().sdpa_forward(Q or None, K or None, V or None, key_lengths or None,
                                        int(causal), out or None, B, H, Lq, Lk, d_k, d_v,
                                        int(dtype), stream or None)
+
+
+def sdpa_forward_restricted(Q: int, K: int, V: int, key_lengths: int, causal: int, radius: int,
+                            out: int, B: int, H: int, Lq: int, Lk: int, d_k: int, d_v: int,
+                            dtype: int, stream: int) -> int:
+    """Raw C call; pointers and the stream are integers (0 = NULL).  Returns the status."""
+    return load_library().sdpa_forward_restricted(Q or None, K or None, V or None,
+                                                  key_lengths or None, int(causal), int(radius),
+                                                  out or None, B, H, Lq, Lk, d_k, d_v, int(dtype),
+                                                  stream or None)
 
 
 def sdpa_decode(Q: int, K: int, V: int, key_lengths: int, out: int, B: int, H: int, Lq: int,
@@ -163,6 +176,23 @@ def forward(q, k, v, key_lengths=None, causal: bool = False, out=None):
                           0 if key_lengths is None else key_lengths.data_ptr(), int(bool(causal)),
                           out.data_ptr(), B, H, Lq, Lk, d_k, d_v, dtype, stream)
     _raise(st, "sdpa_forward")
+    return out
+
+
+def restricted(q, k, v, radius: int, key_lengths=None, causal: bool = False, out=None):
+    """Restricted self-attention (sdpa_forward_restricted): forward() with key j
+    also illegal for query i when |i - j| > radius.  Tensors as for forward()."""
+    import torch
+
+    (B, H, Lq, Lk, d_k, d_v), dtype, key_lengths, out = _check(q, k, v, key_lengths, out)
+    dev = q.device
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = sdpa_forward_restricted(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     0 if key_lengths is None else key_lengths.data_ptr(),
+                                     int(bool(causal)), int(radius), out.data_ptr(), B, H, Lq, Lk,
+                                     d_k, d_v, dtype, stream)
+    _raise(st, "sdpa_forward_restricted")
     return out
 
 

@@ -93,17 +93,27 @@ sdpa_status validate(const void *Q, const void *K, const void *V, const int32_t 
     return SDPA_OK;
 }
 
+// radius < 0: unrestricted attention; radius >= 0: keys within radius of the
+// query row only (restricted self-attention).
 sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                             int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                            int64_t d_k, int64_t d_v, sdpa_dtype dtype, hipStream_t s)
+                            int64_t d_k, int64_t d_v, sdpa_dtype dtype, hipStream_t s,
+                            int64_t radius = -1)
 {
+    // A radius that reaches every key restricts nothing: same kernels, same
+    // result as unrestricted attention.
+    if (radius >= Lq || radius >= Lk) radius = -1;
     // Lk == 0 needs no special case: both kernels then stage no key tile and
     // write 0 for every row (no legal connection).
-    if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128))
+    if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128)) {
+        if (radius >= 0)
+            return hip_status(sdpa::launch_mfma_band(Q, K, V, key_lengths, causal ? 1 : 0, radius, out,
+                                                     B, H, Lq, Lk, (int)d_k, s));
         return hip_status(sdpa::launch_mfma(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
                                             (int)d_k, s));
-    return hip_status(sdpa::launch_generic(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
-                                           (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
+    }
+    return hip_status(sdpa::launch_generic(Q, K, V, key_lengths, causal ? 1 : 0, radius, out, B, H,
+                                           Lq, Lk, (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
 }
 
 // The key-split path of sdpa_decode: bf16, d = 64, one 32-row wave per chunk.
@@ -167,6 +177,19 @@ sdpa_status sdpa_forward(const void *Q, const void *K, const void *V,
     if (st != SDPA_OK || z.empty) return st;
     return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dtype,
                            (hipStream_t)stream);
+}
+
+sdpa_status sdpa_forward_restricted(const void *Q, const void *K, const void *V,
+                                    const int32_t *key_lengths, int causal, int64_t radius,
+                                    void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                    int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream)
+{
+    if (radius < 0) return SDPA_ERR_BAD_SHAPE;
+    Sizes z;
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    if (st != SDPA_OK || z.empty) return st;
+    return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dtype,
+                           (hipStream_t)stream, radius);
 }
 
 int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk,

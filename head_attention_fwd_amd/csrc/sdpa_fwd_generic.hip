@@ -2,7 +2,9 @@
 // fp32 or bf16 storage, fp32 arithmetic, no matrix cores.
 //
 // Computes Eq. (1) of page "Attention Is All You Need/paper/es" (§3.2.1),
-// softmax(Q K^T / sqrt(d_k)) V, with -inf for illegal connections (§3.2.3).
+// softmax(Q K^T / sqrt(d_k)) V, with -inf for illegal connections (§3.2.3)
+// and, given a radius, for keys outside the neighbourhood of restricted
+// self-attention (§4, Table 1).
 // It is the path for fp32 inputs and for head sizes the matrix-core kernel is
 // not built for.
 //
@@ -45,7 +47,7 @@ __device__ inline __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }  // nea
 template <typename T, int DMAX>
 __global__ __launch_bounds__(kRows) void sdpa_fwd_generic_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V,
-    const int32_t *__restrict__ key_lengths, int causal, T *__restrict__ O,
+    const int32_t *__restrict__ key_lengths, int causal, int64_t radius, T *__restrict__ O,
     int H, int64_t Lq, int64_t Lk, int d_k, int d_v, float scale, uint32_t n_qtiles)
 {
     __shared__ float Ks[kTK][DMAX];
@@ -63,9 +65,16 @@ __global__ __launch_bounds__(kRows) void sdpa_fwd_generic_kernel(
         int64_t l = key_lengths[b];
         len = l < 0 ? 0 : (l > Lk ? Lk : l);
     }
-    // Keys this workgroup can use: j < len and, if causal, j <= i < q0 + kRows.
+    // Keys this workgroup can use: j < len and, if causal, j <= i < q0 + kRows;
+    // with a radius (restricted self-attention), q0 - radius <= j <
+    // q0 + kRows + radius.
     int64_t kv_end = len;
     if (causal && q0 + kRows < kv_end) kv_end = q0 + kRows;
+    int64_t kv_begin = 0;
+    if (radius >= 0) {
+        if (q0 + kRows + radius < kv_end) kv_end = q0 + kRows + radius;
+        kv_begin = q0 > radius ? q0 - radius : 0;
+    }
 
     float q[DMAX];
     float acc[DMAX];
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(kRows) void sdpa_fwd_generic_kernel(
     const T *Kh = K + bh * Lk * d_k;
     const T *Vh = V + bh * Lk * d_v;
 
-    for (int64_t j0 = 0; j0 < kv_end; j0 += kTK) {
+    for (int64_t j0 = kv_begin; j0 < kv_end; j0 += kTK) {
         __syncthreads();
         // Stage rows j0 .. j0+kTK-1; rows at or beyond kv_end are zero-filled,
         // so padding contents (even NaN) never reach the arithmetic.
@@ -101,7 +110,8 @@ __global__ __launch_bounds__(kRows) void sdpa_fwd_generic_kernel(
             float dot = 0.f;
 #pragma unroll
             for (int t = 0; t < DMAX; ++t) dot = fmaf(q[t], Ks[r][t], dot);
-            const bool legal = j < kv_end && (!causal || j <= i);
+            const bool legal = j < kv_end && (!causal || j <= i) &&
+                               (radius < 0 || (j >= i - radius && j <= i + radius));
             s[r] = legal ? dot * scale : -INFINITY;
             tile_max = fmaxf(tile_max, s[r]);
         }
@@ -134,41 +144,42 @@ __global__ __launch_bounds__(kRows) void sdpa_fwd_generic_kernel(
 
 template <typename T, int DMAX>
 hipError_t launch_t(const void *Q, const void *K, const void *V, const int32_t *kl,
-                    int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                    int d_k, int d_v, hipStream_t stream)
+                    int causal, int64_t radius, void *out, int64_t B, int64_t H, int64_t Lq,
+                    int64_t Lk, int d_k, int d_v, hipStream_t stream)
 {
     const uint32_t n_qtiles = (uint32_t)((Lq + kRows - 1) / kRows);
     const dim3 grid((unsigned)(n_qtiles * B * H));
     const float scale = (float)(1.0 / sqrt((double)d_k));
     hipLaunchKernelGGL((sdpa_fwd_generic_kernel<T, DMAX>), grid, dim3(kRows), 0, stream,
-                       (const T *)Q, (const T *)K, (const T *)V, kl, causal, (T *)out,
+                       (const T *)Q, (const T *)K, (const T *)V, kl, causal, radius, (T *)out,
                        (int)H, Lq, Lk, d_k, d_v, scale, n_qtiles);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_d(const void *Q, const void *K, const void *V, const int32_t *kl,
-                    int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                    int causal, int64_t r, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                     int d_k, int d_v, hipStream_t stream)
 {
     const int d = d_k > d_v ? d_k : d_v;
-    if (d <= 8) return launch_t<T, 8>(Q, K, V, kl, causal, out, B, H, Lq, Lk, d_k, d_v, stream);
-    if (d <= 32) return launch_t<T, 32>(Q, K, V, kl, causal, out, B, H, Lq, Lk, d_k, d_v, stream);
-    if (d <= 64) return launch_t<T, 64>(Q, K, V, kl, causal, out, B, H, Lq, Lk, d_k, d_v, stream);
-    return launch_t<T, 128>(Q, K, V, kl, causal, out, B, H, Lq, Lk, d_k, d_v, stream);
+    if (d <= 8) return launch_t<T, 8>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
+    if (d <= 32) return launch_t<T, 32>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
+    if (d <= 64) return launch_t<T, 64>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
+    return launch_t<T, 128>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
 }
 
 }  // namespace
 
 hipError_t launch_generic(const void *Q, const void *K, const void *V,
-                          const int32_t *key_lengths, int causal, void *out,
+                          const int32_t *key_lengths, int causal, int64_t radius, void *out,
                           int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                           int d_k, int d_v, bool is_bf16, hipStream_t stream)
 {
     if (is_bf16)
-        return launch_d<__bf16>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v,
+        return launch_d<__bf16>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, d_k, d_v,
                                 stream);
-    return launch_d<float>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, stream);
+    return launch_d<float>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, d_k, d_v,
+                           stream);
 }
 
 }  // namespace sdpa

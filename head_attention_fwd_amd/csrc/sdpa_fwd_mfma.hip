@@ -246,8 +246,9 @@ __device__ inline void wait_vmem_keep() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(
 // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left at their maxima.
 constexpr int kWaitLds0 = 15 | (3 << 14) | (7 << 4);
 
-// Per-wave state of the forward pass and the work on one key tile.
-template <int NW, int NB, int D>
+// Per-wave state of the forward pass and the work on one key tile.  BAND:
+// restricted self-attention, keys within `radius` of the query row only.
+template <int NW, int NB, int D, bool BAND = false>
 struct Attn {
     static constexpr int kD = D;                 // d_k = d_v
     static constexpr int kRowBytes = 2 * D;      // one K or V row in HBM and LDS
@@ -272,6 +273,8 @@ struct Attn {
     int l32;                         // this lane's query row is q0w + l32
     int causal;
     int n_tiles;
+    int64_t qrel;                    // BAND: q0w relative to the first key of the range
+    int64_t radius;                  // BAND: neighbourhood radius
     float scale_log2;
     int g;                           // lane half
 
@@ -480,7 +483,8 @@ struct Attn {
     // with no legal key for any row of the wave contributes exactly 0.
     // Decisions are per row, so a row's result depends on its own legal keys
     // only.
-    __device__ __forceinline__ void tile_blocks_masked(const uint16_t *Ks, const uint16_t *Vs, int lim)
+    __device__ __forceinline__ void tile_blocks_masked(const uint16_t *Ks, const uint16_t *Vs, int lim,
+                                                       int lo = 0)
     {
         f32x16_t s[NB];
         bf16x8_t p[NB][2];
@@ -489,9 +493,19 @@ struct Attn {
         for (int b = 0; b < NB; ++b) {
             // the per-register part is a constant compared with lim - 8g - 32b
             const int lim_g = lim - 8 * g - 32 * b;
+            if constexpr (BAND) {
+                // BAND: keys below offset lo are out of the row's neighbourhood too
+                const int lo_g = lo - 8 * g - 32 * b;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 16 * (r >> 3) + (r & 7);
+                    if (off >= lim_g || off < lo_g) s[b][r] = -INFINITY;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;
+            }
             const float mxs = block_max(s[b]);
             if (b > 0) pv(Vs, b - 1, p[b - 1]);
             rescale_if_needed(mxs);
@@ -555,6 +569,23 @@ struct Attn {
         const int nxt = (t + 2) % 3;
         tile_begin(t, kbuf[0] + nxt * kBufStride, vbuf[0] + nxt * kBufStride);
         const int64_t kv0 = (int64_t)t * BN;
+        if constexpr (BAND) {
+            // Rows qrel .. qrel+31 (relative to the range's first key) may use
+            // keys qrel - radius .. qrel + 31 + radius (and, if causal, up to
+            // their own row); a wave with none in this tile has nothing to do.
+            if (kv0 + BN - 1 < qrel - radius || kv0 > qrel + 31 + radius || (causal && kv0 > qrel + 31))
+                return;
+            int64_t lim64 = len - kv0;
+            const int64_t band_lim = (qrel - kv0) + l32 + radius + 1;
+            if (band_lim < lim64) lim64 = band_lim;
+            const int64_t causal_lim = (qrel - kv0) + l32 + 1;
+            if (causal && causal_lim < lim64) lim64 = causal_lim;
+            const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));
+            const int64_t lo64 = (qrel - kv0) + l32 - radius;
+            const int lo = (int)(lo64 < 0 ? 0 : (lo64 > BN ? BN : lo64));
+            tile_blocks_masked(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim, lo);
+            return;
+        }
         // A wave whose rows all precede the tile's first key has nothing to do.
         if (causal && kv0 > q0w + 31) return;
         // Keys this lane may use in the tile: below the key length and, if
@@ -572,6 +603,10 @@ struct Attn {
     // waves of a workgroup may switch between the phases at different tiles.
     __device__ __forceinline__ void run()
     {
+        if constexpr (BAND) {
+            run_band();
+            return;
+        }
         if (n_tiles == 0) return;
         // Tiles 1 .. n_full-1 are fully legal for every row of this wave.
         int64_t n_full = len / BN;
@@ -594,6 +629,47 @@ struct Attn {
             }
         }
     }
+
+    // BAND: the fully legal tiles of this wave form the middle range
+    // [f_lo, f_hi): every key of such a tile lies within every row's
+    // neighbourhood (and below the key length, and not after the row if
+    // causal), and every row has met a legal key in an earlier tile, so its
+    // reference maximum is finite as the max-free path requires.  The tiles
+    // before and after go block by block with masks.
+    __device__ __forceinline__ void run_band()
+    {
+        if (n_tiles == 0) return;
+        // first tile start >= qrel + 32 - radius: every row's lowest legal key
+        // (qrel + l32 - radius) lies before it
+        const int64_t lo_key = qrel + 32 - radius;
+        int64_t f_lo = lo_key <= 0 ? 1 : (lo_key + BN - 1) / BN;
+        if (f_lo < 1) f_lo = 1;
+        int64_t f_hi = len / BN;
+        const int64_t up = (qrel + radius + 1) / BN;   // (t+1)*BN - 1 <= qrel + radius
+        if (up < f_hi) f_hi = up;
+        if (causal) {
+            const int64_t diag = (qrel + 1) / BN;
+            if (diag < f_hi) f_hi = diag;
+        }
+        for (int t = 0; t < n_tiles;) {
+            if (t == f_lo && f_hi > f_lo) {
+                // tile f_lo landed before tile f_lo-1's barrier; enter the ring
+                // at its phase
+                f32x16_t s_io = scores(kbuf[0] + (t % 3) * kBufStride, 0);
+                if (t % 3 == 2) tile_full<2>(t++, s_io);
+                if (t % 3 == 0 && t < f_hi) tile_full<0>(t++, s_io);
+                for (; t + 2 < f_hi; t += 3) {
+                    tile_full<1>(t, s_io);
+                    tile_full<2>(t + 1, s_io);
+                    tile_full<0>(t + 2, s_io);
+                }
+                if (t < f_hi) tile_full<1>(t++, s_io);
+                if (t < f_hi) tile_full<2>(t++, s_io);
+            } else {
+                tile_any(t++);
+            }
+        }
+    }
 };
 
 // Key-split mode (several query rows against a long key range, split over
@@ -611,14 +687,15 @@ struct SplitOut {
 
 // One query tile (BM rows of head bh) against keys [kv_lo, kv_hi): load Q,
 // stream the key tiles, store O (or, with SPLIT, the partial result).
-template <int NW, int NB, int D, bool SPLIT>
+template <int NW, int NB, int D, bool SPLIT, bool BAND = false>
 __device__ __forceinline__ void attend_query_tile(
     uint16_t *const *kbuf, uint16_t *const *vbuf, const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
-    uint32_t bh, uint32_t qt, int wave, int lane, int64_t kv_lo, int64_t kv_hi, const SplitOut &so, uint32_t u)
+    uint32_t bh, uint32_t qt, int wave, int lane, int64_t kv_lo, int64_t kv_hi, const SplitOut &so, uint32_t u,
+    int64_t radius = 0)
 {
-    using A = Attn<NW, NB, D>;
+    using A = Attn<NW, NB, D, BAND>;
     constexpr int BM = A::BM;
     constexpr int BN = A::BN;
     constexpr int kD = D, kRowBytes = A::kRowBytes, kKB = A::kKB, kDB = A::kDB;
@@ -640,13 +717,25 @@ __device__ __forceinline__ void attend_query_tile(
         const int64_t l = key_lengths[b];
         len = l < 0 ? 0 : (l > Lk ? Lk : l);
     }
+    if constexpr (BAND) {
+        // The workgroup's rows q0 .. q0+BM-1 use keys from q0 - radius on.
+        kv_lo = q0 > radius ? q0 - radius : 0;
+        st.radius = radius;
+        st.qrel = st.q0w - kv_lo;
+    }
     // Legal keys of this workgroup's range, counted from kv_lo (the causal
-    // mask is only used with kv_lo = 0).
+    // mask is only used with kv_lo = 0 or, BAND, through qrel).
     len = (len < kv_hi ? len : kv_hi) - kv_lo;
     len = len < 0 ? 0 : len;
     st.len = len;
     int64_t kv_end = len;                        // keys the workgroup needs
-    if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
+    if constexpr (BAND) {
+        const int64_t q_end = q0 - kv_lo + BM;   // one past the last row, relative
+        if (q_end + radius < kv_end) kv_end = q_end + radius;
+        if (causal && q_end < kv_end) kv_end = q_end;
+    } else {
+        if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
+    }
     st.n_tiles = (int)((kv_end + BN - 1) / BN);
 
     st.Kh = K + ((int64_t)bh * Lk + kv_lo) * kD;
@@ -822,12 +911,13 @@ __device__ __forceinline__ void attend_query_tile(
 //  * Causal: a query tile's work grows with qt, so the tiles go out longest
 //    first (qt descending), which fills the slots greedily longest-first and
 //    leaves only short tiles for the end of the grid.  When 8 divides the head
-//    count each XCD takes its own run of heads, in groups of
-//    SDPA_CAUSAL_HEAD_GROUP heads one after the other, longest first within a
-//    group: fewer heads in flight keep more of their K/V rows in the XCD's L2
-//    (on 8 heads of 8192 keys per XCD: 4 at a time fetched 550 MiB per launch
-//    into L2, all 8 at once 1188 MiB, one at a time 196 MiB but with the long
-//    tiles of the last head starting late).
+//    count each XCD takes its own run of heads; when a head's K and V reach
+//    1 MiB, in groups of SDPA_CAUSAL_HEAD_GROUP heads one after the other,
+//    longest first within a group: fewer heads in flight keep more of their
+//    K/V rows in the XCD's L2 (on 8 heads of 8192 keys per XCD: 4 at a time
+//    fetched 550 MiB per launch into L2, all 8 at once 1188 MiB, one at a time
+//    196 MiB but with the long tiles of the last head starting late).  Short
+//    heads fit the L2 together, and taking all of them at once balances best.
 template <int NW, int NB, int D>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves))) void sdpa_fwd_mfma_kernel(
@@ -854,8 +944,11 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves)))
     if (causal) {
         if ((n_bh & 7) == 0) {
             const uint32_t hx = n_bh >> 3, j = w >> 3;   // heads per XCD, position in the XCD
-            // groups of G heads in turn, longest tiles first within a group
-            const uint32_t G = (SDPA_CAUSAL_HEAD_GROUP > 0 && hx % SDPA_CAUSAL_HEAD_GROUP == 0)
+            // groups of G heads in turn, longest tiles first within a group,
+            // once a head's K and V reach 1 MiB (smaller ones share the L2
+            // anyway, and all heads at once balance better)
+            const bool big = (uint64_t)Lk * (4 * D) >= (1u << 20);
+            const uint32_t G = (big && SDPA_CAUSAL_HEAD_GROUP > 0 && hx % SDPA_CAUSAL_HEAD_GROUP == 0)
                                    ? SDPA_CAUSAL_HEAD_GROUP : hx;
             const uint32_t grp = j / (G * n_qtiles), r = j % (G * n_qtiles);
             bh = (w & 7) * hx + grp * G + r % G;
@@ -872,6 +965,36 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves)))
     }
     attend_query_tile<NW, NB, D, false>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk,
                                      scale_log2, bh, qt, wave, lane, 0, Lk, SplitOut{}, 0);
+}
+
+
+// Restricted self-attention: every workgroup covers about BM + 2 * radius
+// keys, so the work is even and the non-causal order (head-major runs per XCD)
+// is used.
+template <int NW, int NB, int D>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves))) void sdpa_fwd_mfma_band_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
+    int64_t radius, uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
+    uint32_t n_qtiles, uint32_t n_bh)
+{
+    using A = Attn<NW, NB, D, true>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
+    uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
+#pragma unroll
+    for (int i = 0; i < A::kBuffers; ++i) {
+        kbuf[i] = lds + i * A::kBufStride;
+        vbuf[i] = kbuf[i] + A::kTileElems;
+    }
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t w = blockIdx.x;
+    const uint32_t n_items = n_qtiles * n_bh;
+    const uint32_t item = (n_items & 7) == 0 ? (w & 7) * (n_items >> 3) + (w >> 3) : w;
+    attend_query_tile<NW, NB, D, false, true>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk,
+                                              scale_log2, item / n_qtiles, item % n_qtiles, wave, lane,
+                                              0, Lk, SplitOut{}, 0, radius);
 }
 
 
@@ -984,7 +1107,37 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_mfma_band_d(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                              int causal, int64_t radius, void *out, int64_t B, int64_t H, int64_t Lq,
+                              int64_t Lk, hipStream_t stream)
+{
+    constexpr int NW = SDPA_MFMA_WAVES;
+    constexpr int NB = D >= 128 ? 1 : SDPA_MFMA_KEY_BLOCKS;
+    constexpr int BM = 32 * NW;
+    const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
+    const uint32_t n_bh = (uint32_t)(B * H);
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    hipLaunchKernelGGL((sdpa_fwd_mfma_band_kernel<NW, NB, D>), dim3(n_qtiles * n_bh),
+                       dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
+                       (const uint16_t *)V, key_lengths, causal, radius, (uint16_t *)out, (int)H, Lq,
+                       Lk, scale_log2, n_qtiles, n_bh);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_mfma_band(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                            int causal, int64_t radius, void *out, int64_t B, int64_t H, int64_t Lq,
+                            int64_t Lk, int d, hipStream_t stream)
+{
+    switch (d) {
+    case 32: return launch_mfma_band_d<32>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, stream);
+    case 64: return launch_mfma_band_d<64>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, stream);
+    case 128: return launch_mfma_band_d<128>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_mfma(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                        int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,

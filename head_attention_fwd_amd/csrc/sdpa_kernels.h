@@ -11,9 +11,10 @@
 namespace sdpa {
 
 // Any 1 <= d_k, d_v <= 128; elements are fp32 (is_bf16 = false) or bf16.
-// fp32 arithmetic throughout; one lane per query row.
+// fp32 arithmetic throughout; one lane per query row.  radius >= 0: restricted
+// self-attention (|i - j| <= radius); radius < 0: no restriction.
 hipError_t launch_generic(const void *Q, const void *K, const void *V,
-                          const int32_t *key_lengths, int causal, void *out,
+                          const int32_t *key_lengths, int causal, int64_t radius, void *out,
                           int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                           int d_k, int d_v, bool is_bf16, hipStream_t stream);
 
@@ -23,6 +24,13 @@ hipError_t launch_mfma(const void *Q, const void *K, const void *V,
                        const int32_t *key_lengths, int causal, void *out,
                        int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
                        hipStream_t stream);
+
+// As launch_mfma, restricted self-attention: key j is legal for query i only
+// when |i - j| <= radius (radius >= 0).
+hipError_t launch_mfma_band(const void *Q, const void *K, const void *V,
+                            const int32_t *key_lengths, int causal, int64_t radius, void *out,
+                            int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
+                            hipStream_t stream);
 
 // bf16, d_k = d_v = 64, Lq <= 32, no causal mask: keys split into n_split chunks
 // of `chunk` keys per head (chunk a multiple of 64, n_split * chunk >= Lk),

@@ -11,12 +11,27 @@ def clamp_length(length, Lk):
     return int(min(max(int(length), 0), Lk))
 
 
-def pair_count(B, H, Lq, Lk, causal, key_lengths=None):
+def _band_pairs(Lq, lb, causal, radius):
+    """Allowed pairs of one sequence when |i - j| <= radius is also required."""
+    import numpy as np
+    i = np.arange(Lq, dtype=np.int64)
+    lo = np.maximum(i - radius, 0)
+    hi = np.minimum(i + radius, lb - 1)
+    if causal:
+        hi = np.minimum(hi, i)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def pair_count(B, H, Lq, Lk, causal, key_lengths=None, radius=None):
     """Number of (query, key) pairs the mask allows, summed over batch and heads.
 
     Key j is allowed for query i when j < len_b and, for causal attention, j <= i;
-    len_b = clamp(key_lengths[b], 0, Lk), or Lk without key_lengths.
+    len_b = clamp(key_lengths[b], 0, Lk), or Lk without key_lengths.  With a
+    radius (restricted self-attention, §4 of the same page), also |i - j| <= radius.
     """
+    if radius is not None:
+        return H * sum(_band_pairs(Lq, Lk if key_lengths is None else clamp_length(key_lengths[b], Lk),
+                                   causal, int(radius)) for b in range(B))
     total = 0
     for b in range(B):
         lb = Lk if key_lengths is None else clamp_length(key_lengths[b], Lk)
@@ -30,21 +45,23 @@ def pair_count(B, H, Lq, Lk, causal, key_lengths=None):
     return total * H
 
 
-def flops(B, H, Lq, Lk, d_k, d_v, causal, key_lengths=None):
+def flops(B, H, Lq, Lk, d_k, d_v, causal, key_lengths=None, radius=None):
     """Algorithmic FLOPs: (2*d_k + 2*d_v) per allowed pair."""
-    return (2 * d_k + 2 * d_v) * pair_count(B, H, Lq, Lk, causal, key_lengths)
+    return (2 * d_k + 2 * d_v) * pair_count(B, H, Lq, Lk, causal, key_lengths, radius)
 
 
-def min_bytes(B, H, Lq, Lk, d_k, d_v, causal, key_lengths=None, elem=2):
+def min_bytes(B, H, Lq, Lk, d_k, d_v, causal, key_lengths=None, elem=2, radius=None):
     """Algorithmic HBM bytes: Q and O once, and every key/value row some query may use.
 
     Rows j >= len_b are never needed; causal attention with Lq < Lk never needs
-    rows j >= Lq.
+    rows j >= Lq, and with a radius no row needs keys j >= Lq + radius.
     """
     rows_kv = 0
     for b in range(B):
         lb = Lk if key_lengths is None else clamp_length(key_lengths[b], Lk)
         if causal:
             lb = min(lb, Lq)
+        if radius is not None:
+            lb = min(lb, Lq + int(radius)) if Lq > 0 else 0
         rows_kv += lb
     return elem * H * (B * Lq * (d_k + d_v) + rows_kv * (d_k + d_v))

@@ -95,6 +95,25 @@ sdpa_status sdpa_forward(const void *Q, const void *K, const void *V,
                          int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream);
 
 /*
+ * Restricted self-attention (page "Attention Is All You Need/paper/es", §4 and
+ * Table 1: each output position considers only a neighbourhood of size r of
+ * the sequence centred on it; work O(r n d) per layer instead of O(n^2 d)).
+ * The neighbourhood is given by its radius: key j is additionally illegal for
+ * query i when |i - j| > radius, i.e. r = 2 * radius + 1 positions (fewer at
+ * the ends of the sequence).  Positions i and j are compared as in the causal
+ * mask (top-left aligned when Lq != Lk).  Every other argument, the layout,
+ * the arithmetic, the ownership rules and the errors are those of
+ * sdpa_forward; with radius >= max(Lq, Lk) - 1 the result is exactly
+ * sdpa_forward's.  Only the key tiles that meet some row's neighbourhood are
+ * read.
+ *   radius       >= 0 (SDPA_ERR_BAD_SHAPE otherwise, before any HIP call).
+ */
+sdpa_status sdpa_forward_restricted(const void *Q, const void *K, const void *V,
+                                    const int32_t *key_lengths, int causal, int64_t radius,
+                                    void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                    int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream);
+
+/*
  * Decode-step attention: the same result as sdpa_forward with causal = 0, for
  * the case of a few query rows per head against a long key/value cache (the
  * new positions of an autoregressive decoder, page "Attention Is All You

@@ -148,3 +148,35 @@ def test_decode_empty_calls():
     assert dcall(Lq=0, ws=0) == sdpa.SDPA_OK
     assert dcall(Q=0, K=0, V=0, O=0, H=0, ws=0) == sdpa.SDPA_OK
     assert sdpa.sdpa_status_str(sdpa.SDPA_ERR_WORKSPACE).startswith("the workspace")
+
+
+# ---- sdpa_forward_restricted: sdpa_forward's checks plus the radius
+
+def rcall(radius=3, **kw):
+    a = dict(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, causal=0, O=FAKE_O, B=2, H=2, Lq=16, Lk=16,
+             dk=64, dv=64, dtype=sdpa.SDPA_BF16)
+    a.update(kw)
+    return sdpa.sdpa_forward_restricted(a["Q"], a["K"], a["V"], a["kl"], a["causal"], radius,
+                                        a["O"], a["B"], a["H"], a["Lq"], a["Lk"], a["dk"], a["dv"],
+                                        a["dtype"], 0)
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(radius=-1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(radius=-2**40), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(radius=-1, B=0), sdpa.SDPA_ERR_BAD_SHAPE),     # checked before the empty-call shortcut
+    (dict(Q=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(O=0, radius=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(Lk=-1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(dk=129), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=7), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(O=FAKE_V + 64), sdpa.SDPA_ERR_ALIAS),
+])
+def test_restricted_prelaunch_validation(kw, expected):
+    assert rcall(**kw) == expected
+
+
+def test_restricted_empty_calls():
+    assert rcall(B=0) == sdpa.SDPA_OK
+    assert rcall(Lq=0, radius=2**40) == sdpa.SDPA_OK
+    assert rcall(Q=0, K=0, V=0, O=0, H=0, radius=0) == sdpa.SDPA_OK

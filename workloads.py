@@ -44,7 +44,9 @@ class Config:
     key_len_range: Optional[tuple]   # inclusive (lo, hi) or None for "no padding"
     scale: float
     seed: int
-    entry: str = "forward"   # "forward": sdpa_forward; "decode": sdpa_decode (causal = False)
+    entry: str = "forward"   # "forward": sdpa_forward; "decode": sdpa_decode (causal = False);
+    #                          "restricted": sdpa_forward_restricted with `radius`
+    radius: Optional[int] = None
 
 
 CONFIGS = {
@@ -85,6 +87,18 @@ CONFIGS = {
         "h = 8 heads of d_k = d_v = 128, inputs scaled by 0.5", "bf16",
         B=4, H=8, Lq=8192, Lk=8192, d_k=128, d_v=128, causal=True, key_len_range=None,
         scale=0.5, seed=9),
+    # Restricted self-attention (§4, Table 1): the long sequence with a
+    # neighbourhood of r = 2 * 255 + 1 = 511 positions around each output.
+    "restricted_long_bf16": Config(
+        "restricted_long_bf16", "long-sequence restricted self-attention, radius 255 "
+        "(neighbourhood of 511 positions), inputs scaled by 0.5", "bf16",
+        B=4, H=16, Lq=8192, Lk=8192, d_k=64, d_v=64, causal=False, key_len_range=None,
+        scale=0.5, seed=10, entry="restricted", radius=255),
+    "restricted_long_causal_bf16": Config(
+        "restricted_long_causal_bf16", "long-sequence restricted causal self-attention "
+        "(the 256 positions up to each output), inputs scaled by 0.5", "bf16",
+        B=4, H=16, Lq=8192, Lk=8192, d_k=64, d_v=64, causal=True, key_len_range=None,
+        scale=0.5, seed=11, entry="restricted", radius=255),
     # Decode steps (sdpa_decode): the new position of an autoregressive decoder
     # against the cache of the positions generated so far (§3.1, §3.2.3).
     "decode_long_bf16": Config(
@@ -103,8 +117,8 @@ CONFIGS = {
 #: forward configurations, the other head sizes, then the decode steps.
 ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
          "big_cross_bf16", "long_causal_bf16", "rowA_h4_d128_encoder_bf16",
-         "rowA_h16_d32_encoder_bf16", "long_causal_d128_bf16", "decode_base_bf16",
-         "decode_long_bf16"]
+         "rowA_h16_d32_encoder_bf16", "long_causal_d128_bf16", "restricted_long_bf16",
+         "restricted_long_causal_bf16", "decode_base_bf16", "decode_long_bf16"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:

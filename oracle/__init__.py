@@ -16,7 +16,9 @@ with mask = -inf where j >= len_b (key padding, len_b = clamp(key_lengths[b],
 0, Lk)), for causal attention where j > i, and for restricted self-attention
 with radius w (same page, §4 and Table 1: a neighbourhood of size r = 2w + 1
 centred on the output position) where |i - j| > w.  A row with no legal key
-is 0.
+is 0.  ``multihead`` adds the projections of §3.2.2 around it:
+MultiHead(Q, K, V) = Concat(head_1..head_h) W^O, head_i = Attention(Q W_i^Q,
+K W_i^K, V W_i^V).
 """
 from __future__ import annotations
 
@@ -100,8 +102,39 @@ class Oracle:
                                               i64, i64, i64, i64,
                                               ctypes.POINTER(ctypes.c_int64), i64, dp, dp,
                                               ctypes.c_int]
+        lib.oracle_multihead.restype = ctypes.c_int
+        lib.oracle_multihead.argtypes = [dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, i64, i64, i64,
+                                         i64, i64, i64, i64, dp, ctypes.c_int]
         self.lib = lib
         self.path = path
+
+    def multihead(self, xq, xkv, wq, wk, wv, wo, h, key_lengths=None, causal=False, nthreads=0):
+        """MultiHead(Q, K, V) = Concat(head_1..head_h) W^O in fp64 (§3.2.2).
+
+        xq [B, Lq, d_model] (queries' sequence), xkv [B, Lk, d_model] (keys' and
+        values' sequence), wq and wk [d_model, h*d_k], wv [d_model, h*d_v],
+        wo [h*d_v, d_model]; head i uses columns i*d .. i*d + d - 1 of wq, wk,
+        wv.  Returns O [B, Lq, d_model]."""
+        xq, xkv = _f64(xq), _f64(xkv)
+        wq, wk, wv, wo = _f64(wq), _f64(wk), _f64(wv), _f64(wo)
+        if xq.ndim != 3 or xkv.ndim != 3:
+            raise ValueError("xq and xkv must be [B, L, d_model]")
+        B, Lq, dm = xq.shape
+        Lk = xkv.shape[1]
+        if xkv.shape != (B, Lk, dm) or wq.shape[0] != dm or wq.shape[1] % h:
+            raise ValueError("inconsistent shapes")
+        dk = wq.shape[1] // h
+        dv = wv.shape[1] // h
+        if wk.shape != (dm, h * dk) or wv.shape != (dm, h * dv) or wo.shape != (h * dv, dm):
+            raise ValueError("inconsistent weight shapes")
+        kl = _lengths(key_lengths, B)
+        O = np.empty((B, Lq, dm), dtype=np.float64)
+        rc = self.lib.oracle_multihead(_ptr(xq), _ptr(xkv), _ptr(wq), _ptr(wk), _ptr(wv),
+                                       _ptr(wo), _ptr(kl, ctypes.c_int32), int(bool(causal)), B,
+                                       Lq, Lk, dm, h, dk, dv, _ptr(O), int(nthreads))
+        if rc != 0:
+            raise RuntimeError("oracle_multihead failed with code %d" % rc)
+        return O
 
     def attention(self, q, k, v, key_lengths=None, causal=False, return_weights=False,
                   nthreads=0, radius=None):
@@ -175,6 +208,11 @@ def attention(q, k, v, key_lengths=None, causal=False, return_weights=False, nth
               radius=None):
     """Full fp64 attention; see Oracle.attention."""
     return default().attention(q, k, v, key_lengths, causal, return_weights, nthreads, radius)
+
+
+def multihead(xq, xkv, wq, wk, wv, wo, h, key_lengths=None, causal=False, nthreads=0):
+    """fp64 multi-head attention; see Oracle.multihead."""
+    return default().multihead(xq, xkv, wq, wk, wv, wo, h, key_lengths, causal, nthreads)
 
 
 def attention_rows(q, k, v, rows, key_lengths=None, causal=False, nthreads=0, radius=None):

@@ -229,3 +229,99 @@ int oracle_attention_rows(const double *Q, const double *K, const double *V,
     }
     return failed ? 2 : 0;
 }
+
+/*
+ * Multi-head attention -- page "Attention Is All You Need/paper/es", §3.2.2:
+ *
+ *   MultiHead(Q, K, V) = Concat(head_1, ..., head_h) W^O
+ *   head_i             = Attention(Q W_i^Q, K W_i^K, V W_i^V)
+ *
+ * with W_i^Q, W_i^K in R^{d_model x d_k}, W_i^V in R^{d_model x d_v} and
+ * W^O in R^{h d_v x d_model}; Attention is oracle_attention above (Eq. (1) with
+ * the masks).  Q is the sequence the queries come from (Xq), K = V the one the
+ * keys and values come from (Xkv; the same sequence for self-attention).
+ *
+ * Storage, all fp64 row-major:
+ *   Xq [B][Lq][d_model], Xkv [B][Lk][d_model], O [B][Lq][d_model];
+ *   Wq [d_model][h*d_k]: W_i^Q is columns i*d_k .. i*d_k + d_k - 1 (Wk alike),
+ *   Wv [d_model][h*d_v], Wo [h*d_v][d_model]: row i*d_v + t multiplies
+ *   component t of head i in the concatenation.
+ * Returns 0 on success, 1 on a bad shape, 2 on allocation failure.
+ */
+int oracle_multihead(const double *Xq, const double *Xkv, const double *Wq, const double *Wk,
+                     const double *Wv, const double *Wo, const int32_t *key_lengths, int causal,
+                     int64_t B, int64_t Lq, int64_t Lk, int64_t d_model, int64_t h,
+                     int64_t d_k, int64_t d_v, double *O, int nthreads)
+{
+    if (B < 0 || Lq < 0 || Lk < 0 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1) return 1;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#endif
+    const size_t nq = (size_t)(B * h * Lq), nk = (size_t)(B * h * Lk);
+    double *Qp = (double *)malloc((nq * d_k + 1) * sizeof(double));
+    double *Kp = (double *)malloc((nk * d_k + 1) * sizeof(double));
+    double *Vp = (double *)malloc((nk * d_v + 1) * sizeof(double));
+    double *A = (double *)malloc((nq * d_v + 1) * sizeof(double));
+    int rc = 0;
+    if (!Qp || !Kp || !Vp || !A) {
+        rc = 2;
+        goto done;
+    }
+
+    /* The h projections of each position: row x of the source sequence times
+     * W_i (Q W_i^Q etc.), stored per head as [B][h][L][d]. */
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t r = 0; r < B * Lq; ++r) {
+        const int64_t b = r / Lq, i = r % Lq;
+        const double *x = Xq + r * d_model;
+        for (int64_t hd = 0; hd < h; ++hd)
+            for (int64_t t = 0; t < d_k; ++t) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_model; ++c) acc += x[c] * Wq[c * (h * d_k) + hd * d_k + t];
+                Qp[((b * h + hd) * Lq + i) * d_k + t] = acc;
+            }
+    }
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t r = 0; r < B * Lk; ++r) {
+        const int64_t b = r / Lk, j = r % Lk;
+        const double *x = Xkv + r * d_model;
+        for (int64_t hd = 0; hd < h; ++hd) {
+            for (int64_t t = 0; t < d_k; ++t) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_model; ++c) acc += x[c] * Wk[c * (h * d_k) + hd * d_k + t];
+                Kp[((b * h + hd) * Lk + j) * d_k + t] = acc;
+            }
+            for (int64_t t = 0; t < d_v; ++t) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < d_model; ++c) acc += x[c] * Wv[c * (h * d_v) + hd * d_v + t];
+                Vp[((b * h + hd) * Lk + j) * d_v + t] = acc;
+            }
+        }
+    }
+
+    /* head_i for every head (the attention of §3.2.1 on the projections) */
+    rc = oracle_attention(Qp, Kp, Vp, key_lengths, causal, -1, B, h, Lq, Lk, d_k, d_v, A, NULL,
+                          NULL, nthreads);
+    if (rc != 0) goto done;
+
+    /* Concat(head_1, ..., head_h) W^O: component t of head i is column
+     * i*d_v + t of the concatenation. */
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t r = 0; r < B * Lq; ++r) {
+        const int64_t b = r / Lq, i = r % Lq;
+        for (int64_t c = 0; c < d_model; ++c) {
+            double acc = 0.0;
+            for (int64_t hd = 0; hd < h; ++hd)
+                for (int64_t t = 0; t < d_v; ++t)
+                    acc += A[((b * h + hd) * Lq + i) * d_v + t] * Wo[(hd * d_v + t) * d_model + c];
+            O[r * d_model + c] = acc;
+        }
+    }
+
+done:
+    free(Qp);
+    free(Kp);
+    free(Vp);
+    free(A);
+    return rc;
+}

@@ -55,3 +55,37 @@ def attention(q, k, v, key_lengths=None, causal=False, radius=None):
             out_b.append(out_h)
         out.append(out_b)
     return out
+
+
+def multihead(xq, xkv, wq, wk, wv, wo, h, key_lengths=None, causal=False):
+    """MultiHead(Q, K, V) = Concat(head_1..head_h) W^O, head_i = Attention(Q W_i^Q,
+    K W_i^K, V W_i^V) (same page, §3.2.2), by plain loops: every projection is an
+    exactly rounded sum over d_model, the heads go through ``attention`` above,
+    and the concatenation is built explicitly before the product with W^O.
+
+    xq [B][Lq][d_model], xkv [B][Lk][d_model], wq/wk [d_model][h*d_k],
+    wv [d_model][h*d_v], wo [h*d_v][d_model].  Returns nested lists [B][Lq][d_model].
+    """
+    B, Lq, dm = len(xq), len(xq[0]), len(xq[0][0])
+    Lk = len(xkv[0])
+    dk = len(wq[0]) // h
+    dv = len(wv[0]) // h
+
+    def project(x, w, L, d):
+        # [B][h][L][d]: head i of position j is row j of x times columns i*d.. of w
+        return [[[[math.fsum(float(x[b][j][c]) * float(w[c][i * d + t]) for c in range(dm))
+                   for t in range(d)] for j in range(L)] for i in range(h)] for b in range(B)]
+
+    q = project(xq, wq, Lq, dk)
+    k = project(xkv, wk, Lk, dk)
+    v = project(xkv, wv, Lk, dv)
+    heads = attention(q, k, v, key_lengths, causal)          # [B][h][Lq][dv]
+    out = []
+    for b in range(B):
+        rows = []
+        for i in range(Lq):
+            concat = [heads[b][hd][i][t] for hd in range(h) for t in range(dv)]
+            rows.append([math.fsum(concat[r] * float(wo[r][c]) for r in range(h * dv))
+                         for c in range(dm)])
+        out.append(rows)
+    return out

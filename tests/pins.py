@@ -349,6 +349,68 @@ def check_restricted_locality(orc):
     _close(wide, orc.attention(q, k, v), 0.0, "radius >= L - 1 is unrestricted")
 
 
+# ---------------------------------------------------------------- multi-head
+
+def _mh_rand(seed, B=2, Lq=5, Lk=6, dm=6, h=2, dk=3, dv=2):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, Lq, dm)), rng.standard_normal((B, Lk, dm)),
+            rng.standard_normal((dm, h * dk)) / math.sqrt(dm),
+            rng.standard_normal((dm, h * dk)) / math.sqrt(dm),
+            rng.standard_normal((dm, h * dv)) / math.sqrt(dm),
+            rng.standard_normal((h * dv, dm)) / math.sqrt(h * dv))
+
+
+def check_multihead_identity_is_attention(orc):
+    """h = 1, d_k = d_v = d_model and every W the identity: MultiHead(X, X, X) is
+    Attention(X, X, X) of Eq. (1) (scale 1/sqrt(d_model))."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((2, 5, 4))
+    eye = np.eye(4)
+    for causal, lens in ((False, None), (True, [5, 3])):
+        got = orc.multihead(x, x, eye, eye, eye, eye, 1, key_lengths=lens, causal=causal)
+        ref = orc.attention(x[:, None], x[:, None], x[:, None], key_lengths=lens, causal=causal)
+        _close(got, ref[:, 0], 1e-12, "multihead identity causal=%d" % causal)
+
+
+def check_multihead_bruteforce(orc):
+    """Agreement with the plain-loop brute force: self- and cross-attention,
+    masks, d_k != d_v."""
+    for seed, causal, lens, self_attn in ((42, False, None, True), (43, True, [5, 2], True),
+                                          (44, False, [6, 1], False), (45, True, None, False)):
+        xq, xkv, wq, wk, wv, wo = _mh_rand(seed)
+        if self_attn:
+            xkv = xq
+        ref = np.array(bruteforce.multihead(xq, xkv, wq, wk, wv, wo, 2, lens, causal))
+        _close(orc.multihead(xq, xkv, wq, wk, wv, wo, 2, key_lengths=lens, causal=causal), ref,
+               1e-12, "multihead brute force seed=%d" % seed)
+
+
+def check_multihead_uniform_keys(orc):
+    """W^K = 0 makes every score 0: each head's weights are uniform over the legal
+    keys, so the output is the mean of the legal rows of (X_kv W^V), times W^O."""
+    xq, xkv, wq, wk, wv, wo = _mh_rand(46, Lk=6)
+    lens = [6, 4]
+    got = orc.multihead(xq, xkv, wq, np.zeros_like(wk), wv, wo, 2, key_lengths=lens)
+    for b, lb in enumerate(lens):
+        mean_v = (xkv[b, :lb] @ wv).mean(axis=0)            # [h*d_v], heads concatenated
+        _close(got[b], np.tile(mean_v @ wo, (xq.shape[1], 1)), 1e-12, "uniform keys b=%d" % b)
+
+
+def check_multihead_head_order(orc):
+    """Renumbering the heads (the column blocks of W^Q, W^K, W^V and the row
+    blocks of W^O together) leaves MultiHead unchanged; swapping only W^O's
+    blocks changes it."""
+    xq, xkv, wq, wk, wv, wo = _mh_rand(47, h=3, dk=2, dv=3, dm=5)
+    base = orc.multihead(xq, xkv, wq, wk, wv, wo, 3, causal=True)
+    perm = [2, 0, 1]
+    cols = lambda w, d: np.concatenate([w[:, p * d:(p + 1) * d] for p in perm], axis=1)
+    rows = lambda w, d: np.concatenate([w[p * d:(p + 1) * d] for p in perm], axis=0)
+    got = orc.multihead(xq, xkv, cols(wq, 2), cols(wk, 2), cols(wv, 3), rows(wo, 3), 3, causal=True)
+    _close(got, base, 1e-12, "head renumbering")
+    other = orc.multihead(xq, xkv, wq, wk, wv, rows(wo, 3), 3, causal=True)
+    assert np.max(np.abs(other - base)) > 1e-3, "W^O blocks must follow their heads"
+
+
 ALL_CHECKS = [
     check_worked_example, check_worked_example_masked, check_toy_rows, check_toy_causal_row0,
     check_scale_dk64, check_uniform_prefix_means, check_special_cases,
@@ -356,4 +418,6 @@ ALL_CHECKS = [
     check_permutation, check_locality, check_rows_api,
     check_restricted_radius0, check_restricted_toy, check_restricted_bruteforce,
     check_restricted_locality,
+    check_multihead_identity_is_attention, check_multihead_bruteforce, check_multihead_uniform_keys,
+    check_multihead_head_order,
 ]

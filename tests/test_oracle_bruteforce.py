@@ -47,3 +47,23 @@ def test_exhaustive_tiny_restricted(Lq, Lk):
             got = oracle.attention(q, k, v, key_lengths=kl, causal=causal, radius=radius)
             ref = np.array(bruteforce.attention(q, k, v, kl, causal, radius))
             assert np.max(np.abs(got - ref)) <= 1e-12, (radius, causal, kl)
+
+
+@pytest.mark.parametrize("B,Lq,Lk,dm,h,dk,dv", [(1, 3, 3, 4, 2, 2, 2), (2, 4, 5, 6, 3, 2, 1),
+                                                 (1, 1, 4, 3, 1, 3, 3), (2, 5, 2, 4, 2, 1, 3)])
+def test_multihead_tiny(B, Lq, Lk, dm, h, dk, dv):
+    """Multi-head attention against the plain-loop brute force, self- and
+    cross-attention, every key length, with and without the causal mask."""
+    rng = np.random.default_rng(900 + 10 * Lq + Lk)
+    xq = rng.standard_normal((B, Lq, dm))
+    xkv = rng.standard_normal((B, Lk, dm))
+    ws = [rng.standard_normal(s) for s in ((dm, h * dk), (dm, h * dk), (dm, h * dv), (h * dv, dm))]
+    for causal in (False, True):
+        for ln in [None] + [[l] * B for l in range(0, Lk + 1)]:
+            got = oracle.multihead(xq, xkv, *ws, h, key_lengths=ln, causal=causal)
+            ref = np.array(bruteforce.multihead(xq, xkv, *ws, h, ln, causal))
+            assert np.max(np.abs(got - ref)) <= 1e-10 * max(1.0, np.abs(ref).max()), (causal, ln)
+    if Lq == Lk:
+        got = oracle.multihead(xq, xq, *ws, h, causal=True)
+        ref = np.array(bruteforce.multihead(xq, xq, *ws, h, None, True))
+        assert np.max(np.abs(got - ref)) <= 1e-10 * max(1.0, np.abs(ref).max())

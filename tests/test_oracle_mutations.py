@@ -45,6 +45,21 @@ MUTATIONS = {
     "band_upper_dropped": ("|| j > i + radius)", ")"),
     "band_lower_dropped": ("(j < i - radius || j > i + radius)", "(j > i + radius)"),
     "band_radius_doubled": ("j < i - radius || j > i + radius", "j < i - 2 * radius || j > i + 2 * radius"),
+    # multi-head projections (§3.2.2)
+    "mh_wq_transposed": ("acc += x[c] * Wq[c * (h * d_k) + hd * d_k + t];",
+                         "acc += x[c] * Wq[(hd * d_k + t) * d_model + c];"),
+    "mh_wk_head_offset_dropped": ("acc += x[c] * Wk[c * (h * d_k) + hd * d_k + t];",
+                                  "acc += x[c] * Wk[c * (h * d_k) + t];"),
+    "mh_wv_uses_wk": ("acc += x[c] * Wv[c * (h * d_v) + hd * d_v + t];",
+                      "acc += x[c] * Wk[c * (h * d_k) + hd * d_k + t];"),
+    "mh_keys_from_queries": ("const double *x = Xkv + r * d_model;",
+                             "const double *x = Xq + (r % (B * Lq)) * d_model;"),
+    "mh_wo_transposed": ("Wo[(hd * d_v + t) * d_model + c]", "Wo[c * (h * d_v) + hd * d_v + t]"),
+    "mh_concat_head_dropped": ("Wo[(hd * d_v + t) * d_model + c]", "Wo[t * d_model + c]"),
+    "mh_causal_dropped": ("rc = oracle_attention(Qp, Kp, Vp, key_lengths, causal, -1,",
+                          "rc = oracle_attention(Qp, Kp, Vp, key_lengths, 0, -1,"),
+    "mh_lengths_dropped": ("rc = oracle_attention(Qp, Kp, Vp, key_lengths, causal, -1,",
+                           "rc = oracle_attention(Qp, Kp, Vp, NULL, causal, -1,"),
 }
 
 

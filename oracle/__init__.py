@@ -105,8 +105,45 @@ class Oracle:
         lib.oracle_multihead.restype = ctypes.c_int
         lib.oracle_multihead.argtypes = [dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, i64, i64, i64,
                                          i64, i64, i64, i64, dp, ctypes.c_int]
+        lib.oracle_multihead_rows.restype = ctypes.c_int
+        lib.oracle_multihead_rows.argtypes = [dp, dp, dp, dp, dp, dp, ip, ctypes.c_int, i64, i64,
+                                              i64, i64, i64, i64, i64,
+                                              ctypes.POINTER(ctypes.c_int64), i64, dp,
+                                              ctypes.c_int]
         self.lib = lib
         self.path = path
+
+    def _mh_args(self, xq, xkv, wq, wk, wv, wo, h, key_lengths):
+        xq, xkv = _f64(xq), _f64(xkv)
+        wq, wk, wv, wo = _f64(wq), _f64(wk), _f64(wv), _f64(wo)
+        if xq.ndim != 3 or xkv.ndim != 3:
+            raise ValueError("xq and xkv must be [B, L, d_model]")
+        B, Lq, dm = xq.shape
+        Lk = xkv.shape[1]
+        if xkv.shape != (B, Lk, dm) or wq.shape[0] != dm or wq.shape[1] % h:
+            raise ValueError("inconsistent shapes")
+        dk = wq.shape[1] // h
+        dv = wv.shape[1] // h
+        if wk.shape != (dm, h * dk) or wv.shape != (dm, h * dv) or wo.shape != (h * dv, dm):
+            raise ValueError("inconsistent weight shapes")
+        return xq, xkv, wq, wk, wv, wo, _lengths(key_lengths, B), (B, Lq, Lk, dm, dk, dv)
+
+    def multihead_rows(self, xq, xkv, wq, wk, wv, wo, h, rows, key_lengths=None, causal=False,
+                       nthreads=0):
+        """Rows of multihead(): ``rows`` is an int array of (b, i) pairs.
+        Returns O_rows [n, d_model]."""
+        xq, xkv, wq, wk, wv, wo, kl, (B, Lq, Lk, dm, dk, dv) = self._mh_args(
+            xq, xkv, wq, wk, wv, wo, h, key_lengths)
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+        flat = np.ascontiguousarray(rows[:, 0] * Lq + rows[:, 1])
+        O = np.empty((rows.shape[0], dm), dtype=np.float64)
+        rc = self.lib.oracle_multihead_rows(_ptr(xq), _ptr(xkv), _ptr(wq), _ptr(wk), _ptr(wv),
+                                            _ptr(wo), _ptr(kl, ctypes.c_int32), int(bool(causal)),
+                                            B, Lq, Lk, dm, h, dk, dv, _ptr(flat, ctypes.c_int64),
+                                            len(flat), _ptr(O), int(nthreads))
+        if rc != 0:
+            raise RuntimeError("oracle_multihead_rows failed with code %d" % rc)
+        return O
 
     def multihead(self, xq, xkv, wq, wk, wv, wo, h, key_lengths=None, causal=False, nthreads=0):
         """MultiHead(Q, K, V) = Concat(head_1..head_h) W^O in fp64 (§3.2.2).
@@ -213,6 +250,12 @@ def attention(q, k, v, key_lengths=None, causal=False, return_weights=False, nth
 def multihead(xq, xkv, wq, wk, wv, wo, h, key_lengths=None, causal=False, nthreads=0):
     """fp64 multi-head attention; see Oracle.multihead."""
     return default().multihead(xq, xkv, wq, wk, wv, wo, h, key_lengths, causal, nthreads)
+
+
+def multihead_rows(xq, xkv, wq, wk, wv, wo, h, rows, key_lengths=None, causal=False, nthreads=0):
+    """fp64 multi-head attention for selected (b, i) rows; see Oracle.multihead_rows."""
+    return default().multihead_rows(xq, xkv, wq, wk, wv, wo, h, rows, key_lengths, causal,
+                                    nthreads)
 
 
 def attention_rows(q, k, v, rows, key_lengths=None, causal=False, nthreads=0, radius=None):

@@ -248,6 +248,27 @@ int oracle_attention_rows(const double *Q, const double *K, const double *V,
  *   component t of head i in the concatenation.
  * Returns 0 on success, 1 on a bad shape, 2 on allocation failure.
  */
+/* y[n] = sum_c x[c] * W[c][n] for one row x (W row-major [d_model][n_cols]):
+ * the product of a row with W_i for all heads i at once.  Loops over c, then
+ * n, so that W is read along its rows. */
+static void row_times(const double *x, const double *W, int64_t d_model, int64_t n_cols, double *y)
+{
+    for (int64_t n = 0; n < n_cols; ++n) y[n] = 0.0;
+    for (int64_t c = 0; c < d_model; ++c) {
+        const double xc = x[c];
+        const double *w = W + c * n_cols;
+        for (int64_t n = 0; n < n_cols; ++n) y[n] += xc * w[n];
+    }
+}
+
+/* Split a projected row y[h*d] into head-major storage P[b][h][L][d] at position i. */
+static void scatter_heads(const double *y, int64_t h, int64_t d, int64_t b, int64_t L, int64_t i,
+                          double *P)
+{
+    for (int64_t hd = 0; hd < h; ++hd)
+        for (int64_t t = 0; t < d; ++t) P[((b * h + hd) * L + i) * d + t] = y[hd * d + t];
+}
+
 int oracle_multihead(const double *Xq, const double *Xkv, const double *Wq, const double *Wk,
                      const double *Wv, const double *Wo, const int32_t *key_lengths, int causal,
                      int64_t B, int64_t Lq, int64_t Lk, int64_t d_model, int64_t h,
@@ -258,6 +279,7 @@ int oracle_multihead(const double *Xq, const double *Xkv, const double *Wq, cons
     if (nthreads < 1) nthreads = omp_get_max_threads();
 #endif
     const size_t nq = (size_t)(B * h * Lq), nk = (size_t)(B * h * Lk);
+    const int64_t wide = h * (d_k > d_v ? d_k : d_v);
     double *Qp = (double *)malloc((nq * d_k + 1) * sizeof(double));
     double *Kp = (double *)malloc((nk * d_k + 1) * sizeof(double));
     double *Vp = (double *)malloc((nk * d_v + 1) * sizeof(double));
@@ -270,34 +292,29 @@ int oracle_multihead(const double *Xq, const double *Xkv, const double *Wq, cons
 
     /* The h projections of each position: row x of the source sequence times
      * W_i (Q W_i^Q etc.), stored per head as [B][h][L][d]. */
-#pragma omp parallel for num_threads(nthreads) schedule(static)
-    for (int64_t r = 0; r < B * Lq; ++r) {
-        const int64_t b = r / Lq, i = r % Lq;
-        const double *x = Xq + r * d_model;
-        for (int64_t hd = 0; hd < h; ++hd)
-            for (int64_t t = 0; t < d_k; ++t) {
-                double acc = 0.0;
-                for (int64_t c = 0; c < d_model; ++c) acc += x[c] * Wq[c * (h * d_k) + hd * d_k + t];
-                Qp[((b * h + hd) * Lq + i) * d_k + t] = acc;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *y = (double *)malloc((size_t)(wide > d_model ? wide : d_model) * sizeof(double));
+        if (!y) {
+#pragma omp atomic write
+            rc = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < B * Lq; ++r) {
+                row_times(Xq + r * d_model, Wq, d_model, h * d_k, y);
+                scatter_heads(y, h, d_k, r / Lq, Lq, r % Lq, Qp);
             }
-    }
-#pragma omp parallel for num_threads(nthreads) schedule(static)
-    for (int64_t r = 0; r < B * Lk; ++r) {
-        const int64_t b = r / Lk, j = r % Lk;
-        const double *x = Xkv + r * d_model;
-        for (int64_t hd = 0; hd < h; ++hd) {
-            for (int64_t t = 0; t < d_k; ++t) {
-                double acc = 0.0;
-                for (int64_t c = 0; c < d_model; ++c) acc += x[c] * Wk[c * (h * d_k) + hd * d_k + t];
-                Kp[((b * h + hd) * Lk + j) * d_k + t] = acc;
-            }
-            for (int64_t t = 0; t < d_v; ++t) {
-                double acc = 0.0;
-                for (int64_t c = 0; c < d_model; ++c) acc += x[c] * Wv[c * (h * d_v) + hd * d_v + t];
-                Vp[((b * h + hd) * Lk + j) * d_v + t] = acc;
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < B * Lk; ++r) {
+                row_times(Xkv + r * d_model, Wk, d_model, h * d_k, y);
+                scatter_heads(y, h, d_k, r / Lk, Lk, r % Lk, Kp);
+                row_times(Xkv + r * d_model, Wv, d_model, h * d_v, y);
+                scatter_heads(y, h, d_v, r / Lk, Lk, r % Lk, Vp);
             }
         }
+        free(y);
     }
+    if (rc != 0) goto done;
 
     /* head_i for every head (the attention of §3.2.1 on the projections) */
     rc = oracle_attention(Qp, Kp, Vp, key_lengths, causal, -1, B, h, Lq, Lk, d_k, d_v, A, NULL,
@@ -306,16 +323,23 @@ int oracle_multihead(const double *Xq, const double *Xkv, const double *Wq, cons
 
     /* Concat(head_1, ..., head_h) W^O: component t of head i is column
      * i*d_v + t of the concatenation. */
-#pragma omp parallel for num_threads(nthreads) schedule(static)
-    for (int64_t r = 0; r < B * Lq; ++r) {
-        const int64_t b = r / Lq, i = r % Lq;
-        for (int64_t c = 0; c < d_model; ++c) {
-            double acc = 0.0;
-            for (int64_t hd = 0; hd < h; ++hd)
-                for (int64_t t = 0; t < d_v; ++t)
-                    acc += A[((b * h + hd) * Lq + i) * d_v + t] * Wo[(hd * d_v + t) * d_model + c];
-            O[r * d_model + c] = acc;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *cat = (double *)malloc((size_t)(h * d_v) * sizeof(double));
+        if (!cat) {
+#pragma omp atomic write
+            rc = 2;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < B * Lq; ++r) {
+                const int64_t b = r / Lq, i = r % Lq;
+                for (int64_t hd = 0; hd < h; ++hd)
+                    for (int64_t t = 0; t < d_v; ++t)
+                        cat[hd * d_v + t] = A[((b * h + hd) * Lq + i) * d_v + t];
+                row_times(cat, Wo, h * d_v, d_model, O + r * d_model);
+            }
         }
+        free(cat);
     }
 
 done:
@@ -323,5 +347,89 @@ done:
     free(Kp);
     free(Vp);
     free(A);
+    return rc;
+}
+
+/*
+ * oracle_multihead for chosen output rows only: rows[n] = b * Lq + i.  The keys
+ * and values of every batch entry involved are projected in full (a row may
+ * use any of them); queries only for the chosen rows.  O_rows [nrows][d_model].
+ */
+int oracle_multihead_rows(const double *Xq, const double *Xkv, const double *Wq,
+                          const double *Wk, const double *Wv, const double *Wo,
+                          const int32_t *key_lengths, int causal, int64_t B, int64_t Lq,
+                          int64_t Lk, int64_t d_model, int64_t h, int64_t d_k, int64_t d_v,
+                          const int64_t *rows, int64_t nrows, double *O_rows, int nthreads)
+{
+    if (B < 0 || Lq < 0 || Lk < 0 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1) return 1;
+    for (int64_t n = 0; n < nrows; ++n)
+        if (rows[n] < 0 || rows[n] >= B * Lq) return 1;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#endif
+    const int64_t wide = h * (d_k > d_v ? d_k : d_v);
+    const size_t hk = (size_t)(h * Lk);
+    double *Kp = (double *)malloc((hk * d_k + 1) * sizeof(double));
+    double *Vp = (double *)malloc((hk * d_v + 1) * sizeof(double));
+    int rc = 0;
+    if (!Kp || !Vp) {
+        rc = 2;
+        goto out;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        int used = 0;
+        for (int64_t n = 0; n < nrows; ++n) used |= rows[n] / Lq == b;
+        if (!used) continue;
+        /* keys and values of batch entry b, as [1][h][Lk][d] */
+#pragma omp parallel num_threads(nthreads)
+        {
+            double *y = (double *)malloc((size_t)wide * sizeof(double));
+            if (!y) {
+#pragma omp atomic write
+                rc = 2;
+            } else {
+#pragma omp for schedule(static)
+                for (int64_t j = 0; j < Lk; ++j) {
+                    row_times(Xkv + (b * Lk + j) * d_model, Wk, d_model, h * d_k, y);
+                    scatter_heads(y, h, d_k, 0, Lk, j, Kp);
+                    row_times(Xkv + (b * Lk + j) * d_model, Wv, d_model, h * d_v, y);
+                    scatter_heads(y, h, d_v, 0, Lk, j, Vp);
+                }
+            }
+            free(y);
+        }
+        if (rc != 0) goto out;
+        const int64_t len = clamp_len(key_lengths, b, Lk);
+#pragma omp parallel num_threads(nthreads)
+        {
+            double *q = (double *)malloc((size_t)(h * d_k + 1) * sizeof(double));
+            double *cat = (double *)malloc((size_t)(h * d_v + 1) * sizeof(double));
+            double *sc = (double *)malloc((size_t)(Lk + 1) * sizeof(double));
+            double *w = (double *)malloc((size_t)(Lk + 1) * sizeof(double));
+            if (!q || !cat || !sc || !w) {
+#pragma omp atomic write
+                rc = 2;
+            } else {
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t n = 0; n < nrows; ++n) {
+                    if (rows[n] / Lq != b) continue;
+                    const int64_t i = rows[n] % Lq;
+                    row_times(Xq + rows[n] * d_model, Wq, d_model, h * d_k, q);
+                    for (int64_t hd = 0; hd < h; ++hd)
+                        attention_row(q + hd * d_k, Kp + hd * Lk * d_k, Vp + hd * Lk * d_v, Lk, d_k,
+                                      d_v, len, causal, -1, i, sc, w, cat + hd * d_v, NULL, NULL);
+                    row_times(cat, Wo, h * d_v, d_model, O_rows + n * d_model);
+                }
+            }
+            free(q);
+            free(cat);
+            free(sc);
+            free(w);
+        }
+        if (rc != 0) goto out;
+    }
+out:
+    free(Kp);
+    free(Vp);
     return rc;
 }

@@ -411,6 +411,20 @@ def check_multihead_head_order(orc):
     assert np.max(np.abs(other - base)) > 1e-3, "W^O blocks must follow their heads"
 
 
+def check_multihead_rows_api(orc):
+    """multihead_rows gives the full call's rows; batch entries are independent."""
+    xq, xkv, wq, wk, wv, wo = _mh_rand(48, Lq=6, Lk=6)
+    xkv = xq
+    lens = [6, 3]
+    full = orc.multihead(xq, xkv, wq, wk, wv, wo, 2, key_lengths=lens, causal=True)
+    rows = [(0, 0), (1, 5), (1, 2), (0, 4), (1, 0)]
+    got = orc.multihead_rows(xq, xkv, wq, wk, wv, wo, 2, rows, key_lengths=lens, causal=True)
+    for n, (b, i) in enumerate(rows):
+        _close(got[n], full[b, i], 1e-12, "multihead row (%d,%d)" % (b, i))
+    ref = np.array(bruteforce.multihead(xq, xkv, wq, wk, wv, wo, 2, lens, True))
+    _close(got, ref[[r[0] for r in rows], [r[1] for r in rows]], 1e-12, "rows vs brute force")
+
+
 ALL_CHECKS = [
     check_worked_example, check_worked_example_masked, check_toy_rows, check_toy_causal_row0,
     check_scale_dk64, check_uniform_prefix_means, check_special_cases,
@@ -419,5 +433,5 @@ ALL_CHECKS = [
     check_restricted_radius0, check_restricted_toy, check_restricted_bruteforce,
     check_restricted_locality,
     check_multihead_identity_is_attention, check_multihead_bruteforce, check_multihead_uniform_keys,
-    check_multihead_head_order,
+    check_multihead_head_order, check_multihead_rows_api,
 ]

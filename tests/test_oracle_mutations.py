@@ -46,20 +46,27 @@ MUTATIONS = {
     "band_lower_dropped": ("(j < i - radius || j > i + radius)", "(j > i + radius)"),
     "band_radius_doubled": ("j < i - radius || j > i + radius", "j < i - 2 * radius || j > i + 2 * radius"),
     # multi-head projections (§3.2.2)
-    "mh_wq_transposed": ("acc += x[c] * Wq[c * (h * d_k) + hd * d_k + t];",
-                         "acc += x[c] * Wq[(hd * d_k + t) * d_model + c];"),
-    "mh_wk_head_offset_dropped": ("acc += x[c] * Wk[c * (h * d_k) + hd * d_k + t];",
-                                  "acc += x[c] * Wk[c * (h * d_k) + t];"),
-    "mh_wv_uses_wk": ("acc += x[c] * Wv[c * (h * d_v) + hd * d_v + t];",
-                      "acc += x[c] * Wk[c * (h * d_k) + hd * d_k + t];"),
-    "mh_keys_from_queries": ("const double *x = Xkv + r * d_model;",
-                             "const double *x = Xq + (r % (B * Lq)) * d_model;"),
-    "mh_wo_transposed": ("Wo[(hd * d_v + t) * d_model + c]", "Wo[c * (h * d_v) + hd * d_v + t]"),
-    "mh_concat_head_dropped": ("Wo[(hd * d_v + t) * d_model + c]", "Wo[t * d_model + c]"),
+    "mh_wq_uses_wk": ("row_times(Xq + r * d_model, Wq, d_model, h * d_k, y);",
+                      "row_times(Xq + r * d_model, Wk, d_model, h * d_k, y);"),
+    "mh_wv_uses_wk": ("row_times(Xkv + r * d_model, Wv, d_model, h * d_v, y);",
+                      "row_times(Xkv + r * d_model, Wk, d_model, h * d_v, y);"),
+    "mh_keys_from_queries": ("row_times(Xkv + r * d_model, Wk, d_model, h * d_k, y);",
+                             "row_times(Xq + (r % (B * Lq)) * d_model, Wk, d_model, h * d_k, y);"),
+    "mh_projection_transposed": ("y[n] += xc * w[n];", "y[n] += xc * W[n * d_model + c];"),
+    "mh_head_split_offset_dropped": ("P[((b * h + hd) * L + i) * d + t] = y[hd * d + t];",
+                                     "P[((b * h + hd) * L + i) * d + t] = y[t];"),
+    "mh_concat_head_dropped": ("cat[hd * d_v + t] = A[((b * h + hd) * Lq + i) * d_v + t];",
+                               "cat[hd * d_v + t] = A[((b * h) * Lq + i) * d_v + t];"),
+    "mh_wo_uses_wv": ("row_times(cat, Wo, h * d_v, d_model, O + r * d_model);",
+                      "row_times(cat, Wv, h * d_v, d_model, O + r * d_model);"),
     "mh_causal_dropped": ("rc = oracle_attention(Qp, Kp, Vp, key_lengths, causal, -1,",
                           "rc = oracle_attention(Qp, Kp, Vp, key_lengths, 0, -1,"),
     "mh_lengths_dropped": ("rc = oracle_attention(Qp, Kp, Vp, key_lengths, causal, -1,",
                            "rc = oracle_attention(Qp, Kp, Vp, NULL, causal, -1,"),
+    "mh_rows_causal_dropped": ("d_v, len, causal, -1, i, sc, w, cat + hd * d_v, NULL, NULL);",
+                               "d_v, len, 0, -1, i, sc, w, cat + hd * d_v, NULL, NULL);"),
+    "mh_rows_head_offset": ("attention_row(q + hd * d_k, Kp + hd * Lk * d_k,",
+                            "attention_row(q, Kp + hd * Lk * d_k,"),
 }
 
 

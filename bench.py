@@ -122,6 +122,35 @@ def cpu_baseline(x, target_seconds=15.0):
                           radius=c.radius), dt)}
 
 
+def cpu_baseline_multihead(x, target_seconds=15.0):
+    """The fp64 oracle's MultiHead, as it is, on the first B' batch entries of the
+    workload (B' sized for about target_seconds), FLOPs counted like the GPU's."""
+    import oracle
+
+    c = x.config
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    oracle.default()
+
+    def run(nb):
+        kl = None if x.key_lengths is None else x.key_lengths[:nb]
+        args = [np.ascontiguousarray(a[:nb], dtype=np.float64) for a in (x.xq, x.xkv)]
+        t0 = time.perf_counter()
+        oracle.multihead(args[0], args[1], x.wq, x.wk, x.wv, x.wo, c.H, key_lengths=kl,
+                         causal=c.causal, nthreads=threads)
+        return time.perf_counter() - t0, perfmodel.multihead_flops(
+            nb, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v, c.causal, kl)
+
+    dt, f = run(1)
+    nb = int(max(1, min(c.B, round(target_seconds / max(dt, 1e-3)))))
+    if nb > 1:
+        dt, f = run(nb)
+    total = perfmodel.multihead_flops(c.B, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v, c.causal,
+                                      x.key_lengths)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "the first %d of %d batch entries (%.3g of the workload's FLOPs, %.1f s), "
+                      "fp64 C oracle with OpenMP" % (nb, c.B, f / total, dt)}
+
+
 def copy_calibration(torch, dev, args):
     """A plain copy of known size: reads and writes args.copy_mib MiB per launch."""
     n = args.copy_mib << 20
@@ -180,10 +209,16 @@ def main():
     x = workloads.generate(args.config)
     c = x.config
     tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
-    flops = perfmodel.flops(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
-                            radius=c.radius)
-    nbytes = perfmodel.min_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
-                                 elem=2 if c.dtype == "bf16" else 4, radius=c.radius)
+    if c.entry == "multihead":
+        flops = perfmodel.multihead_flops(c.B, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v, c.causal,
+                                          x.key_lengths)
+        nbytes = perfmodel.multihead_min_bytes(c.B, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v,
+                                               c.self_attention)
+    else:
+        flops = perfmodel.flops(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
+                                radius=c.radius)
+        nbytes = perfmodel.min_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
+                                     elem=2 if c.dtype == "bf16" else 4, radius=c.radius)
     hbm_bound = flops / nbytes < (PEAK_TFLOPS[c.dtype] * 1e12) / (PEAK_HBM_GBS * 1e9)
 
     rotate = args.rotate
@@ -191,25 +226,45 @@ def main():
         # HBM-bound workloads cycle through copies totalling >= 1 GiB so that the
         # 256 MB Infinity Cache cannot hold the inputs between launches.
         rotate = min(64, max(1, -(-(1 << 30) // nbytes))) if (hbm_bound and nbytes >= (1 << 20)) else 1
+    if c.entry == "multihead":
+        rotate = 1          # one weight set and one input set (a matrix-core-bound step)
 
     def up(a):
         return torch.from_numpy(a).to(tdt).to(dev)
 
-    base = (up(x.q), up(x.k), up(x.v))
     kl = None if x.key_lengths is None else torch.as_tensor(x.key_lengths).to(dev)
     sets = []
-    for r in range(rotate):
-        qkv = base if r == 0 else tuple(t.clone() for t in base)
-        sets.append((qkv, torch.empty((c.B, c.H, c.Lq, c.d_v), dtype=tdt, device=dev)))
+    if c.entry == "multihead":
+        xq_d = up(x.xq)
+        mh = (xq_d, xq_d if c.self_attention else up(x.xkv), up(x.wq), up(x.wk), up(x.wv),
+              up(x.wo))
+        sets.append((mh, torch.empty((c.B, c.Lq, c.d_model), dtype=tdt, device=dev)))
+    else:
+        base = (up(x.q), up(x.k), up(x.v))
+        for r in range(rotate):
+            qkv = base if r == 0 else tuple(t.clone() for t in base)
+            sets.append((qkv, torch.empty((c.B, c.H, c.Lq, c.d_v), dtype=tdt, device=dev)))
 
     # Validate the binding once, then time pre-marshalled C-ABI calls so that the
     # host cost per step stays far below the kernel time.
-    (q0, k0, v0), o0 = sets[0]
     stream = torch.cuda.current_stream(dev)
     lib = sdpa.load_library()
     dcode = sdpa.SDPA_BF16 if c.dtype == "bf16" else sdpa.SDPA_F32
     klp = None if kl is None else kl.data_ptr()
-    if c.entry == "decode":
+    if c.entry == "multihead":
+        (xq_d, xkv_d, wq_d, wk_d, wv_d, wo_d), o0 = sets[0]
+        ws_bytes = sdpa.sdpa_multihead_workspace_bytes(c.B, c.Lq, c.Lk, c.d_model, c.H, c.d_k,
+                                                       c.d_v, dcode)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        sdpa.multihead(xq_d, xkv_d, wq_d, wk_d, wv_d, wo_d, c.H, key_lengths=kl, causal=c.causal,
+                       out=o0, workspace=ws)
+        calls = [(xq_d.data_ptr(), xkv_d.data_ptr(), wq_d.data_ptr(), wk_d.data_ptr(),
+                  wv_d.data_ptr(), wo_d.data_ptr(), klp, int(c.causal), o0.data_ptr(), c.B, c.Lq,
+                  c.Lk, c.d_model, c.H, c.d_k, c.d_v, dcode, ws.data_ptr(), ws_bytes,
+                  stream.cuda_stream)]
+        fn, fn_name = lib.sdpa_multihead_forward, "sdpa_multihead_forward"
+    elif c.entry == "decode":
+        (q0, k0, v0), o0 = sets[0]
         ws_bytes = sdpa.sdpa_decode_workspace_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dcode)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         sdpa.decode(q0, k0, v0, key_lengths=kl, out=o0, workspace=ws)
@@ -218,12 +273,14 @@ def main():
                  for (q, k, v), o in sets]
         fn, fn_name = lib.sdpa_decode, "sdpa_decode"
     elif c.entry == "restricted":
+        (q0, k0, v0), o0 = sets[0]
         sdpa.restricted(q0, k0, v0, c.radius, key_lengths=kl, causal=c.causal, out=o0)
         calls = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), klp, int(c.causal), c.radius,
                   o.data_ptr(), c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dcode, stream.cuda_stream)
                  for (q, k, v), o in sets]
         fn, fn_name = lib.sdpa_forward_restricted, "sdpa_forward_restricted"
     else:
+        (q0, k0, v0), o0 = sets[0]
         sdpa.forward(q0, k0, v0, key_lengths=kl, causal=c.causal, out=o0)
         calls = [(q.data_ptr(), k.data_ptr(), v.data_ptr(), klp, int(c.causal), o.data_ptr(),
                   c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dcode, stream.cuda_stream)
@@ -249,7 +306,7 @@ def main():
             settle_steps += 1
         torch.cuda.synchronize()
 
-    use_graph = args.graph == "on" or (args.graph == "auto" and c.entry == "decode")
+    use_graph = args.graph == "on" or (args.graph == "auto" and c.entry in ("decode", "multihead"))
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     if use_graph:
@@ -315,6 +372,9 @@ def main():
                 "traffic": traffic}
     if c.entry == "decode":
         roof["kernel"] = "sdpa_split_mfma_d64_kernel + sdpa_split_merge_d64_kernel"
+    elif c.entry == "multihead":
+        roof["kernel"] = ("whole step: projection GEMMs (proj_gemm_kernel) + attention "
+                          "(sdpa_fwd_mfma_kernel); per-kernel split in the rocprofv3 summary")
     elif c.entry == "restricted":
         roof["kernel"] = ("sdpa_fwd_mfma_band_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
                                                            c.d_k in (32, 64, 128)) else "sdpa_fwd_generic_kernel")
@@ -327,7 +387,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(x)
+        cpu = cpu_baseline_multihead(x) if c.entry == "multihead" else cpu_baseline(x)
 
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
@@ -341,7 +401,9 @@ def main():
                    "Lq": c.Lq, "Lk": c.Lk, "d_k": c.d_k, "d_v": c.d_v, "causal": c.causal,
                    "key_lengths": None if x.key_lengths is None else "U{%d..%d} seed %d" % (
                        c.key_len_range[0], c.key_len_range[1], c.seed),
-                   "radius": c.radius, "input_sets": rotate},
+                   "radius": c.radius, "d_model": c.d_model,
+                   "self_attention": c.self_attention if c.entry == "multihead" else None,
+                   "input_sets": rotate},
         "frac_of_peak": value / PEAK_TFLOPS[c.dtype],
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -22,11 +22,14 @@ from ._binding import (  # noqa: F401
     decode,
     forward,
     load_library,
+    multihead,
     sdpa_decode,
     sdpa_decode_workspace_bytes,
     restricted,
     sdpa_forward,
     sdpa_forward_restricted,
     sdpa_last_hip_error,
+    sdpa_multihead_forward,
+    sdpa_multihead_workspace_bytes,
     sdpa_status_str,
 )

@@ -25,7 +25,8 @@ SDPA_BF16 = 1
 
 #: Symbols include/sdpa.h declares.
 EXPORTED = ("sdpa_decode", "sdpa_decode_workspace_bytes", "sdpa_forward",
-            "sdpa_forward_restricted", "sdpa_last_hip_error", "sdpa_status_str")
+            "sdpa_forward_restricted", "sdpa_last_hip_error", "sdpa_multihead_forward",
+            "sdpa_multihead_workspace_bytes", "sdpa_status_str")
 
 _lib = None
 
@@ -54,6 +55,11 @@ def load_library(path: str = LIBRARY):
     lib.sdpa_forward_restricted.restype = ctypes.c_int
     lib.sdpa_forward_restricted.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, vp, i64, i64, i64,
                                             i64, i64, i64, ctypes.c_int, vp]
+    lib.sdpa_multihead_forward.restype = ctypes.c_int
+    lib.sdpa_multihead_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, i64, i64,
+                                           i64, i64, i64, i64, i64, ctypes.c_int, vp, i64, vp]
+    lib.sdpa_multihead_workspace_bytes.restype = i64
+    lib.sdpa_multihead_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.sdpa_decode.restype = ctypes.c_int
     lib.sdpa_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                 vp, i64, vp]
@@ -84,6 +90,23 @@ def sdpa_forward_restricted(Q: int, K: int, V: int, key_lengths: int, causal: in
                                                   key_lengths or None, int(causal), int(radius),
                                                   out or None, B, H, Lq, Lk, d_k, d_v, int(dtype),
                                                   stream or None)
+
+
+def sdpa_multihead_forward(Xq: int, Xkv: int, Wq: int, Wk: int, Wv: int, Wo: int,
+                           key_lengths: int, causal: int, out: int, B: int, Lq: int, Lk: int,
+                           d_model: int, h: int, d_k: int, d_v: int, dtype: int, workspace: int,
+                           workspace_bytes: int, stream: int) -> int:
+    """Raw C call; pointers and the stream are integers (0 = NULL).  Returns the status."""
+    return load_library().sdpa_multihead_forward(
+        Xq or None, Xkv or None, Wq or None, Wk or None, Wv or None, Wo or None,
+        key_lengths or None, int(causal), out or None, B, Lq, Lk, d_model, h, d_k, d_v,
+        int(dtype), workspace or None, workspace_bytes, stream or None)
+
+
+def sdpa_multihead_workspace_bytes(B: int, Lq: int, Lk: int, d_model: int, h: int, d_k: int,
+                                   d_v: int, dtype: int) -> int:
+    return load_library().sdpa_multihead_workspace_bytes(B, Lq, Lk, d_model, h, d_k, d_v,
+                                                         int(dtype))
 
 
 def sdpa_decode(Q: int, K: int, V: int, key_lengths: int, out: int, B: int, H: int, Lq: int,
@@ -193,6 +216,62 @@ def restricted(q, k, v, radius: int, key_lengths=None, causal: bool = False, out
                                      int(bool(causal)), int(radius), out.data_ptr(), B, H, Lq, Lk,
                                      d_k, d_v, dtype, stream)
     _raise(st, "sdpa_forward_restricted")
+    return out
+
+
+def multihead(xq, xkv, wq, wk, wv, wo, h: int, key_lengths=None, causal: bool = False, out=None,
+              workspace=None):
+    """MultiHead(Q, K, V) = Concat(head_1..head_h) W^O (sdpa_multihead_forward).
+
+    xq [B, Lq, d_model], xkv [B, Lk, d_model] (pass xq itself for
+    self-attention), wq and wk [d_model, h*d_k], wv [d_model, h*d_v],
+    wo [h*d_v, d_model]: contiguous torch.bfloat16 tensors on one GPU.
+    key_lengths, causal as for forward().  workspace: optional uint8 tensor of
+    at least sdpa_multihead_workspace_bytes(...) bytes (allocated here if None).
+    Returns out [B, Lq, d_model].
+    """
+    import torch
+
+    if xq.dim() != 3 or xkv.dim() != 3:
+        raise ValueError("xq and xkv must be [B, L, d_model]")
+    B, Lq, dm = xq.shape
+    Lk = xkv.shape[1]
+    if tuple(xkv.shape) != (B, Lk, dm) or wq.dim() != 2 or wq.shape[0] != dm or wq.shape[1] % h:
+        raise ValueError("inconsistent shapes")
+    dk, dv = wq.shape[1] // h, wv.shape[1] // h
+    if tuple(wk.shape) != (dm, h * dk) or tuple(wv.shape) != (dm, h * dv) or \
+            tuple(wo.shape) != (h * dv, dm):
+        raise ValueError("inconsistent weight shapes")
+    dev = xq.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for name, t in (("xq", xq), ("xkv", xkv), ("wq", wq), ("wk", wk), ("wv", wv), ("wo", wo)):
+        if t.dtype != torch.bfloat16 or t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bfloat16 tensor on xq's device" % name)
+    if key_lengths is not None and not isinstance(key_lengths, torch.Tensor):
+        key_lengths = torch.as_tensor(list(key_lengths), dtype=torch.int32, device=dev)
+    if key_lengths is not None and (key_lengths.dtype != torch.int32 or key_lengths.device != dev
+                                    or tuple(key_lengths.shape) != (B,)):
+        raise ValueError("key_lengths must be an int32 [B] tensor on xq's device")
+    if out is None:
+        out = torch.empty((B, Lq, dm), dtype=torch.bfloat16, device=dev)
+    elif tuple(out.shape) != (B, Lq, dm) or out.dtype != torch.bfloat16 or out.device != dev or \
+            not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [B, Lq, d_model] tensor")
+    need = sdpa_multihead_workspace_bytes(B, Lq, Lk, dm, h, dk, dv, SDPA_BF16)
+    if need < 0:
+        raise SdpaError(SDPA_ERR_UNSUPPORTED, "sizes rejected", "sdpa_multihead_forward")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = sdpa_multihead_forward(xq.data_ptr(), xkv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                                    wv.data_ptr(), wo.data_ptr(),
+                                    0 if key_lengths is None else key_lengths.data_ptr(),
+                                    int(bool(causal)), out.data_ptr(), B, Lq, Lk, dm, h, dk, dv,
+                                    SDPA_BF16, workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), stream)
+    _raise(st, "sdpa_multihead_forward")
     return out
 
 

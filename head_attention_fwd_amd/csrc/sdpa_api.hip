@@ -147,6 +147,68 @@ int64_t split_workspace_bytes(int64_t n_bh, int64_t Lq, const SplitPlan &sp)
     return 4 * (64 + 2) * n_bh * sp.n_split * Lq;
 }
 
+// ---- multi-head attention: projections around the attention (§3.2.2)
+
+// Largest buffer a projection product addresses (32-bit offsets, with room for
+// the out-of-range marker).
+constexpr int64_t kMaxGemmBytes = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+
+struct MhPlan {
+    int64_t q_bytes, k_bytes, v_bytes, a_bytes;   // head-major Q, K, V, attention output
+    int64_t q_off, k_off, v_off, a_off, total;    // workspace offsets (256-byte aligned)
+    int64_t x_q_bytes, x_kv_bytes, out_bytes, wq_bytes, wk_bytes, wv_bytes, wo_bytes;
+};
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+sdpa_status mh_plan(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model, int64_t h, int64_t d_k,
+                    int64_t d_v, sdpa_dtype dtype, MhPlan &p)
+{
+    if (B < 0 || Lq < 0 || Lk < 0 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1)
+        return SDPA_ERR_BAD_SHAPE;
+    if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
+    if (d_k > kMaxHeadDim || d_v > kMaxHeadDim || d_model % 32 != 0 || d_k % 8 != 0 ||
+        d_v % 32 != 0)
+        return SDPA_ERR_UNSUPPORTED;
+    if (B > kMaxDim || Lq > kMaxDim || Lk > kMaxDim || d_model > kMaxDim || h > kMaxDim)
+        return SDPA_ERR_BAD_SHAPE;
+    const sdpa_status st = check_sizes(B, h, Lq, Lk, d_k, d_v, dtype);
+    if (st != SDPA_OK) return st;
+    bool ok = mul_ok(p.q_bytes, {B, h, Lq, d_k, 2}) && mul_ok(p.k_bytes, {B, h, Lk, d_k, 2}) &&
+              mul_ok(p.v_bytes, {B, h, Lk, d_v, 2}) && mul_ok(p.a_bytes, {B, h, Lq, d_v, 2}) &&
+              mul_ok(p.x_q_bytes, {B, Lq, d_model, 2}) && mul_ok(p.x_kv_bytes, {B, Lk, d_model, 2}) &&
+              mul_ok(p.wq_bytes, {d_model, h, d_k, 2}) && mul_ok(p.wv_bytes, {d_model, h, d_v, 2});
+    if (!ok) return SDPA_ERR_BAD_SHAPE;
+    p.out_bytes = p.x_q_bytes;
+    p.wk_bytes = p.wq_bytes;
+    p.wo_bytes = p.wv_bytes;
+    for (int64_t n : {p.q_bytes, p.k_bytes, p.v_bytes, p.a_bytes, p.x_q_bytes, p.x_kv_bytes,
+                      p.wq_bytes, p.wv_bytes})
+        if (n > kMaxGemmBytes) return SDPA_ERR_BAD_SHAPE;
+    p.q_off = 0;
+    p.k_off = align256(p.q_off + p.q_bytes);
+    p.v_off = align256(p.k_off + p.k_bytes);
+    p.a_off = align256(p.v_off + p.v_bytes);
+    p.total = align256(p.a_off + p.a_bytes);
+    // projection grids: ceil(B*L / 128) row tiles times at most 3 * ceil(h*d / 128) column tiles
+    const int64_t mt = (B * (Lq > Lk ? Lq : Lk) + 127) / 128;
+    const int64_t nt = 3 * ((h * (d_k > d_v ? d_k : d_v) + 127) / 128) + (d_model + 127) / 128;
+    if (mt > 0 && nt > kMaxWorkgroups / mt) return SDPA_ERR_BAD_SHAPE;
+    return SDPA_OK;
+}
+
+sdpa::GemmSegment segment(const void *W, void *C, int64_t N, int64_t d, int64_t c_elems)
+{
+    sdpa::GemmSegment sg;
+    sg.W = W;
+    sg.C = C;
+    sg.N = N;
+    sg.d = d;
+    sg.c_elems = c_elems;
+    sg.n_tiles = (int)((N + 127) / 128);
+    return sg;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,6 +239,97 @@ sdpa_status sdpa_forward(const void *Q, const void *K, const void *V,
     if (st != SDPA_OK || z.empty) return st;
     return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dtype,
                            (hipStream_t)stream);
+}
+
+int64_t sdpa_multihead_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model,
+                                       int64_t h, int64_t d_k, int64_t d_v, sdpa_dtype dtype)
+{
+    MhPlan p;
+    if (mh_plan(B, Lq, Lk, d_model, h, d_k, d_v, dtype, p) != SDPA_OK) return -1;
+    return p.total;
+}
+
+sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *Wq, const void *Wk,
+                                   const void *Wv, const void *Wo, const int32_t *key_lengths,
+                                   int causal, void *out, int64_t B, int64_t Lq, int64_t Lk,
+                                   int64_t d_model, int64_t h, int64_t d_k, int64_t d_v,
+                                   sdpa_dtype dtype, void *workspace, int64_t workspace_bytes,
+                                   void *stream)
+{
+    MhPlan p;
+    const sdpa_status st = mh_plan(B, Lq, Lk, d_model, h, d_k, d_v, dtype, p);
+    if (st != SDPA_OK) return st;
+    if (B == 0 || Lq == 0) return SDPA_OK;   // empty output
+    if (!Xq || !Wq || !Wk || !Wv || !Wo || !out || (Lk > 0 && !Xkv)) return SDPA_ERR_NULL_POINTER;
+    if (overlaps(out, p.out_bytes, Xq, p.x_q_bytes) || overlaps(out, p.out_bytes, Xkv, p.x_kv_bytes) ||
+        overlaps(out, p.out_bytes, Wq, p.wq_bytes) || overlaps(out, p.out_bytes, Wk, p.wk_bytes) ||
+        overlaps(out, p.out_bytes, Wv, p.wv_bytes) || overlaps(out, p.out_bytes, Wo, p.wo_bytes) ||
+        overlaps(out, p.out_bytes, key_lengths, 4 * B))
+        return SDPA_ERR_ALIAS;
+    if (!workspace || workspace_bytes < p.total) return SDPA_ERR_WORKSPACE;
+    if (overlaps(workspace, p.total, Xq, p.x_q_bytes) || overlaps(workspace, p.total, Xkv, p.x_kv_bytes) ||
+        overlaps(workspace, p.total, Wq, p.wq_bytes) || overlaps(workspace, p.total, Wk, p.wk_bytes) ||
+        overlaps(workspace, p.total, Wv, p.wv_bytes) || overlaps(workspace, p.total, Wo, p.wo_bytes) ||
+        overlaps(workspace, p.total, out, p.out_bytes) ||
+        overlaps(workspace, p.total, key_lengths, 4 * B))
+        return SDPA_ERR_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    void *Qh = ws + p.q_off, *Kh = ws + p.k_off, *Vh = ws + p.v_off, *Ah = ws + p.a_off;
+
+    // 1. Q W_i^Q, K W_i^K, V W_i^V for every head, into [B, h, L, d]; one launch
+    //    when queries, keys and values come from the same sequence.
+    sdpa::GemmShape sq{};
+    sq.K = d_model;
+    sq.M = B * Lq;
+    sq.n_mtiles = (uint32_t)((sq.M + 127) / 128);
+    sq.Lc = Lq;
+    sq.Hc = h;
+    sdpa::GemmSegments gq{};
+    gq.seg[0] = segment(Wq, Qh, h * d_k, d_k, p.q_bytes / 2);
+    gq.count = 1;
+    const bool self_attn = Xkv == Xq && Lk == Lq;
+    if (self_attn) {
+        gq.seg[1] = segment(Wk, Kh, h * d_k, d_k, p.k_bytes / 2);
+        gq.seg[2] = segment(Wv, Vh, h * d_v, d_v, p.v_bytes / 2);
+        gq.count = 3;
+    }
+    for (int i = 0; i < gq.count; ++i) gq.n_ntiles += (uint32_t)gq.seg[i].n_tiles;
+    sdpa_status r = hip_status(sdpa::launch_proj_gemm(Xq, 0, sq, gq, 1, s));
+    if (r != SDPA_OK) return r;
+    if (!self_attn && Lk > 0) {
+        sdpa::GemmShape sk = sq;
+        sk.M = B * Lk;
+        sk.n_mtiles = (uint32_t)((sk.M + 127) / 128);
+        sk.Lc = Lk;
+        sdpa::GemmSegments gk{};
+        gk.seg[0] = segment(Wk, Kh, h * d_k, d_k, p.k_bytes / 2);
+        gk.seg[1] = segment(Wv, Vh, h * d_v, d_v, p.v_bytes / 2);
+        gk.count = 2;
+        gk.n_ntiles = (uint32_t)(gk.seg[0].n_tiles + gk.seg[1].n_tiles);
+        r = hip_status(sdpa::launch_proj_gemm(Xkv, 0, sk, gk, 1, s));
+        if (r != SDPA_OK) return r;
+    }
+
+    // 2. head_i = Attention(...) for every head (Eq. (1) with the masks).
+    r = forward_kernels(Qh, Kh, Vh, key_lengths, causal, Ah, B, h, Lq, Lk, d_k, d_v, SDPA_BF16, s);
+    if (r != SDPA_OK) return r;
+
+    // 3. Concat(head_1, ..., head_h) W^O, the concatenation read in place.
+    sdpa::GemmShape so{};
+    so.M = B * Lq;
+    so.K = h * d_v;
+    so.n_mtiles = (uint32_t)((so.M + 127) / 128);
+    so.La = Lq;
+    so.Ha = h;
+    so.da = d_v;
+    so.a_elems = p.a_bytes / 2;
+    sdpa::GemmSegments go{};
+    go.seg[0] = segment(Wo, out, d_model, d_model, p.out_bytes / 2);
+    go.count = 1;
+    go.n_ntiles = (uint32_t)go.seg[0].n_tiles;
+    return hip_status(sdpa::launch_proj_gemm(Ah, 1, so, go, 0, s));
 }
 
 sdpa_status sdpa_forward_restricted(const void *Q, const void *K, const void *V,

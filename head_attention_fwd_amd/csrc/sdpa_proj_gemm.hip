@@ -1,0 +1,312 @@
+// Projections of multi-head attention on the gfx950 matrix cores:
+//
+//   MultiHead(Q, K, V) = Concat(head_1, ..., head_h) W^O,
+//   head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V)
+//
+// (page "Attention Is All You Need/paper/es", §3.2.2).  Both kinds of
+// projection are one product C[M, N] = A[M, K] W[K, N] over the M = B * L
+// positions of a sequence, bf16 inputs, fp32 accumulation, bf16 result:
+//
+//  * input projections: A = the sequence [B, L, d_model] (row-major), W = the
+//    h matrices W_i of one kind side by side, [d_model, h * d] (W_i in columns
+//    i*d .. i*d + d - 1), and C written straight into the head-major layout
+//    [B, h, L, d] that the attention kernels read (column n = i*d + t of C is
+//    component t of head i).  Up to three such products that share A (Q, K and
+//    V of self-attention) run as one launch, the output columns of the three
+//    laid side by side;
+//  * output projection: A = Concat(head_1, ..., head_h), read from the
+//    attention's head-major output [B, h, L, d_v] (column k = i*d_v + t of the
+//    concatenation is component t of head i), W = W^O [h * d_v, d_model], and
+//    C = the result [B, L, d_model], row-major.
+//
+// Design (one workgroup = 4 waves = a 128 x 128 tile of C; k in steps of 32):
+//  * Computed transposed, C^T = W^T A^T, one 32 x 32 block per MFMA chain
+//    (v_mfma_f32_32x32x16_bf16): A operand = 32 columns n of W x 16 k, read
+//    from a W tile kept as it sits in HBM ([k][n], n contiguous) with
+//    ds_read_b64_tr_b16, which transposes 16-bit elements across 16 lanes; B
+//    operand = 16 k x 32 rows m of A, read from an A tile kept as in HBM ([m][k]).
+//    In the accumulator a lane holds one row m and, per block, 16 columns n in
+//    runs of 4, so the result leaves through LDS as whole 128-byte rows.
+//  * Each wave owns a 64 x 64 quarter of the tile: 2 x 2 blocks, 4 MFMAs per
+//    16-k step, each W operand and each A operand used twice.
+//  * HBM -> LDS copies without registers (buffer_load ... lds), 16-byte chunks
+//    XOR-swizzled by the row so that the operand reads are free of bank
+//    conflicts; a ring of three buffers with two tiles in flight and one
+//    barrier per tile.  48 KiB of LDS: three workgroups per CU.
+//  * Bounded buffer descriptors: rows of A past M read 0, stores past M or past
+//    a product's N are dropped.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sdpa_kernels.h"
+
+namespace sdpa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int kWaves = 4;
+constexpr int kBuffers = 3;
+constexpr int kATileElems = BM * BK;            // [128 m][32 k]: 64-byte rows
+constexpr int kWTileElems = BK * BN;            // [32 k][128 n]: 256-byte rows
+constexpr int kBufElems = kATileElems + kWTileElems;
+constexpr int kCopiesPerTile = (kATileElems + kWTileElems) * 2 / 1024;   // 1 KiB copies
+constexpr int kCopiesPerWave = kCopiesPerTile / kWaves;                  // 4: 2 of A, 2 of W
+constexpr uint32_t kNoOffset = 0x7FFFFFF0u;     // past every descriptor bound: read 0 / store dropped
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ inline u32x2_t ds_read_tr16_b64(const uint16_t *p)
+{
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p));
+}
+__device__ inline f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One wave-wide HBM -> LDS copy: lane L's 16 bytes at byte offset voff of the
+// buffer land at LDS address dst + 16*L.  Inline assembly, untracked by the
+// compiler: the kernel waits for these copies itself (vmcnt) before the barrier
+// that publishes a tile.
+__device__ inline void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint16_t *dst, uint32_t voff)
+{
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Chunk swizzles.  A tile rows (64 bytes, 4 chunks): rows r and r + 4 share
+// banks, so the chunk index is XORed with (r / 4) % 4.  W tile rows (256 bytes):
+// the 4 rows one transposing read touches get disjoint chunk pairs.
+__device__ inline int swz_a(int row) { return (row >> 2) & 3; }
+__device__ inline int swz_w(int row) { return (row & 3) << 1; }
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0,
+                                             (int)(bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes)),
+                                             kBufferRsrcWord3);
+}
+
+template <int AMODE, int CMODE>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments segs)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kBuffers * kBufElems];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+    const int wm = wave & 1, wn = wave >> 1;      // the wave's 64 x 64 quarter
+
+    // Tile of this workgroup: each XCD (workgroup w goes to XCD w % 8) takes a
+    // contiguous run of items, n fastest, so the workgroups reading one row
+    // block of A share that XCD's L2.
+    const uint32_t w = blockIdx.x;
+    const uint32_t n_items = sh.n_mtiles * segs.n_ntiles;
+    const uint32_t item = (n_items & 7) == 0 ? (w & 7) * (n_items >> 3) + (w >> 3) : w;
+    const int64_t m0 = (int64_t)(item / segs.n_ntiles) * BM;
+    int nt = (int)(item % segs.n_ntiles);
+    int s = 0;
+    while (s + 1 < segs.count && nt >= segs.seg[s].n_tiles) nt -= segs.seg[s++].n_tiles;
+    const GemmSegment seg = segs.seg[s];
+    const uint16_t *Wg = (const uint16_t *)seg.W;
+    const int64_t n0 = (int64_t)nt * BN;
+    const int64_t M = sh.M, K = sh.K, N = seg.N;
+
+    // ---- copy offsets (fixed per lane; tiles move the descriptor base)
+    // A tile: copy j of this wave fills rows 16*(2*wave + j) .. +15, lane L ->
+    // row 16*slice + L/4, physical chunk L%4 (logical chunk L%4 ^ swz_a(row)).
+    uint32_t aoff[2];
+    int64_t arow_base[2];     // AMODE 1: element offset of the row's (b, i) in head 0
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 16 * (2 * wave + j) + (lane >> 2);
+        const int lc = (lane & 3) ^ swz_a(row);
+        const int64_t m = m0 + row;
+        if constexpr (AMODE == 0) {
+            aoff[j] = (uint32_t)((row * K + lc * 8) * 2);    // relative to A + m0*K + k0
+            arow_base[j] = 0;
+        } else {
+            // A(m, k) = heads[b][k / d][i][k % d], m = b * L + i
+            const int64_t b = m / sh.La, i = m % sh.La;
+            arow_base[j] = (b * sh.Ha * sh.La + i) * sh.da;
+            aoff[j] = m < M ? (uint32_t)((arow_base[j] + lc * 8) * 2) : kNoOffset;
+        }
+    }
+    // W tile: copy j of this wave fills rows 4*(2*wave + j) .. +3 (k), lane L ->
+    // row 4*slice + L/16, physical chunk L%16 (logical L%16 ^ swz_w(row)).
+    uint32_t woff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 4 * (2 * wave + j) + (lane >> 4);
+        const int lc = (lane & 15) ^ swz_w(row);
+        woff[j] = (uint32_t)((row * N + lc * 8) * 2);          // relative to W + k0*N + n0
+    }
+
+    const int n_k = (int)((K + BK - 1) / BK);
+    auto issue = [&](int t, int buf) {
+        const int64_t k0 = (int64_t)t * BK;
+        uint16_t *As = lds + buf * kBufElems;
+        uint16_t *Ws = As + kATileElems;
+        __amdgpu_buffer_rsrc_t ra;
+        if constexpr (AMODE == 0) {
+            const int64_t base = m0 * K + k0;
+            ra = rsrc(A + base, (M * K - base) * 2);
+        } else {
+            // the 32 k of a tile lie in one head (d % 32 == 0)
+            const int64_t head = k0 / sh.da, t0 = k0 % sh.da;
+            const int64_t base = head * sh.La * sh.da + t0;
+            ra = rsrc(A + base, sh.a_elems * 2 - base * 2);
+        }
+        const int64_t wbase = k0 * N + n0;
+        const __amdgpu_buffer_rsrc_t rw = rsrc(Wg + wbase, (K * N - wbase) * 2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) copy_to_lds(ra, As + (2 * wave + j) * 512, aoff[j]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) copy_to_lds(rw, Ws + (2 * wave + j) * 512, woff[j]);
+    };
+
+    // ---- operand read offsets (bytes within a tile)
+    // B operand (A^T): row 64*wm + 32*mb + l32, logical chunk 2*kk + g.
+    int boff[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int row = 64 * wm + 32 * mb + l32;
+            boff[mb][kk] = row * 64 + (((2 * kk + g) ^ swz_a(row)) << 4);
+        }
+    // A operand (W^T), transposing read: in 16-lane group G, lane i addresses
+    // row 8*g + i/4 (+4 for the second read, +16*kk per 16-k step) and the 4
+    // columns 32*nb' + 16*(G%2) + 4*(i%4) of the tile, nb' = 2*wn + nb; lane l
+    // then holds column 32*nb' + l%32 at k = 16*kk + 8*g .. +7.
+    int voff[2];
+    {
+        const int i = lane & 15, G1 = (lane >> 4) & 1;
+        const int row = 8 * g + (i >> 2);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int col = 32 * (2 * wn + nb) + 16 * G1 + 4 * (i & 3);
+            voff[nb] = 2 * (row * BN + ((((col >> 3) ^ swz_w(row))) << 3) + (col & 7));
+        }
+    }
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+
+    issue(0, 0);
+    if (n_k > 1) issue(1, 1);
+    for (int t = 0; t < n_k; ++t) {
+        // Tile t has landed once at most tile t+1's copies are outstanding; the
+        // barrier publishes it and retires every wave's reads of tile t-1, whose
+        // buffer takes tile t+2.
+        if (t + 1 < n_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCopiesPerWave));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        if (t + 2 < n_k) issue(t + 2, (t + 2) % kBuffers);
+        const char *As = (const char *)(lds + (t % kBuffers) * kBufElems);
+        const char *Ws = As + kATileElems * 2;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8_t bop[2], aop[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) bop[mb] = as_bf16x8(*(const u32x4_t *)(As + boff[mb][kk]));
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const char *vb = Ws + voff[nb] + 16 * kk * BN * 2;
+                const u32x2_t lo = ds_read_tr16_b64((const uint16_t *)vb);
+                const u32x2_t hi = ds_read_tr16_b64((const uint16_t *)(vb + 4 * BN * 2));
+                const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+                aop[nb] = as_bf16x8(a);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32(aop[nb], bop[mb], acc[nb][mb]);
+        }
+    }
+
+    // ---- epilogue: the wave's 64 x 64 quarter through LDS (rows m of 128 bytes,
+    // chunks XOR-swizzled by the row), then 16-byte stores of whole chunks.
+    __syncthreads();                  // every wave is done with the tile buffers
+    uint16_t *stage = lds + wave * 64 * 64;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // acc[nb][mb][4q .. 4q+3]: row 32*mb + l32, columns 32*nb + 8*q + 4*g .. +3
+                const int row = 32 * mb + l32;
+                const int c = 4 * nb + q;
+                u32x2_t v;
+                v[0] = pack_bf16x2(acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1]);
+                v[1] = pack_bf16x2(acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+                *(u32x2_t *)((char *)stage + row * 128 + ((c ^ (row & 7)) << 4) + 8 * g) = v;
+            }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stage writes done
+    const __amdgpu_buffer_rsrc_t rc = rsrc(seg.C, seg.c_elems * 2);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int row = 8 * it + (lane >> 3), c = lane & 7;
+        const u32x4_t v = *(const u32x4_t *)((const char *)stage + row * 128 + ((c ^ (row & 7)) << 4));
+        const int64_t m = m0 + 64 * wm + row;
+        const int64_t n = n0 + 64 * wn + 8 * c;
+        uint32_t off = kNoOffset;
+        if (m < M && n < N) {
+            if constexpr (CMODE == 0) {
+                off = (uint32_t)((m * N + n) * 2);
+            } else {
+                const int64_t b = m / sh.Lc, i = m % sh.Lc;
+                const int64_t head = n / seg.d, tt = n % seg.d;
+                off = (uint32_t)((((b * sh.Hc + head) * sh.Lc + i) * seg.d + tt) * 2);
+            }
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_proj_gemm(const void *A, int a_mode, const GemmShape &shape,
+                            const GemmSegments &segs, int c_mode, hipStream_t stream)
+{
+    const uint32_t grid = shape.n_mtiles * segs.n_ntiles;
+    if (a_mode == 0 && c_mode == 1)
+        hipLaunchKernelGGL((proj_gemm_kernel<0, 1>), dim3(grid), dim3(kWaves * 64), 0, stream,
+                           (const uint16_t *)A, shape, segs);
+    else if (a_mode == 1 && c_mode == 0)
+        hipLaunchKernelGGL((proj_gemm_kernel<1, 0>), dim3(grid), dim3(kWaves * 64), 0, stream,
+                           (const uint16_t *)A, shape, segs);
+    else if (a_mode == 0 && c_mode == 0)
+        hipLaunchKernelGGL((proj_gemm_kernel<0, 0>), dim3(grid), dim3(kWaves * 64), 0, stream,
+                           (const uint16_t *)A, shape, segs);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace sdpa

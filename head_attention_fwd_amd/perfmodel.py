@@ -65,3 +65,20 @@ def min_bytes(B, H, Lq, Lk, d_k, d_v, causal, key_lengths=None, elem=2, radius=N
             lb = min(lb, Lq + int(radius)) if Lq > 0 else 0
         rows_kv += lb
     return elem * H * (B * Lq * (d_k + d_v) + rows_kv * (d_k + d_v))
+
+
+def multihead_flops(B, Lq, Lk, d_model, h, d_k, d_v, causal, key_lengths=None):
+    """Algorithmic FLOPs of MultiHead(Q, K, V) (same page, §3.2.2): the products
+    with W^Q (every query position), W^K and W^V (every key position), W^O, and
+    the attention's allowed pairs."""
+    proj = 2 * B * Lq * d_model * h * d_k + 2 * B * Lk * d_model * h * (d_k + d_v) \
+        + 2 * B * Lq * h * d_v * d_model
+    return proj + flops(B, h, Lq, Lk, d_k, d_v, causal, key_lengths)
+
+
+def multihead_min_bytes(B, Lq, Lk, d_model, h, d_k, d_v, self_attention, elem=2):
+    """Algorithmic HBM bytes of one MultiHead call: the input sequence(s), the
+    four weight matrices and the output once."""
+    x = B * Lq * d_model + (0 if self_attention else B * Lk * d_model)
+    w = d_model * h * (2 * d_k + d_v) + h * d_v * d_model
+    return elem * (x + w + B * Lq * d_model)

@@ -114,6 +114,53 @@ sdpa_status sdpa_forward_restricted(const void *Q, const void *K, const void *V,
                                     int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream);
 
 /*
+ * Multi-head attention with its projections (page "Attention Is All You
+ * Need/paper/es", §3.2.2):
+ *
+ *   out = MultiHead(Q, K, V) = Concat(head_1, ..., head_h) W^O,
+ *   head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V),
+ *
+ * Attention being the operation of sdpa_forward (scale 1/sqrt(d_k), the
+ * padding mask from key_lengths and, if causal, the causal mask).  Q is the
+ * sequence the queries come from, K = V the sequence the keys and values come
+ * from: the same buffer for encoder or decoder self-attention (Xkv == Xq and
+ * Lk == Lq), the encoder output for encoder-decoder attention (§3.2.3).
+ *   Xq        device [B, Lq, d_model];
+ *   Xkv       device [B, Lk, d_model] (may equal Xq);
+ *   Wq, Wk    device [d_model, h * d_k]: W_i^Q (W_i^K) in R^{d_model x d_k} is
+ *             columns i*d_k .. i*d_k + d_k - 1;
+ *   Wv        device [d_model, h * d_v], W_i^V likewise;
+ *   Wo        device [h * d_v, d_model] = W^O: row i*d_v + t multiplies
+ *             component t of head i in the concatenation;
+ *   out       device [B, Lq, d_model], written completely;
+ *   workspace device scratch of at least sdpa_multihead_workspace_bytes(...)
+ *             bytes (the projected heads and the attention output, bf16),
+ *             owned by the caller; its contents on entry do not matter.
+ * All arrays contiguous row-major, dtype SDPA_BF16 only: bf16 products with
+ * fp32 accumulation, the projected heads and the attention output rounded to
+ * bf16 (nearest even), the result rounded to bf16.  No bias terms (the pages'
+ * projections are matrices).  Supported: d_model % 32 == 0, d_k % 8 == 0,
+ * d_v % 32 == 0, d_k, d_v <= 128, every array and each projected tensor below
+ * 2 GiB - 1 MiB (SDPA_ERR_UNSUPPORTED / SDPA_ERR_BAD_SHAPE otherwise).
+ * Errors as sdpa_forward, plus SDPA_ERR_WORKSPACE (missing, too small, or
+ * overlapping another buffer); out must not overlap an input.  Four kernels
+ * (three when Xkv == Xq) are enqueued on `stream`; calls that share a
+ * workspace must be ordered on one stream.  B == 0 or Lq == 0: SDPA_OK,
+ * nothing launched.
+ */
+sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *Wq,
+                                   const void *Wk, const void *Wv, const void *Wo,
+                                   const int32_t *key_lengths, int causal, void *out,
+                                   int64_t B, int64_t Lq, int64_t Lk, int64_t d_model,
+                                   int64_t h, int64_t d_k, int64_t d_v, sdpa_dtype dtype,
+                                   void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes sdpa_multihead_forward needs for these sizes, or -1 when it
+ * would reject them (no pointers are involved). */
+int64_t sdpa_multihead_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model,
+                                       int64_t h, int64_t d_k, int64_t d_v, sdpa_dtype dtype);
+
+/*
  * Decode-step attention: the same result as sdpa_forward with causal = 0, for
  * the case of a few query rows per head against a long key/value cache (the
  * new positions of an autoregressive decoder, page "Attention Is All You

@@ -180,3 +180,69 @@ def test_restricted_empty_calls():
     assert rcall(B=0) == sdpa.SDPA_OK
     assert rcall(Lq=0, radius=2**40) == sdpa.SDPA_OK
     assert rcall(Q=0, K=0, V=0, O=0, H=0, radius=0) == sdpa.SDPA_OK
+
+
+# ---- sdpa_multihead_forward: host-side checks
+
+FAKE_X, FAKE_WQ, FAKE_WK, FAKE_WV, FAKE_WO, FAKE_WS = (0x100000, 0x200000, 0x300000, 0x400000,
+                                                       0x500000, 0x1000000)
+FAKE_OUT = 0x600000
+
+
+def mcall(**kw):
+    a = dict(Xq=FAKE_X, Xkv=FAKE_X, Wq=FAKE_WQ, Wk=FAKE_WK, Wv=FAKE_WV, Wo=FAKE_WO, kl=0,
+             causal=0, out=FAKE_OUT, B=2, Lq=16, Lk=16, dm=64, h=2, dk=32, dv=32,
+             dtype=sdpa.SDPA_BF16, ws=FAKE_WS, ws_bytes=1 << 20)
+    a.update(kw)
+    return sdpa.sdpa_multihead_forward(a["Xq"], a["Xkv"], a["Wq"], a["Wk"], a["Wv"], a["Wo"],
+                                       a["kl"], a["causal"], a["out"], a["B"], a["Lq"], a["Lk"],
+                                       a["dm"], a["h"], a["dk"], a["dv"], a["dtype"], a["ws"],
+                                       a["ws_bytes"], 0)
+
+
+def test_multihead_workspace_bytes():
+    f = sdpa.sdpa_multihead_workspace_bytes
+    # Q, K, V heads and the attention output, bf16, each 256-byte aligned
+    assert f(2, 16, 16, 64, 2, 32, 32, sdpa.SDPA_BF16) == 4 * (2 * 2 * 16 * 32 * 2)
+    n = f(3, 7, 9, 64, 2, 8, 32, sdpa.SDPA_BF16)
+    sizes = [3 * 2 * 7 * 8 * 2, 3 * 2 * 9 * 8 * 2, 3 * 2 * 9 * 32 * 2, 3 * 2 * 7 * 32 * 2]
+    off = 0
+    for s in sizes:
+        off = (off + s + 255) // 256 * 256
+    assert n == off
+    assert f(2, 16, 16, 64, 2, 32, 32, sdpa.SDPA_F32) == -1      # bf16 only
+    assert f(2, 16, 16, 48, 2, 32, 32, sdpa.SDPA_BF16) == -1     # d_model % 32
+    assert f(2, 16, 16, 64, 2, 12, 32, sdpa.SDPA_BF16) == -1     # d_k % 8
+    assert f(2, 16, 16, 64, 2, 32, 16, sdpa.SDPA_BF16) == -1     # d_v % 32
+    assert f(2, 16, 16, 64, 2, 256, 32, sdpa.SDPA_BF16) == -1    # d_k > 128
+    assert f(-1, 16, 16, 64, 2, 32, 32, sdpa.SDPA_BF16) == -1
+    assert f(1, 2**21, 2**21, 1024, 16, 64, 64, sdpa.SDPA_BF16) == -1   # tensors past 2 GiB
+    assert f(0, 16, 16, 64, 2, 32, 32, sdpa.SDPA_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(Xq=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(Wk=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(Wo=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(out=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(Xkv=0, Lk=4), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(dtype=sdpa.SDPA_F32), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dm=40), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dv=40), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(h=0), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(Lk=-3), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(ws=0), sdpa.SDPA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), sdpa.SDPA_ERR_WORKSPACE),
+    (dict(ws=FAKE_X), sdpa.SDPA_ERR_WORKSPACE),          # workspace over an input
+    (dict(ws=FAKE_OUT - 64), sdpa.SDPA_ERR_WORKSPACE),   # workspace over out
+    (dict(out=FAKE_WQ + 64), sdpa.SDPA_ERR_ALIAS),
+    (dict(out=FAKE_X), sdpa.SDPA_ERR_ALIAS),
+])
+def test_multihead_prelaunch_validation(kw, expected):
+    assert mcall(**kw) == expected
+
+
+def test_multihead_empty_calls():
+    assert mcall(B=0) == sdpa.SDPA_OK
+    assert mcall(Lq=0, Lk=3) == sdpa.SDPA_OK
+    assert mcall(B=0, Xq=0, Xkv=0, Wq=0, Wk=0, Wv=0, Wo=0, out=0, ws=0) == sdpa.SDPA_OK

@@ -47,6 +47,8 @@ class Config:
     entry: str = "forward"   # "forward": sdpa_forward; "decode": sdpa_decode (causal = False);
     #                          "restricted": sdpa_forward_restricted with `radius`
     radius: Optional[int] = None
+    d_model: Optional[int] = None   # entry "multihead": model width; H heads of d_k, d_v
+    self_attention: bool = True     # entry "multihead": keys and values from the query sequence
 
 
 CONFIGS = {
@@ -99,6 +101,23 @@ CONFIGS = {
         "(the 256 positions up to each output), inputs scaled by 0.5", "bf16",
         B=4, H=16, Lq=8192, Lk=8192, d_k=64, d_v=64, causal=True, key_len_range=None,
         scale=0.5, seed=11, entry="restricted", radius=255),
+    # Multi-head attention with its projections (§3.2.2, sdpa_multihead_forward):
+    # random-init weights of the base and big models' shapes.
+    "mha_base_encoder_bf16": Config(
+        "mha_base_encoder_bf16", "base-model encoder multi-head self-attention with the "
+        "projections (d_model 512, h 8), key padding", "bf16",
+        B=64, H=8, Lq=256, Lk=256, d_k=64, d_v=64, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=12, entry="multihead", d_model=512),
+    "mha_big_cross_bf16": Config(
+        "mha_big_cross_bf16", "big-model encoder-decoder multi-head attention with the "
+        "projections (d_model 1024, h 16), encoder padding", "bf16",
+        B=32, H=16, Lq=256, Lk=320, d_k=64, d_v=64, causal=False, key_len_range=(128, 320),
+        scale=1.0, seed=13, entry="multihead", d_model=1024, self_attention=False),
+    "mha_long_causal_bf16": Config(
+        "mha_long_causal_bf16", "long-sequence causal multi-head self-attention with the "
+        "projections (d_model 1024, h 16), inputs scaled by 0.5", "bf16",
+        B=4, H=16, Lq=8192, Lk=8192, d_k=64, d_v=64, causal=True, key_len_range=None,
+        scale=0.5, seed=14, entry="multihead", d_model=1024),
     # Decode steps (sdpa_decode): the new position of an autoregressive decoder
     # against the cache of the positions generated so far (§3.1, §3.2.3).
     "decode_long_bf16": Config(
@@ -118,7 +137,8 @@ CONFIGS = {
 ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
          "big_cross_bf16", "long_causal_bf16", "rowA_h4_d128_encoder_bf16",
          "rowA_h16_d32_encoder_bf16", "long_causal_d128_bf16", "restricted_long_bf16",
-         "restricted_long_causal_bf16", "decode_base_bf16", "decode_long_bf16"]
+         "restricted_long_causal_bf16", "mha_base_encoder_bf16", "mha_big_cross_bf16",
+         "mha_long_causal_bf16", "decode_base_bf16", "decode_long_bf16"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -164,9 +184,63 @@ def draw(B: int, H: int, Lq: int, Lk: int, d_k: int, d_v: int, *, dtype: str = "
     return q, k, v, kl
 
 
-def generate(name: str) -> Inputs:
-    """Inputs for one named configuration."""
+@dataclasses.dataclass
+class MultiHeadInputs:
+    config: Config
+    xq: np.ndarray                      # [B, Lq, d_model] float32
+    xkv: np.ndarray                     # [B, Lk, d_model]; xq itself for self-attention
+    wq: np.ndarray                      # [d_model, h*d_k]
+    wk: np.ndarray                      # [d_model, h*d_k]
+    wv: np.ndarray                      # [d_model, h*d_v]
+    wo: np.ndarray                      # [h*d_v, d_model]
+    key_lengths: Optional[np.ndarray]   # [B] int32 or None
+
+
+def draw_multihead(B: int, Lq: int, Lk: int, d_model: int, h: int, d_k: int, d_v: int, *,
+                   seed: int = 0, scale: float = 1.0, self_attention: bool = True,
+                   key_len_range: Optional[tuple] = None, dtype: str = "bf16"):
+    """Draw (xq, xkv, wq, wk, wv, wo, key_lengths) with the module's recipe.
+
+    Recipe: the same generator; xq (then xkv unless self-attention; then xkv is
+    xq and Lk must equal Lq) standard normal times ``scale``; then wq, wk, wv,
+    wo standard normal divided by sqrt(fan_in) (d_model for wq, wk, wv; h*d_v for
+    wo), so that every projection keeps unit scale; key_lengths last.  All
+    rounded to float32 and, for bf16, to bfloat16 (nearest even)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def one(shape, mult):
+        a = rng.standard_normal(shape)
+        if mult != 1.0:
+            a = a * mult
+        a = a.astype(np.float32)
+        return round_to_bf16(a) if dtype == "bf16" else a
+
+    xq = one((B, Lq, d_model), scale)
+    if self_attention:
+        if Lk != Lq:
+            raise ValueError("self-attention needs Lk == Lq")
+        xkv = xq
+    else:
+        xkv = one((B, Lk, d_model), scale)
+    wq = one((d_model, h * d_k), 1.0 / np.sqrt(d_model))
+    wk = one((d_model, h * d_k), 1.0 / np.sqrt(d_model))
+    wv = one((d_model, h * d_v), 1.0 / np.sqrt(d_model))
+    wo = one((h * d_v, d_model), 1.0 / np.sqrt(h * d_v))
+    kl = None
+    if key_len_range is not None:
+        lo, hi = key_len_range
+        kl = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    return xq, xkv, wq, wk, wv, wo, kl
+
+
+def generate(name: str):
+    """Inputs for one named configuration (MultiHeadInputs for entry "multihead")."""
     c = CONFIGS[name]
+    if c.entry == "multihead":
+        return MultiHeadInputs(c, *draw_multihead(c.B, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v,
+                                                  seed=c.seed, scale=c.scale,
+                                                  self_attention=c.self_attention,
+                                                  key_len_range=c.key_len_range, dtype=c.dtype))
     q, k, v, kl = draw(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, dtype=c.dtype, seed=c.seed,
                        scale=c.scale, key_len_range=c.key_len_range)
     return Inputs(c, q, k, v, kl)

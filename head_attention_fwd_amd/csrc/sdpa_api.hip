@@ -190,7 +190,8 @@ sdpa_status mh_plan(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model, int64_t 
     p.v_off = align256(p.k_off + p.k_bytes);
     p.a_off = align256(p.v_off + p.v_bytes);
     p.total = align256(p.a_off + p.a_bytes);
-    // projection grids: ceil(B*L / 128) row tiles times at most 3 * ceil(h*d / 128) column tiles
+    // projection grids (128 x 128 tiles at most): row tiles times at most 3
+    // products' column tiles
     const int64_t mt = (B * (Lq > Lk ? Lq : Lk) + 127) / 128;
     const int64_t nt = 3 * ((h * (d_k > d_v ? d_k : d_v) + 127) / 128) + (d_model + 127) / 128;
     if (mt > 0 && nt > kMaxWorkgroups / mt) return SDPA_ERR_BAD_SHAPE;
@@ -205,7 +206,7 @@ sdpa::GemmSegment segment(const void *W, void *C, int64_t N, int64_t d, int64_t 
     sg.N = N;
     sg.d = d;
     sg.c_elems = c_elems;
-    sg.n_tiles = (int)((N + 127) / 128);
+    sg.n_tiles = 0;   // set by the launcher
     return sg;
 }
 
@@ -283,7 +284,7 @@ sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *
     sdpa::GemmShape sq{};
     sq.K = d_model;
     sq.M = B * Lq;
-    sq.n_mtiles = (uint32_t)((sq.M + 127) / 128);
+
     sq.Lc = Lq;
     sq.Hc = h;
     sdpa::GemmSegments gq{};
@@ -295,19 +296,16 @@ sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *
         gq.seg[2] = segment(Wv, Vh, h * d_v, d_v, p.v_bytes / 2);
         gq.count = 3;
     }
-    for (int i = 0; i < gq.count; ++i) gq.n_ntiles += (uint32_t)gq.seg[i].n_tiles;
     sdpa_status r = hip_status(sdpa::launch_proj_gemm(Xq, 0, sq, gq, 1, s));
     if (r != SDPA_OK) return r;
     if (!self_attn && Lk > 0) {
         sdpa::GemmShape sk = sq;
         sk.M = B * Lk;
-        sk.n_mtiles = (uint32_t)((sk.M + 127) / 128);
         sk.Lc = Lk;
         sdpa::GemmSegments gk{};
         gk.seg[0] = segment(Wk, Kh, h * d_k, d_k, p.k_bytes / 2);
         gk.seg[1] = segment(Wv, Vh, h * d_v, d_v, p.v_bytes / 2);
         gk.count = 2;
-        gk.n_ntiles = (uint32_t)(gk.seg[0].n_tiles + gk.seg[1].n_tiles);
         r = hip_status(sdpa::launch_proj_gemm(Xkv, 0, sk, gk, 1, s));
         if (r != SDPA_OK) return r;
     }
@@ -320,7 +318,6 @@ sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *
     sdpa::GemmShape so{};
     so.M = B * Lq;
     so.K = h * d_v;
-    so.n_mtiles = (uint32_t)((so.M + 127) / 128);
     so.La = Lq;
     so.Ha = h;
     so.da = d_v;
@@ -328,7 +325,6 @@ sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *
     sdpa::GemmSegments go{};
     go.seg[0] = segment(Wo, out, d_model, d_model, p.out_bytes / 2);
     go.count = 1;
-    go.n_ntiles = (uint32_t)go.seg[0].n_tiles;
     return hip_status(sdpa::launch_proj_gemm(Ah, 1, so, go, 0, s));
 }
 

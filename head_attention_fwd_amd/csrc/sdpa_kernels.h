@@ -42,24 +42,25 @@ hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
                                  void *workspace, hipStream_t stream);
 
 // Projection products of multi-head attention, C = A W on the matrix cores
-// (bf16, fp32 accumulation), 128 x 128 tiles of C, k in steps of 32.
+// (bf16, fp32 accumulation), tiles of 128 x 128 or 256 x 128 elements of C
+// (chosen by the launcher from the problem size), k in steps of 32.
 struct GemmSegment {
     const void *W;       // [K, N] row-major
     void *C;             // c_mode 0: [M, N] row-major; c_mode 1: [B, Hc, Lc, d], column n = head*d + t
     int64_t N;           // columns of this product (multiple of 8)
     int64_t d;           // c_mode 1: head size (multiple of 8)
     int64_t c_elems;     // elements of C
-    int n_tiles;         // ceil(N / 128)
+    int n_tiles;         // set by launch_proj_gemm
 };
 // Up to three products that share A, their output columns side by side.
 struct GemmSegments {
     GemmSegment seg[3];
     int count;
-    uint32_t n_ntiles;   // sum of the segments' n_tiles
+    uint32_t n_ntiles;   // set by launch_proj_gemm
 };
 struct GemmShape {
     int64_t M, K;        // rows of A and C; K a multiple of 32
-    uint32_t n_mtiles;   // ceil(M / 128)
+    uint32_t n_mtiles;   // set by launch_proj_gemm
     int64_t La, Ha, da;  // a_mode 1: A(m, k) = heads[b][k / da][i][k % da], m = b*La + i (da % 32 == 0)
     int64_t a_elems;     // elements of A
     int64_t Lc, Hc;      // c_mode 1: m = b*Lc + i, Hc heads

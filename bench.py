@@ -377,10 +377,10 @@ def main():
                           "(sdpa_fwd_mfma_kernel); per-kernel split in the rocprofv3 summary")
     elif c.entry == "restricted":
         roof["kernel"] = ("sdpa_fwd_mfma_band_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
-                                                           c.d_k in (32, 64, 128)) else "sdpa_fwd_generic_kernel")
+                                                           c.d_k in (16, 32, 64, 128)) else "sdpa_fwd_generic_kernel")
     else:
         roof["kernel"] = ("sdpa_fwd_mfma_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
-                                                      c.d_k in (32, 64, 128)) else "sdpa_fwd_generic_kernel")
+                                                      c.d_k in (16, 32, 64, 128)) else "sdpa_fwd_generic_kernel")
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
     roof["kernel_ms"] = kern_ms

@@ -105,7 +105,7 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
     if (radius >= Lq || radius >= Lk) radius = -1;
     // Lk == 0 needs no special case: both kernels then stage no key tile and
     // write 0 for every row (no legal connection).
-    if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128)) {
+    if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128)) {
         if (radius >= 0)
             return hip_status(sdpa::launch_mfma_band(Q, K, V, key_lengths, causal ? 1 : 0, radius, out,
                                                      B, H, Lq, Lk, (int)d_k, s));

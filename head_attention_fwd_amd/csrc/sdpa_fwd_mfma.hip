@@ -1,5 +1,5 @@
 // Scaled dot-product attention forward for bf16 inputs with d_k = d_v = D,
-// D in {32, 64, 128}, on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
+// D in {16, 32, 64, 128}, on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation).
 //
 // What it computes: Eq. (1) of page "Attention Is All You Need/paper/es"
@@ -101,7 +101,7 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget at D = 64: 3 waves per SIMD
 #endif
 // Waves per SIMD the register budget is set for, by head size: D = 128 needs
-// 64 accumulator and 32 Q-operand registers (2 waves), D = 32 fits 4.
+// 64 accumulator and 32 Q-operand registers (2 waves), D = 32 and D = 16 fit 4.
 template <int D>
 struct Occupancy {
     static constexpr int kWaves = D >= 128 ? 2 : (D >= 64 ? SDPA_MFMA_WAVES_PER_SIMD : 4);
@@ -114,12 +114,17 @@ struct Occupancy {
 // on the 8 even or 8 odd rows of any 16 consecutive rows; D = 32, four rows per
 // 256 bytes: rows r and r + 4 differ).
 template <int D>
-__device__ inline int swz(int row) { return D >= 64 ? (row ^ (row >> 3)) & 7 : (row >> 2) & 3; }
+__device__ inline int swz(int row)
+{
+    // D = 16: rows of 32 bytes; 8 consecutive rows at one chunk already cover
+    // 8 distinct bank groups
+    return D >= 64 ? (row ^ (row >> 3)) & 7 : (D >= 32 ? (row >> 2) & 3 : 0);
+}
 
 // V rows: the 4 rows one ds_read_b64_tr_b16 group touches get disjoint chunk
 // pairs (D = 32: the two 16-dim halves of a row stay apart).
 template <int D>
-__device__ inline int swz_v(int row) { return D >= 64 ? (row & 3) << 1 : (row & 1) << 1; }
+__device__ inline int swz_v(int row) { return D >= 64 ? (row & 3) << 1 : (D >= 32 ? (row & 1) << 1 : 0); }
 
 // Key row order fed to the score MFMA: swap bits 2 and 3 (an involution).
 __device__ inline int pi32(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -253,7 +258,12 @@ struct Attn {
     static constexpr int kD = D;                 // d_k = d_v
     static constexpr int kRowBytes = 2 * D;      // one K or V row in HBM and LDS
     static constexpr int kKB = D / 16;           // 16-dim chunks of the score contraction
-    static constexpr int kDB = D / 32;           // 32-dim blocks of the output
+    // 32-dim blocks of the output.  D = 16: one block whose dims 16..31 are not
+    // head dims: their V^T rows are read from the neighbouring LDS row (an
+    // MFMA output row depends only on its own A row, so they never mix into
+    // dims 0..15) and they are never stored.
+    static constexpr int kDB = (D + 31) / 32;
+    static constexpr int kLdsPad = D < 32 ? 32 : 0;   // elements: those reads past the last row stay in LDS
     static constexpr int BM = 32 * NW;
     static constexpr int BN = 32 * NB;
     static constexpr int kTileElems = BN * kD;   // bf16 elements per K (or V) tile
@@ -264,7 +274,7 @@ struct Attn {
     // (D = 128 with 32-key tiles) the Q operand is loaded straight into
     // registers.
     static constexpr bool kQViaLds = 2 * BN / NW >= 32;
-    static_assert(D == 32 || D == 64 || D == 128, "head sizes with a matrix-core layout");
+    static_assert(D == 16 || D == 32 || D == 64 || D == 128, "head sizes with a matrix-core layout");
 
     uint16_t *kbuf[kBuffers], *vbuf[kBuffers];   // LDS tile buffers
     const uint16_t *Kh, *Vh;
@@ -528,7 +538,8 @@ struct Attn {
     __device__ __forceinline__ void read_q()
     {
         if constexpr (kQViaLds) {
-            const uint16_t *row = (l32 < 16 ? kbuf[2] : vbuf[2]) + (16 * wave + (l32 & 15)) * kD;
+            const uint16_t *row = D < 32 ? kbuf[2] + (32 * wave + l32) * kD
+                                         : (l32 < 16 ? kbuf[2] : vbuf[2]) + (16 * wave + (l32 & 15)) * kD;
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb)
                 qf[kb] = *(const bf16x8_t *)(row + (((2 * kb + g) ^ swz<D>(l32)) << 3));
@@ -787,14 +798,16 @@ __device__ __forceinline__ void attend_query_tile(
     if (st.n_tiles > 0) {
         if constexpr (A::kQViaLds) {
             // This wave's 32 Q rows into buffer 2 (rows 0-15 where its share of
-            // tile 2's K rows lands, rows 16-31 where its V rows land), 512/D
-            // rows per copy, chunks swizzled by the row.
+            // tile 2's K rows lands, rows 16-31 where its V rows land; D = 16:
+            // all 32 in its K share, 32 rows of 128 keys), 512/D rows per copy,
+            // chunks swizzled by the row.
             constexpr int kRps = 512 / D, kC = D / 8;
 #pragma unroll
             for (int sl = 0; sl < 32 / kRps; ++sl) {
                 const int qrow = kRps * sl + lane / kC;
                 const int r0 = kRps * sl;                    // first Q row of this copy
-                const uint16_t *dst = (r0 < 16 ? st.kbuf[2] : st.vbuf[2]) + (16 * wave + (r0 & 15)) * kD;
+                const uint16_t *dst = D < 32 ? st.kbuf[2] + 32 * wave * kD
+                                             : (r0 < 16 ? st.kbuf[2] : st.vbuf[2]) + (16 * wave + (r0 & 15)) * kD;
                 copy_to_lds(rq, dst, (uint32_t)(qrow * kRowBytes + (((lane % kC) ^ swz<D>(qrow)) << 4)));
             }
         } else {
@@ -871,11 +884,12 @@ __device__ __forceinline__ void attend_query_tile(
     __syncthreads();
     uint16_t *stage = kbuf[0] + wave * 32 * kD;
     constexpr int kC = kD / 8, kRps = 512 / kD;
-    auto oswz = [](int r) { return kD >= 64 ? r & 7 : (r >> 2) & 3; };
+    auto oswz = [](int r) { return kD >= 64 ? r & 7 : (kD >= 32 ? (r >> 2) & 3 : 0); };
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int rq4 = 0; rq4 < 4; ++rq4) {
+            if (32 * db + 8 * rq4 >= kD) continue;   // D = 16: dims 16..31 are not output
             u32x2_t w;
             w[0] = pack_bf16x2(st.acc[db][4 * rq4 + 0] * inv, st.acc[db][4 * rq4 + 1] * inv);
             w[1] = pack_bf16x2(st.acc[db][4 * rq4 + 2] * inv, st.acc[db][4 * rq4 + 3] * inv);
@@ -893,6 +907,7 @@ __device__ __forceinline__ void attend_query_tile(
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int rq4 = 0; rq4 < 4; ++rq4) {
+            if (32 * db + 8 * rq4 >= kD) continue;
             u32x2_t w;
             w[0] = pack_bf16x2(st.acc[db][4 * rq4 + 0] * inv, st.acc[db][4 * rq4 + 1] * inv);
             w[1] = pack_bf16x2(st.acc[db][4 * rq4 + 2] * inv, st.acc[db][4 * rq4 + 3] * inv);
@@ -927,7 +942,7 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves)))
     uint32_t n_qtiles, uint32_t n_bh)
 {
     using A = Attn<NW, NB, D>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride + A::kLdsPad];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
 #pragma unroll
     for (int i = 0; i < A::kBuffers; ++i) {
@@ -980,7 +995,7 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves)))
     uint32_t n_qtiles, uint32_t n_bh)
 {
     using A = Attn<NW, NB, D, true>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride + A::kLdsPad];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
 #pragma unroll
     for (int i = 0; i < A::kBuffers; ++i) {
@@ -1010,7 +1025,7 @@ __global__ __launch_bounds__(64) void sdpa_split_mfma_d64_kernel(
     // keep the cache streaming.
     constexpr int NW = 1, NB = SDPA_SPLIT_KEY_BLOCKS, D = 64;
     using A = Attn<NW, NB, D>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride + A::kLdsPad];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
 #pragma unroll
     for (int i = 0; i < A::kBuffers; ++i) {
@@ -1094,8 +1109,9 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
                          hipStream_t stream)
 {
     constexpr int NW = SDPA_MFMA_WAVES;
-    // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB.
-    constexpr int NB = D >= 128 ? 1 : SDPA_MFMA_KEY_BLOCKS;
+    // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB;
+    // D = 16: 128-key tiles, so that each wave copies one whole 1 KiB slice.
+    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 4);
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
@@ -1113,7 +1129,7 @@ hipError_t launch_mfma_band_d(const void *Q, const void *K, const void *V, const
                               int64_t Lk, hipStream_t stream)
 {
     constexpr int NW = SDPA_MFMA_WAVES;
-    constexpr int NB = D >= 128 ? 1 : SDPA_MFMA_KEY_BLOCKS;
+    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 4);
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
@@ -1132,6 +1148,7 @@ hipError_t launch_mfma_band(const void *Q, const void *K, const void *V, const i
                             int64_t Lk, int d, hipStream_t stream)
 {
     switch (d) {
+    case 16: return launch_mfma_band_d<16>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, stream);
     case 32: return launch_mfma_band_d<32>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, stream);
     case 64: return launch_mfma_band_d<64>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, stream);
     case 128: return launch_mfma_band_d<128>(Q, K, V, key_lengths, causal, radius, out, B, H, Lq, Lk, stream);
@@ -1144,6 +1161,7 @@ hipError_t launch_mfma(const void *Q, const void *K, const void *V, const int32_
                        hipStream_t stream)
 {
     switch (d) {
+    case 16: return launch_mfma_d<16>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
     case 32: return launch_mfma_d<32>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
     case 64: return launch_mfma_d<64>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
     case 128: return launch_mfma_d<128>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);

@@ -18,7 +18,7 @@ hipError_t launch_generic(const void *Q, const void *K, const void *V,
                           int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                           int d_k, int d_v, bool is_bf16, hipStream_t stream);
 
-// bf16, d_k = d_v = d with d in {32, 64, 128}, on the matrix cores
+// bf16, d_k = d_v = d with d in {16, 32, 64, 128}, on the matrix cores
 // (hipErrorInvalidValue for any other d).
 hipError_t launch_mfma(const void *Q, const void *K, const void *V,
                        const int32_t *key_lengths, int causal, void *out,

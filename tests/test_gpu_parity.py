@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("name", ["tiny_causal_f32", "base_encoder_bf16",
                                   "base_decoder_causal_bf16", "big_cross_bf16",
-                                  "rowA_h4_d128_encoder_bf16", "rowA_h16_d32_encoder_bf16"])
+                                  "rowA_h4_d128_encoder_bf16", "rowA_h16_d32_encoder_bf16",
+                                  "rowA_h32_d16_encoder_bf16"])
 def test_config_full(name):
     x = workloads.generate(name)
     c = x.config
@@ -73,13 +74,15 @@ RAGGED = [
     (1, 1, 5, 7, 16, 16, False, None),
 ]
 # The same shapes on the matrix-core kernel's other head sizes (d = 128 uses
-# 32-key tiles and loads Q straight into registers; d = 32 packs 4 rows per 256 B).
-for _d in (32, 128):
+# 32-key tiles and loads Q straight into registers; d = 32 packs 4 rows per 256 B;
+# d = 16 uses 128-key tiles and half of each 32-row output block).
+for _d in (16, 32, 128):
     RAGGED += [(B, H, Lq, Lk, _d, _d, c, ln) for (B, H, Lq, Lk, dk, dv, c, ln) in RAGGED[:10]]
 RAGGED += [
     (2, 2, 70, 90, 32, 32, True, [50, 90]),
     (2, 2, 70, 90, 128, 128, False, [90, 3]),
     (2, 3, 160, 97, 128, 128, True, [97, 33]),   # several 32-key tiles, ragged tail
+    (2, 3, 300, 700, 16, 16, True, [700, 250]),  # several 128-key tiles, ragged tail
 ]
 
 
@@ -116,7 +119,7 @@ def test_ragged_f32(case):
     assert_parity(got, ref, v, "f32", str(case))
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
 def test_long_keys_sampled_rows(d):
     """A long key sequence (32768 keys) on the matrix-core kernel, non-causal with
     padding, rows sampled for the oracle."""

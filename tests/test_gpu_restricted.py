@@ -59,6 +59,8 @@ CASES = [
     (2, 2, 1000, 1000, 128, False, [1000, 555], 70),
     (2, 2, 1000, 1000, 128, True, None, 33),
     (1, 2, 1000, 1000, 128, False, None, 16),
+    (2, 2, 1000, 1000, 16, False, [1000, 555], 70),
+    (2, 2, 1000, 1000, 16, True, None, 129),
 ]
 
 

@@ -42,7 +42,7 @@ hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
                                  void *workspace, hipStream_t stream);
 
 // Projection products of multi-head attention, C = A W on the matrix cores
-// (bf16, fp32 accumulation), tiles of 128 x 128 or 256 x 128 elements of C
+// (bf16, fp32 accumulation), tiles of 128 x 128 or 256 x 256 elements of C
 // (chosen by the launcher from the problem size), k in steps of 32.
 struct GemmSegment {
     const void *W;       // [K, N] row-major

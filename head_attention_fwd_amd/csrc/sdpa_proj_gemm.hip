@@ -19,8 +19,8 @@
 //    concatenation is component t of head i), W = W^O [h * d_v, d_model], and
 //    C = the result [B, L, d_model], row-major.
 //
-// Design (one workgroup = 4 waves = a 128 x 128 or 256 x 128 tile of C; k in
-// steps of 32):
+// Design (one workgroup = 4 waves and a 128 x 128 tile of C, or 8 waves and a
+// 256 x 256 tile; k in steps of 32):
 //  * Computed transposed, C^T = W^T A^T, one 32 x 32 block per MFMA chain
 //    (v_mfma_f32_32x32x16_bf16): A operand = 32 columns n of W x 16 k, read
 //    from a W tile kept as it sits in HBM ([k][n], n contiguous) with
@@ -28,20 +28,27 @@
 //    operand = 16 k x 32 rows m of A, read from an A tile kept as in HBM ([m][k]).
 //    In the accumulator a lane holds one row m and, per block, 16 columns n in
 //    runs of 4, so the result leaves through LDS as whole 128-byte rows.
-//  * Each wave owns a quarter of the tile, WM x WN blocks (2 x 2 or 4 x 2):
-//    WM * WN MFMAs per 16-k step, each W operand used WM times and each A
-//    operand WN times.
+//  * The waves form a 2 x GN grid over the tile, each wave WM x WN blocks
+//    (2 x 2 or 4 x 2): WM * WN MFMAs per 16-k step, each W operand used WM
+//    times and each A operand WN times.
 //  * HBM -> LDS copies without registers (buffer_load ... lds), 16-byte chunks
 //    XOR-swizzled by the row so that the operand reads are free of bank
 //    conflicts; a ring of three buffers with two tiles in flight and one
-//    barrier per tile.  48 KiB of LDS (three workgroups per CU) or 72 KiB (two).
+//    barrier per tile, the k loop unrolled over the ring.  48 KiB of LDS
+//    (three workgroups per CU) or 128 KiB (one; its output stage is the
+//    largest part).
 //  * Bounded buffer descriptors: rows of A past M read 0, stores past M or past
 //    a product's N are dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sdpa_kernels.h"
 
+#ifndef SDPA_GEMM_BIG_GN
+#define SDPA_GEMM_BIG_GN 4         // waves along n in the large tile (2: 4 waves, 4: 8 waves)
+#endif
 #ifndef SDPA_GEMM_BIG_TILES
 #define SDPA_GEMM_BIG_TILES 1024   // 256 x 128 tiles from this many on (else 128 x 128)
 #endif
@@ -57,14 +64,14 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 32;
-constexpr int kWaves = 4;
 constexpr int kBuffers = 3;
 
-// Tile shape: the 4 waves form a 2 x 2 grid, each wave WM x WN blocks of 32 x 32
-// (rows m x columns n); the workgroup tile is BM x BN = 64*WM x 64*WN.
-template <int WM, int WN>
+// Tile shape: the waves form a 2 x GN grid (m x n), each wave WM x WN blocks of
+// 32 x 32; the workgroup tile is BM x BN = 64*WM x 32*GN*WN.
+template <int WM, int WN, int GN>
 struct Tile {
-    static constexpr int BM = 64 * WM, BN = 64 * WN;
+    static constexpr int kWaves = 2 * GN;
+    static constexpr int BM = 64 * WM, BN = 32 * GN * WN;
     static constexpr int kATileElems = BM * BK;     // [BM m][32 k]: 64-byte rows
     static constexpr int kWTileElems = BK * BN;     // [32 k][BN n]: 2*BN-byte rows
     static constexpr int kBufElems = kATileElems + kWTileElems;
@@ -74,9 +81,9 @@ struct Tile {
     static constexpr int kCopiesPerWave = kAPerWave + kWPerWave;
     static constexpr int kWRowsPerSlice = 1024 / (2 * BN);
     static constexpr int kWChunks = BN / 8;         // 16-byte chunks per W row
-    static constexpr int kLdsElems = kBuffers * kBufElems;
+    static constexpr int kStageElems = kWaves * 32 * WM * 32 * WN;   // output stage
+    static constexpr int kLdsElems = kBuffers * kBufElems > kStageElems ? kBuffers * kBufElems : kStageElems;
     static_assert(kASlices % kWaves == 0 && kWSlices % kWaves == 0, "even copy split");
-    static_assert(kWaves * 32 * WM * 32 * WN <= kLdsElems, "output stage fits in LDS");
 };
 
 constexpr uint32_t kNoOffset = 0x7FFFFFF0u;     // past every descriptor bound: read 0 / store dropped
@@ -126,19 +133,20 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes)
                                              kBufferRsrcWord3);
 }
 
-template <int AMODE, int CMODE, int WM, int WN>
-__global__ __launch_bounds__(kWaves * 64)
+template <int AMODE, int CMODE, int WM, int WN, int GN>
+__global__ __launch_bounds__(2 * GN * 64)
 __attribute__((amdgpu_waves_per_eu(WM * WN > 4 ? 2 : 3, WM * WN > 4 ? 2 : 3)))
 void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments segs)
 {
-    using T = Tile<WM, WN>;
+    using T = Tile<WM, WN, GN>;
+    constexpr int kWaves = T::kWaves;
     constexpr int BM = T::BM, BN = T::BN, kATileElems = T::kATileElems, kBufElems = T::kBufElems;
     __shared__ __attribute__((aligned(16))) uint16_t lds[T::kLdsElems];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, g = lane >> 5;
-    const int wm = wave & 1, wn = wave >> 1;      // the wave's quarter: 32*WM x 32*WN
+    const int wm = wave & 1, wn = wave >> 1;      // the wave's part: 32*WM x 32*WN
 
     // Tile of this workgroup: each XCD (workgroup w goes to XCD w % 8) takes a
     // contiguous run of items, n fastest, so the workgroups reading one row
@@ -243,17 +251,18 @@ void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
 
-    issue(0, 0);
-    if (n_k > 1) issue(1, 1);
-    for (int t = 0; t < n_k; ++t) {
+    // One k-tile in LDS buffer BUF = t % 3 (instantiated per buffer, so that
+    // every LDS operand address is a register plus an immediate).
+    auto tile = [&](int t, auto buf_tag) {
+        constexpr int BUF = decltype(buf_tag)::value;
         // Tile t has landed once at most tile t+1's copies are outstanding; the
         // barrier publishes it and retires every wave's reads of tile t-1, whose
         // buffer takes tile t+2.
         if (t + 1 < n_k) __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::kCopiesPerWave));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __syncthreads();
-        if (t + 2 < n_k) issue(t + 2, (t + 2) % kBuffers);
-        const char *As = (const char *)(lds + (t % kBuffers) * kBufElems);
+        if (t + 2 < n_k) issue(t + 2, (BUF + 2) % kBuffers);
+        const char *As = (const char *)(lds + BUF * kBufElems);
         const char *Ws = As + kATileElems * 2;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -273,7 +282,23 @@ void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments
 #pragma unroll
                 for (int mb = 0; mb < WM; ++mb) acc[nb][mb] = mfma32(aop[nb], bop[mb], acc[nb][mb]);
         }
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using B2 = std::integral_constant<int, 2>;
+
+    issue(0, 0);
+    if (n_k > 1) issue(1, 1);
+    // Unrolled over the ring (a branch on t % 3 per tile made the register
+    // allocator copy the accumulators at every join: 6x slower).
+    int t = 0;
+    for (; t + 2 < n_k; t += 3) {
+        tile(t, B0{});
+        tile(t + 1, B1{});
+        tile(t + 2, B2{});
     }
+    if (t < n_k) tile(t++, B0{});
+    if (t < n_k) tile(t++, B1{});
 
     // ---- epilogue: the wave's quarter through LDS (rows m of 64*WN bytes, chunks
     // XOR-swizzled by the row within each group of 8), then 16-byte stores of
@@ -318,11 +343,12 @@ void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments
 }
 
 // Tile counts of one shape, then the launch.
-template <int WM, int WN>
+template <int WM, int WN, int GN>
 hipError_t launch_shape(const void *A, int a_mode, GemmShape shape, GemmSegments segs,
                         int c_mode, hipStream_t stream)
 {
-    using T = Tile<WM, WN>;
+    using T = Tile<WM, WN, GN>;
+    constexpr int kWaves = T::kWaves;
     shape.n_mtiles = (uint32_t)((shape.M + T::BM - 1) / T::BM);
     segs.n_ntiles = 0;
     for (int i = 0; i < segs.count; ++i) {
@@ -332,13 +358,13 @@ hipError_t launch_shape(const void *A, int a_mode, GemmShape shape, GemmSegments
     const uint32_t grid = shape.n_mtiles * segs.n_ntiles;
     if (grid == 0) return hipSuccess;
     if (a_mode == 0 && c_mode == 1)
-        hipLaunchKernelGGL((proj_gemm_kernel<0, 1, WM, WN>), dim3(grid), dim3(kWaves * 64), 0, stream,
+        hipLaunchKernelGGL((proj_gemm_kernel<0, 1, WM, WN, GN>), dim3(grid), dim3(kWaves * 64), 0, stream,
                            (const uint16_t *)A, shape, segs);
     else if (a_mode == 1 && c_mode == 0)
-        hipLaunchKernelGGL((proj_gemm_kernel<1, 0, WM, WN>), dim3(grid), dim3(kWaves * 64), 0, stream,
+        hipLaunchKernelGGL((proj_gemm_kernel<1, 0, WM, WN, GN>), dim3(grid), dim3(kWaves * 64), 0, stream,
                            (const uint16_t *)A, shape, segs);
     else if (a_mode == 0 && c_mode == 0)
-        hipLaunchKernelGGL((proj_gemm_kernel<0, 0, WM, WN>), dim3(grid), dim3(kWaves * 64), 0, stream,
+        hipLaunchKernelGGL((proj_gemm_kernel<0, 0, WM, WN, GN>), dim3(grid), dim3(kWaves * 64), 0, stream,
                            (const uint16_t *)A, shape, segs);
     else
         return hipErrorInvalidValue;
@@ -347,12 +373,15 @@ hipError_t launch_shape(const void *A, int a_mode, GemmShape shape, GemmSegments
 
 }  // namespace
 
-// Tile shape by problem size: 256 x 128 tiles (two workgroups per CU, 0.75 KiB
-// of LDS reads per MFMA instead of 1 KiB) once there are at least 1024 of them;
-// smaller products keep 128 x 128 tiles (three workgroups per CU, twice as many
-// tiles to spread).  Measured on MI355X: 32768 x 1024 x 3072 took 224 us with
-// 256 x 128 tiles and 251 us with 128 x 128; 16384 x 512 x 1536 (768 large
-// tiles) 38.1 us against 36.4 us.
+// Tile shape by problem size: once there would be at least 1024 tiles of
+// 256 x 128, one 8-wave workgroup per CU on 256 x 256 tiles (each wave 4 x 2
+// blocks: 0.75 KiB of LDS reads per MFMA instead of 1 KiB, and each A and W
+// tile copied into LDS serves twice the columns); smaller products keep
+// 128 x 128 tiles (three 4-wave workgroups per CU, more tiles to spread).
+// Measured on MI355X: 32768 x 1024 x 3072 took 251 us on 128 x 128 tiles,
+// 224 us on 256 x 128 (4 waves) and 209 us on 256 x 256 (8 waves);
+// 16384 x 512 x 1536 (768 tiles of 256 x 128) 36.4 us on 128 x 128 tiles
+// against 38.1 us on 256 x 128.
 hipError_t launch_proj_gemm(const void *A, int a_mode, const GemmShape &shape,
                             const GemmSegments &segs, int c_mode, hipStream_t stream)
 {
@@ -360,8 +389,8 @@ hipError_t launch_proj_gemm(const void *A, int a_mode, const GemmShape &shape,
     for (int i = 0; i < segs.count; ++i) big_tiles += (segs.seg[i].N + 127) / 128;
     big_tiles *= (shape.M + 255) / 256;
     if (big_tiles >= SDPA_GEMM_BIG_TILES)
-        return launch_shape<4, 2>(A, a_mode, shape, segs, c_mode, stream);
-    return launch_shape<2, 2>(A, a_mode, shape, segs, c_mode, stream);
+        return launch_shape<4, 2, SDPA_GEMM_BIG_GN>(A, a_mode, shape, segs, c_mode, stream);
+    return launch_shape<2, 2, 2>(A, a_mode, shape, segs, c_mode, stream);
 }
 
 }  // namespace sdpa

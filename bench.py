@@ -354,6 +354,32 @@ def main():
         torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
+
+    # Distribution of single launches (after the timed window; not part of
+    # `value`): each step bracketed by its own pair of events on the launch
+    # stream.  And, for workloads timed on rotated input sets (cold caches),
+    # the same launches repeated on one set: the warm-cache figure.
+    def per_launch(n_launch, fixed_set):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_launch)]
+        for n, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            step(0 if fixed_set else n)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+
+    def summary(us):
+        return {"median": us[len(us) // 2], "p10": us[len(us) // 10], "p90": us[(9 * len(us)) // 10],
+                "n": len(us)}
+
+    n_dist = min(args.steps, 200)
+    launch_us = summary(per_launch(n_dist, False))
+    warm = None
+    if rotate > 1:
+        wus = per_launch(n_dist, True)
+        warm = {"launch_us": summary(wus), "value": flops / (wus[len(wus) // 2] * 1e-6) / 1e12,
+                "unit": "TFLOP/s", "note": "one input set reused: inputs warm in the 256 MB cache"}
     # One kernel launch per step (decode: the split kernel and its merge),
     # launched back to back on this stream: the average launch duration is the
     # event window over the launch count.
@@ -407,6 +433,8 @@ def main():
         "frac_of_peak": value / PEAK_TFLOPS[c.dtype],
         "roofline": roof,
         "cpu_baseline": cpu,
+        "launch_us": launch_us,
+        "warm": warm,
         "wall_s_timed": wall,
     }
     print(json.dumps(rec), flush=True)

@@ -139,7 +139,6 @@ __attribute__((amdgpu_waves_per_eu(WM * WN > 4 ? 2 : 3, WM * WN > 4 ? 2 : 3)))
 void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments segs)
 {
     using T = Tile<WM, WN, GN>;
-    constexpr int kWaves = T::kWaves;
     constexpr int BM = T::BM, BN = T::BN, kATileElems = T::kATileElems, kBufElems = T::kBufElems;
     __shared__ __attribute__((aligned(16))) uint16_t lds[T::kLdsElems];
 
@@ -168,7 +167,6 @@ void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments
     // + j), lane L -> row 16*slice + L/4, physical chunk L%4 (logical chunk
     // L%4 ^ swz_a(row)).
     uint32_t aoff[T::kAPerWave];
-    int64_t arow_base[T::kAPerWave];   // AMODE 1: element offset of the row's (b, i) in head 0
 #pragma unroll
     for (int j = 0; j < T::kAPerWave; ++j) {
         const int row = 16 * (T::kAPerWave * wave + j) + (lane >> 2);
@@ -176,12 +174,12 @@ void proj_gemm_kernel(const uint16_t *__restrict__ A, GemmShape sh, GemmSegments
         const int64_t m = m0 + row;
         if constexpr (AMODE == 0) {
             aoff[j] = (uint32_t)((row * K + lc * 8) * 2);    // relative to A + m0*K + k0
-            arow_base[j] = 0;
         } else {
-            // A(m, k) = heads[b][k / d][i][k % d], m = b * L + i
+            // A(m, k) = heads[b][k / d][i][k % d], m = b * L + i: the row's
+            // element offset in head 0, relative to the tile's head and k
             const int64_t b = m / sh.La, i = m % sh.La;
-            arow_base[j] = (b * sh.Ha * sh.La + i) * sh.da;
-            aoff[j] = m < M ? (uint32_t)((arow_base[j] + lc * 8) * 2) : kNoOffset;
+            const int64_t row_base = (b * sh.Ha * sh.La + i) * sh.da;
+            aoff[j] = m < M ? (uint32_t)((row_base + lc * 8) * 2) : kNoOffset;
         }
     }
     // W tile: copy j of this wave fills rows R*slice .. +R-1 (k; R = 1024 / (2*BN)

@@ -100,9 +100,10 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
                             int64_t d_k, int64_t d_v, sdpa_dtype dtype, hipStream_t s,
                             int64_t radius = -1)
 {
-    // A radius that reaches every key restricts nothing: same kernels, same
-    // result as unrestricted attention.
-    if (radius >= Lq || radius >= Lk) radius = -1;
+    // A radius that reaches every (query, key) pair restricts nothing: the
+    // largest |i - j| is max(Lq, Lk) - 1.  Then the unrestricted kernels run
+    // (the same result as sdpa_forward, bit for bit).
+    if (radius >= Lq - 1 && radius >= Lk - 1) radius = -1;
     // Lk == 0 needs no special case: both kernels then stage no key tile and
     // write 0 for every row (no legal connection).
     if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128)) {

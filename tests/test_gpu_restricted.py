@@ -52,6 +52,10 @@ CASES = [
     (2, 2, 300, 900, 64, False, [900, 400], 80),     # Lq < Lk
     (2, 2, 900, 300, 64, False, [300, 211], 80),     # Lq > Lk: late rows see no key
     (2, 2, 900, 300, 64, True, None, 40),
+    (2, 2, 10, 1000, 64, False, [1000, 600], 10),    # radius >= Lq but < Lk: still restricts
+    (2, 2, 1000, 10, 64, False, None, 10),           # radius >= Lk but < Lq
+    (1, 2, 100, 700, 64, False, None, 150),
+    (2, 2, 10, 1000, 16, False, None, 10),
     (1, 3, 1, 1, 64, False, None, 0),
     (1, 1, 65, 65, 64, False, None, 2),
     (2, 2, 1000, 1000, 32, False, [1000, 555], 70),
@@ -101,22 +105,23 @@ def test_restricted_generic_kernel(case, dtype):
 
 
 def test_restricted_wide_radius_is_forward():
-    """radius >= max(Lq, Lk) restricts nothing: exactly sdpa_forward's result;
-    radius = L - 1 (band kernel) agrees within the bars."""
+    """radius >= max(Lq, Lk) - 1 restricts nothing: exactly sdpa_forward's result;
+    radius = L - 2 (band kernel, one pair excluded per corner) agrees with the
+    oracle within the bars."""
     B, H, L = 2, 2, 300
     q, k, v, _ = workloads.draw(B, H, L, L, 64, 64, dtype="bf16", seed=5)
     dq, dk, dv = (to_dev(a, torch.bfloat16) for a in (q, k, v))
     announce("restricted wide radius")
     for causal in (False, True):
         f = sdpa.forward(dq, dk, dv, causal=causal)
-        r = sdpa.restricted(dq, dk, dv, L, causal=causal)
+        r = sdpa.restricted(dq, dk, dv, L - 1, causal=causal)
         r2 = sdpa.restricted(dq, dk, dv, 10 ** 12, causal=causal)
-        b = sdpa.restricted(dq, dk, dv, L - 1, causal=causal)
+        b = sdpa.restricted(dq, dk, dv, L - 2, causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(f.view(torch.int16), r.view(torch.int16))
         assert torch.equal(f.view(torch.int16), r2.view(torch.int16))
-        ref = oracle.attention(q, k, v, causal=causal)
-        assert_parity(b.float().cpu().numpy(), ref, v, "bf16", "radius L-1")
+        ref = oracle.attention(q, k, v, causal=causal, radius=L - 2)
+        assert_parity(b.float().cpu().numpy(), ref, v, "bf16", "radius L-2")
 
 
 def test_restricted_negative_radius_raises():

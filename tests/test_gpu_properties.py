@@ -99,7 +99,8 @@ def test_causal_row0_is_first_value_exactly(dtype):
     assert np.array_equal(got[:, :, 0], v[:, :, 0].astype(np.float64))
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 32), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 32), ("bf16", 16), ("bf16", 128),
+                                     ("f32", 64)])
 def test_padding_contents_do_not_matter(dtype, d):
     """Key/value rows j >= len_b filled with NaN and huge values change nothing."""
     B, H, Lq, Lk = 3, 2, 150, 200
@@ -147,7 +148,7 @@ def test_deterministic_and_fully_written(name):
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 8), ("bf16", 16)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 8), ("bf16", 16), ("bf16", 128)])
 def test_no_legal_key_gives_zero(dtype, d):
     q, k, v, _ = workloads.draw(3, 2, 70, 40, d, d, dtype=dtype, seed=71)
     announce("zero-length rows %s d=%d" % (dtype, d))
@@ -229,3 +230,38 @@ def test_lds_left_by_earlier_launches_never_reaches_result(causal):
             assert_parity(got, ref, v, "bf16", "after NaN-filled launches")
         else:
             assert np.array_equal(got, first)
+
+
+def test_restricted_and_multihead_deterministic_and_fully_written():
+    """The restricted and multi-head entry points: run to run bit for bit, every
+    output element written (outputs pre-filled with NaN), padding contents
+    irrelevant to the restricted path."""
+    dev = require_gpu()
+    q, k, v, _ = workloads.draw(2, 2, 500, 500, 64, 64, dtype="bf16", seed=71)
+    lengths = [500, 321]
+    dq, dk, dv = (to_dev(a, torch.bfloat16) for a in (q, k, v))
+    kl = torch.as_tensor(np.asarray(lengths, np.int32)).to(dev)
+    announce("restricted determinism")
+    o1 = torch.full((2, 2, 500, 64), float("nan"), dtype=torch.bfloat16, device=dev)
+    o2 = torch.full_like(o1, float("nan"))
+    sdpa.restricted(dq, dk, dv, 40, key_lengths=kl, causal=True, out=o1)
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, 321:] = np.nan
+    v2[1, :, 321:] = np.nan
+    sdpa.restricted(dq, to_dev(k2, torch.bfloat16), to_dev(v2, torch.bfloat16), 40, key_lengths=kl,
+                    causal=True, out=o2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o1).any()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+    xq, _, wq, wk, wv, wo, _ = workloads.draw_multihead(2, 130, 130, 128, 4, 32, 32, seed=72)
+    dx = to_dev(xq, torch.bfloat16)
+    w = [to_dev(a, torch.bfloat16) for a in (wq, wk, wv, wo)]
+    announce("multihead determinism")
+    m1 = torch.full((2, 130, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    m2 = torch.full_like(m1, float("nan"))
+    sdpa.multihead(dx, dx, *w, 4, causal=True, out=m1)
+    sdpa.multihead(dx, dx, *w, 4, causal=True, out=m2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(m1).any()
+    assert torch.equal(m1.view(torch.int16), m2.view(torch.int16))

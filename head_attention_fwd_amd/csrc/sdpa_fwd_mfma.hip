@@ -94,6 +94,9 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #ifndef SDPA_SPLIT_KEY_BLOCKS
 #define SDPA_SPLIT_KEY_BLOCKS 1   // 32-key blocks per LDS tile of the key-split kernel
 #endif
+#ifndef SDPA_SHORT_CAUSAL_KEYS
+#define SDPA_SHORT_CAUSAL_KEYS 512   // d = 64 causal launches up to this many keys take 32-key tiles
+#endif
 #ifndef SDPA_CAUSAL_HEAD_GROUP
 #define SDPA_CAUSAL_HEAD_GROUP 4  // causal order: heads per group on an XCD (0: all of its heads)
 #endif
@@ -101,10 +104,11 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 #define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget at D = 64: 3 waves per SIMD
 #endif
 // Waves per SIMD the register budget is set for, by head size: D = 128 needs
-// 64 accumulator and 32 Q-operand registers (2 waves), D = 32 and D = 16 fit 4.
-template <int D>
+// 64 accumulator and 32 Q-operand registers (2 waves), D = 32 and D = 16 fit 4;
+// D = 64 with 32-key tiles (one score block in flight) fits 4 as well.
+template <int D, int NB = 2>
 struct Occupancy {
-    static constexpr int kWaves = D >= 128 ? 2 : (D >= 64 ? SDPA_MFMA_WAVES_PER_SIMD : 4);
+    static constexpr int kWaves = D >= 128 ? 2 : (D >= 64 ? (NB == 1 ? 4 : SDPA_MFMA_WAVES_PER_SIMD) : 4);
 };
 
 // 16-byte chunk swizzles of a row of D bf16 values (D/8 chunks), XORed into
@@ -935,7 +939,7 @@ __device__ __forceinline__ void attend_query_tile(
 //    heads fit the L2 together, and taking all of them at once balances best.
 template <int NW, int NB, int D>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves))) void sdpa_fwd_mfma_kernel(
+__attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::kWaves))) void sdpa_fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
@@ -1116,6 +1120,18 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    if constexpr (D == 64) {
+        // Causal self-attention over short key ranges: 32-key tiles at four
+        // waves per SIMD (24 KiB of LDS, 127 VGPRs), so that every query tile of
+        // the base model's decoder is resident at once, and the tiles that
+        // cross the diagonal are half as long.
+        if (causal && Lk <= SDPA_SHORT_CAUSAL_KEYS) {
+            hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, 1, D>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0, stream,
+                               (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths, causal,
+                               (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D>), dim3(n_qtiles * n_bh),
                        dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
                        (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,

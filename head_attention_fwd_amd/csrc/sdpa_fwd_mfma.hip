@@ -992,7 +992,7 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::k
 // is used.
 template <int NW, int NB, int D>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(Occupancy<D>::kWaves, Occupancy<D>::kWaves))) void sdpa_fwd_mfma_band_kernel(
+__attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::kWaves))) void sdpa_fwd_mfma_band_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     int64_t radius, uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
@@ -1145,7 +1145,10 @@ hipError_t launch_mfma_band_d(const void *Q, const void *K, const void *V, const
                               int64_t Lk, hipStream_t stream)
 {
     constexpr int NW = SDPA_MFMA_WAVES;
-    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 4);
+#ifndef SDPA_BAND_NB64
+#define SDPA_BAND_NB64 1   // d = 64: 32-key tiles at 4 waves per SIMD (finer band edges)
+#endif
+    constexpr int NB = D >= 128 ? 1 : (D == 64 ? SDPA_BAND_NB64 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 4));
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);

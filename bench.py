@@ -219,7 +219,13 @@ def main():
                                 radius=c.radius)
         nbytes = perfmodel.min_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
                                      elem=2 if c.dtype == "bf16" else 4, radius=c.radius)
-    hbm_bound = flops / nbytes < (PEAK_TFLOPS[c.dtype] * 1e12) / (PEAK_HBM_GBS * 1e9)
+    # Arithmetic of the path: the matrix cores (bf16 products, fp32 sums) for
+    # bf16 with d_k = d_v in {16, 32, 64, 128} (and the decode and multi-head
+    # entry points); fp32 on the vector units otherwise.
+    mfma_path = c.entry in ("decode", "multihead") or (
+        c.dtype == "bf16" and c.d_k == c.d_v and c.d_k in (16, 32, 64, 128))
+    arith = "bf16" if mfma_path else "f32"
+    hbm_bound = flops / nbytes < (PEAK_TFLOPS[arith] * 1e12) / (PEAK_HBM_GBS * 1e9)
 
     rotate = args.rotate
     if rotate <= 0:
@@ -393,20 +399,20 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_TFLOPS[c.dtype],
-                "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_TFLOPS[c.dtype],
-                "traffic": traffic}
+        roof = {"bound": "mfma" if mfma_path else "alu", "achieved": achieved_tflops,
+                "peak": PEAK_TFLOPS[arith], "unit": "TFLOP/s",
+                "frac": achieved_tflops / PEAK_TFLOPS[arith], "traffic": traffic}
     if c.entry == "decode":
         roof["kernel"] = "sdpa_split_mfma_d64_kernel + sdpa_split_merge_d64_kernel"
     elif c.entry == "multihead":
         roof["kernel"] = ("whole step: projection GEMMs (proj_gemm_kernel) + attention "
                           "(sdpa_fwd_mfma_kernel); per-kernel split in the rocprofv3 summary")
     elif c.entry == "restricted":
-        roof["kernel"] = ("sdpa_fwd_mfma_band_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
-                                                           c.d_k in (16, 32, 64, 128)) else "sdpa_fwd_generic_kernel")
+        roof["kernel"] = ("sdpa_fwd_mfma_band_kernel" if mfma_path else
+                          "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 128 else "sdpa_fwd_generic_kernel")
     else:
-        roof["kernel"] = ("sdpa_fwd_mfma_kernel" if (c.dtype == "bf16" and c.d_k == c.d_v and
-                                                      c.d_k in (16, 32, 64, 128)) else "sdpa_fwd_generic_kernel")
+        roof["kernel"] = ("sdpa_fwd_mfma_kernel" if mfma_path else
+                          "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 128 else "sdpa_fwd_generic_kernel")
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
     roof["kernel_ms"] = kern_ms
@@ -421,7 +427,7 @@ def main():
         "timing": "hip graph of the timed steps" if use_graph else "back-to-back launches",
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": c.dtype, "data": "synthetic",
+        "dtype": arith, "data": "synthetic",
         "config": {"workload": c.name, "description": c.description, "entry": fn_name,
                    "B": c.B, "h": c.H,
                    "Lq": c.Lq, "Lk": c.Lk, "d_k": c.d_k, "d_v": c.d_v, "causal": c.causal,
@@ -430,7 +436,7 @@ def main():
                    "radius": c.radius, "d_model": c.d_model,
                    "self_attention": c.self_attention if c.entry == "multihead" else None,
                    "input_sets": rotate},
-        "frac_of_peak": value / PEAK_TFLOPS[c.dtype],
+        "frac_of_peak": value / PEAK_TFLOPS[arith],
         "roofline": roof,
         "cpu_baseline": cpu,
         "launch_us": launch_us,

@@ -15,7 +15,8 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int64_t kMaxHeadDim = 128;
+constexpr int64_t kMaxHeadDim = 512;      // d_k, d_v of the attention entry points
+constexpr int64_t kMaxProjHeadDim = 128;  // d_k, d_v of sdpa_multihead_forward
 constexpr int64_t kMaxDim = INT32_MAX;
 // Workgroups of a 1-D launch: grid size in work-items must fit in 32 bits.
 constexpr int64_t kMaxWorkgroups = (int64_t)1 << 24;
@@ -60,8 +61,8 @@ sdpa_status check_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_
         !mul_ok(n, {B, H, Lk, d_v, elem}) || !mul_ok(n, {B, H, Lq, d_v, elem}))
         return SDPA_ERR_BAD_SHAPE;
     if (B * H > kMaxDim) return SDPA_ERR_BAD_SHAPE;
-    // Both kernels use at most ceil(Lq / 64) workgroups per head.
-    if (((Lq + 63) / 64) > kMaxWorkgroups / (B * H)) return SDPA_ERR_BAD_SHAPE;
+    // Every kernel uses at most ceil(Lq / 32) workgroups per head.
+    if (((Lq + 31) / 32) > kMaxWorkgroups / (B * H)) return SDPA_ERR_BAD_SHAPE;
     return SDPA_OK;
 }
 
@@ -168,7 +169,7 @@ sdpa_status mh_plan(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model, int64_t 
     if (B < 0 || Lq < 0 || Lk < 0 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1)
         return SDPA_ERR_BAD_SHAPE;
     if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
-    if (d_k > kMaxHeadDim || d_v > kMaxHeadDim || d_model % 32 != 0 || d_k % 8 != 0 ||
+    if (d_k > kMaxProjHeadDim || d_v > kMaxProjHeadDim || d_model % 32 != 0 || d_k % 8 != 0 ||
         d_v % 32 != 0)
         return SDPA_ERR_UNSUPPORTED;
     if (B > kMaxDim || Lq > kMaxDim || Lk > kMaxDim || d_model > kMaxDim || h > kMaxDim)

@@ -62,9 +62,9 @@ def call(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, causal=0, O=FAKE_O, B=2, H=2, Lq=16
     (dict(Lq=2**31), sdpa.SDPA_ERR_BAD_SHAPE),
     (dict(B=2**20, H=2**20), sdpa.SDPA_ERR_BAD_SHAPE),
     (dict(B=2**16, H=2**10, Lq=2**20, Lk=1, dk=1, dv=1), sdpa.SDPA_ERR_BAD_SHAPE),
-    (dict(dk=129), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(dv=256), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(dk=129, dtype=sdpa.SDPA_F32), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dv=513), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dk=513, dtype=sdpa.SDPA_F32), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(dtype=7), sdpa.SDPA_ERR_UNSUPPORTED),
     # out overlapping an input (byte ranges computed on the host)
     (dict(O=FAKE_Q), sdpa.SDPA_ERR_ALIAS),
@@ -124,7 +124,7 @@ def test_decode_workspace_bytes():
     assert ws(4, 16, 1, 0, 64, 64, bf) == 4 * 66 * 64   # no keys: one (empty) chunk
     # sizes the entry point rejects
     assert ws(-1, 16, 1, 8192, 64, 64, bf) == -1
-    assert ws(4, 16, 1, 8192, 129, 64, bf) == -1
+    assert ws(4, 16, 1, 8192, 513, 64, bf) == -1
     assert ws(4, 16, 1, 8192, 64, 64, 9) == -1
 
 
@@ -132,7 +132,7 @@ def test_decode_workspace_bytes():
     (dict(Q=0), sdpa.SDPA_ERR_NULL_POINTER),
     (dict(O=0), sdpa.SDPA_ERR_NULL_POINTER),
     (dict(B=-1), sdpa.SDPA_ERR_BAD_SHAPE),
-    (dict(dk=129), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(O=FAKE_Q), sdpa.SDPA_ERR_ALIAS),
     (dict(ws=0), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ws_bytes=1024), sdpa.SDPA_ERR_WORKSPACE),
@@ -168,7 +168,7 @@ def rcall(radius=3, **kw):
     (dict(Q=0), sdpa.SDPA_ERR_NULL_POINTER),
     (dict(O=0, radius=0), sdpa.SDPA_ERR_NULL_POINTER),
     (dict(Lk=-1), sdpa.SDPA_ERR_BAD_SHAPE),
-    (dict(dk=129), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(dtype=7), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(O=FAKE_V + 64), sdpa.SDPA_ERR_ALIAS),
 ])

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name", ["tiny_causal_f32", "base_encoder_bf16",
                                   "base_decoder_causal_bf16", "big_cross_bf16",
                                   "rowA_h4_d128_encoder_bf16", "rowA_h16_d32_encoder_bf16",
-                                  "rowA_h32_d16_encoder_bf16"])
+                                  "rowA_h32_d16_encoder_bf16", "rowA_h1_d512_encoder_bf16"])
 def test_config_full(name):
     x = workloads.generate(name)
     c = x.config
@@ -86,6 +86,12 @@ RAGGED += [
     # d = 64 causal: 32-key tiles up to 512 keys, 64-key tiles beyond
     (2, 2, 300, 512, 64, 64, True, [512, 129]),
     (2, 2, 300, 513, 64, 64, True, [513, 129]),
+    # head sizes 129 .. 512 (8 lanes per query row, 32 rows per workgroup)
+    (2, 2, 70, 90, 256, 256, True, None),
+    (2, 1, 100, 130, 512, 512, False, [130, 17]),
+    (2, 2, 33, 40, 200, 320, True, [40, 0]),
+    (3, 1, 65, 300, 512, 136, True, [300, 77, 1]),
+    (1, 1, 1, 5, 129, 512, False, None),
 ]
 
 
@@ -108,6 +114,8 @@ F32_CASES = [
     (2, 2, 65, 130, 64, 64, False, [129, 130]),
     (1, 1, 40, 33, 100, 128, True, None),
     (1, 1, 40, 33, 128, 40, False, [20]),
+    (1, 1, 40, 50, 512, 512, True, None),
+    (2, 1, 33, 17, 300, 129, False, [17, 5]),
 ]
 
 

@@ -173,7 +173,7 @@ def test_zero_keys_and_empty_calls():
 
 def test_error_paths_raise():
     dev = require_gpu()
-    q = torch.zeros(1, 1, 4, 256, device=dev, dtype=torch.bfloat16)
+    q = torch.zeros(1, 1, 4, 520, device=dev, dtype=torch.bfloat16)   # head size above 512
     with pytest.raises(sdpa.SdpaError) as ei:
         sdpa.forward(q, q, q)
     assert ei.value.status == sdpa.SDPA_ERR_UNSUPPORTED

@@ -90,6 +90,7 @@ def test_restricted_bf16(case):
     (2, 2, 130, 130, 64, 64, False, None, 20),
     (1, 2, 90, 120, 16, 48, False, [100], 7),
     (1, 1, 200, 200, 128, 40, True, None, 65),
+    (1, 2, 150, 150, 512, 512, False, [140], 20),
 ])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_restricted_generic_kernel(case, dtype):

@@ -89,6 +89,11 @@ CONFIGS = {
         "h = 32 heads of d_k = d_v = 16 (Table 3 row A)", "bf16",
         B=64, H=32, Lq=256, Lk=256, d_k=16, d_v=16, causal=False, key_len_range=(64, 256),
         scale=1.0, seed=15),
+    "rowA_h1_d512_encoder_bf16": Config(
+        "rowA_h1_d512_encoder_bf16", "encoder self-attention with key padding, "
+        "h = 1 head of d_k = d_v = 512 (Table 3 row A)", "bf16",
+        B=64, H=1, Lq=256, Lk=256, d_k=512, d_v=512, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=16),
     "long_causal_d128_bf16": Config(
         "long_causal_d128_bf16", "long-sequence causal self-attention, d_model = 1024 as "
         "h = 8 heads of d_k = d_v = 128, inputs scaled by 0.5", "bf16",
@@ -141,7 +146,8 @@ CONFIGS = {
 #: forward configurations, the other head sizes, then the decode steps.
 ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
          "big_cross_bf16", "long_causal_bf16", "rowA_h4_d128_encoder_bf16",
-         "rowA_h16_d32_encoder_bf16", "rowA_h32_d16_encoder_bf16", "long_causal_d128_bf16", "restricted_long_bf16",
+         "rowA_h16_d32_encoder_bf16", "rowA_h32_d16_encoder_bf16", "rowA_h1_d512_encoder_bf16",
+         "long_causal_d128_bf16", "restricted_long_bf16",
          "restricted_long_causal_bf16", "mha_base_encoder_bf16", "mha_big_cross_bf16",
          "mha_long_causal_bf16", "decode_base_bf16", "decode_long_bf16"]
 

@@ -20,16 +20,18 @@
 // (แบบจับต้องได้)", section on dividing by sqrt(d_k): [100,100,100] splits
 // like [0,0,0]).
 //
-// Head sizes 129 .. 512 (sdpa_fwd_wide_kernel; Table 3 row (A) of the first
-// page ends at h = 1, d_k = d_v = 512): a row's q and accumulator no longer
-// fit one lane, so 8 lanes share a query row, lane l holding dims
-// l*DL .. l*DL + DL-1 (DL = 32 or 64); 32 rows per 256-thread workgroup.  A
-// score is the sum of the 8 lanes' partial dot products (three xor shuffles
-// inside the group), after which all 8 lanes hold the same score and run the
-// same online softmax on their own dims.  K and V tiles are staged as fp32 with
-// each lane's chunk padded by 16 bytes, so that the 8 lanes' 16-byte reads of
-// one key row fall in distinct banks (the other rows of the wave read the same
-// addresses: broadcast).
+// Head sizes 129 .. 512 (sdpa_fwd_wide_kernel; Table 3 row (A) of page
+// "Attention Is All You Need/paper/es" ends at h = 1, d_k = d_v = 512): a
+// row's q and accumulator no longer fit one lane, so G = 8 (d <= 256) or 16
+// (d <= 512) lanes share a query row, lane l holding dims 32*l .. 32*l + 31;
+// 256 / G rows per 256-thread workgroup.  A score is the sum of the G lanes'
+// partial dot products (log2 G xor shuffles inside the group), after which all
+// G lanes hold the same score and run the same online softmax on their own
+// dims.  K and V tiles (16 or 8 keys) are staged as fp32 with each lane's
+// chunk padded by 16 bytes, so that the G lanes' 16-byte reads of one key row
+// fall in distinct banks (the other rows of the wave read the same addresses:
+// broadcast), and the next tile's rows are loaded into registers while the
+// current tile computes.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

@@ -15,8 +15,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int64_t kMaxHeadDim = 512;      // d_k, d_v of the attention entry points
-constexpr int64_t kMaxProjHeadDim = 128;  // d_k, d_v of sdpa_multihead_forward
+constexpr int64_t kMaxHeadDim = 512;
 constexpr int64_t kMaxDim = INT32_MAX;
 // Workgroups of a 1-D launch: grid size in work-items must fit in 32 bits.
 constexpr int64_t kMaxWorkgroups = (int64_t)1 << 24;
@@ -169,7 +168,7 @@ sdpa_status mh_plan(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model, int64_t 
     if (B < 0 || Lq < 0 || Lk < 0 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1)
         return SDPA_ERR_BAD_SHAPE;
     if (dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
-    if (d_k > kMaxProjHeadDim || d_v > kMaxProjHeadDim || d_model % 32 != 0 || d_k % 8 != 0 ||
+    if (d_k > kMaxHeadDim || d_v > kMaxHeadDim || d_model % 32 != 0 || d_k % 8 != 0 ||
         d_v % 32 != 0)
         return SDPA_ERR_UNSUPPORTED;
     if (B > kMaxDim || Lq > kMaxDim || Lk > kMaxDim || d_model > kMaxDim || h > kMaxDim)

@@ -141,7 +141,7 @@ sdpa_status sdpa_forward_restricted(const void *Q, const void *K, const void *V,
  * fp32 accumulation, the projected heads and the attention output rounded to
  * bf16 (nearest even), the result rounded to bf16.  No bias terms (the pages'
  * projections are matrices).  Supported: d_model % 32 == 0, d_k % 8 == 0,
- * d_v % 32 == 0, d_k, d_v <= 128, every array and each projected tensor below
+ * d_v % 32 == 0, d_k, d_v <= 512, every array and each projected tensor below
  * 2 GiB - 1 MiB (SDPA_ERR_UNSUPPORTED / SDPA_ERR_BAD_SHAPE otherwise).
  * Errors as sdpa_forward, plus SDPA_ERR_WORKSPACE (missing, too small, or
  * overlapping another buffer); out must not overlap an input.  Four kernels

@@ -214,7 +214,7 @@ def test_multihead_workspace_bytes():
     assert f(2, 16, 16, 48, 2, 32, 32, sdpa.SDPA_BF16) == -1     # d_model % 32
     assert f(2, 16, 16, 64, 2, 12, 32, sdpa.SDPA_BF16) == -1     # d_k % 8
     assert f(2, 16, 16, 64, 2, 32, 16, sdpa.SDPA_BF16) == -1     # d_v % 32
-    assert f(2, 16, 16, 64, 2, 256, 32, sdpa.SDPA_BF16) == -1    # d_k > 128
+    assert f(2, 16, 16, 64, 2, 520, 32, sdpa.SDPA_BF16) == -1    # d_k > 512
     assert f(-1, 16, 16, 64, 2, 32, 32, sdpa.SDPA_BF16) == -1
     assert f(1, 2**21, 2**21, 1024, 16, 64, 64, sdpa.SDPA_BF16) == -1   # tensors past 2 GiB
     assert f(0, 16, 16, 64, 2, 32, 32, sdpa.SDPA_BF16) == 0

@@ -58,6 +58,8 @@ CASES = [
     (3, 70, 130, 128, 4, 32, 32, False, [130, 1, 0], False),    # cross, padding, empty keys
     (1, 300, 300, 256, 2, 128, 128, True, None, True),          # d = 128 heads
     (2, 129, 129, 512, 8, 64, 64, False, [129, 64], True),      # base-model width, ragged rows
+    (2, 70, 70, 512, 1, 512, 512, True, [70, 33], True),        # Table 3 row (A): h = 1, d = 512
+    (2, 50, 90, 256, 2, 256, 128, False, [90, 5], False),       # wide heads, cross, d_k != d_v
     (1, 50, 50, 96, 3, 16, 32, False, None, True),              # d_k != d_v: generic attention
     (2, 1, 1, 64, 2, 32, 32, False, None, True),                # one position
     (1, 5, 300, 1024, 16, 64, 64, False, None, False),          # few queries, big-model width

@@ -60,8 +60,9 @@ sdpa_status check_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_
         !mul_ok(n, {B, H, Lk, d_v, elem}) || !mul_ok(n, {B, H, Lq, d_v, elem}))
         return SDPA_ERR_BAD_SHAPE;
     if (B * H > kMaxDim) return SDPA_ERR_BAD_SHAPE;
-    // Every kernel uses at most ceil(Lq / 32) workgroups per head.
-    if (((Lq + 31) / 32) > kMaxWorkgroups / (B * H)) return SDPA_ERR_BAD_SHAPE;
+    // Every kernel uses at most ceil(Lq / 16) workgroups per head (the wide
+    // kernel at d > 256: 16 query rows per workgroup).
+    if (((Lq + 15) / 16) > kMaxWorkgroups / (B * H)) return SDPA_ERR_BAD_SHAPE;
     return SDPA_OK;
 }
 

@@ -62,6 +62,8 @@ def call(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, causal=0, O=FAKE_O, B=2, H=2, Lq=16
     (dict(Lq=2**31), sdpa.SDPA_ERR_BAD_SHAPE),
     (dict(B=2**20, H=2**20), sdpa.SDPA_ERR_BAD_SHAPE),
     (dict(B=2**16, H=2**10, Lq=2**20, Lk=1, dk=1, dv=1), sdpa.SDPA_ERR_BAD_SHAPE),
+    # the wide kernel (d > 256) uses ceil(Lq / 16) workgroups per head: 2^24 + 1 is too many
+    (dict(B=1, H=1, Lq=2**28 + 1, Lk=1, dk=512, dv=512), sdpa.SDPA_ERR_BAD_SHAPE),
     (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(dv=513), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(dk=513, dtype=sdpa.SDPA_F32), sdpa.SDPA_ERR_UNSUPPORTED),

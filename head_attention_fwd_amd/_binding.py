@@ -172,6 +172,13 @@ def _check(q, k, v, key_lengths, out):
     return (B, H, Lq, Lk, d_k, d_v), dtype, key_lengths, out
 
 
+def _check_workspace(workspace, dev):
+    """A caller-given workspace: a contiguous tensor on the calls' device (its size in
+    bytes is checked by the library)."""
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+
+
 def _raise(st, entry):
     if st != SDPA_OK:
         msg = sdpa_status_str(st)
@@ -232,6 +239,8 @@ def multihead(xq, xkv, wq, wk, wv, wo, h: int, key_lengths=None, causal: bool = 
     """
     import torch
 
+    if int(h) < 1:
+        raise ValueError("h must be at least 1")
     if xq.dim() != 3 or xkv.dim() != 3:
         raise ValueError("xq and xkv must be [B, L, d_model]")
     B, Lq, dm = xq.shape
@@ -251,8 +260,9 @@ def multihead(xq, xkv, wq, wk, wv, wo, h: int, key_lengths=None, causal: bool = 
     if key_lengths is not None and not isinstance(key_lengths, torch.Tensor):
         key_lengths = torch.as_tensor(list(key_lengths), dtype=torch.int32, device=dev)
     if key_lengths is not None and (key_lengths.dtype != torch.int32 or key_lengths.device != dev
-                                    or tuple(key_lengths.shape) != (B,)):
-        raise ValueError("key_lengths must be an int32 [B] tensor on xq's device")
+                                    or tuple(key_lengths.shape) != (B,)
+                                    or not key_lengths.is_contiguous()):
+        raise ValueError("key_lengths must be a contiguous int32 [B] tensor on xq's device")
     if out is None:
         out = torch.empty((B, Lq, dm), dtype=torch.bfloat16, device=dev)
     elif tuple(out.shape) != (B, Lq, dm) or out.dtype != torch.bfloat16 or out.device != dev or \
@@ -263,6 +273,7 @@ def multihead(xq, xkv, wq, wk, wv, wo, h: int, key_lengths=None, causal: bool = 
         raise SdpaError(SDPA_ERR_UNSUPPORTED, "sizes rejected", "sdpa_multihead_forward")
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = sdpa_multihead_forward(xq.data_ptr(), xkv.data_ptr(), wq.data_ptr(), wk.data_ptr(),
@@ -292,6 +303,8 @@ def decode(q, k, v, key_lengths=None, out=None, workspace=None):
         raise SdpaError(SDPA_ERR_BAD_SHAPE, "sizes rejected", "sdpa_decode")
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_workspace(workspace, dev)
     ws_ptr = 0 if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):

@@ -102,6 +102,16 @@ def test_python_forward_rejects_bad_arguments_without_gpu():
         sdpa.forward(q.half(), q.half(), q.half())
 
 
+def test_python_multihead_rejects_bad_arguments_without_gpu():
+    import torch
+    x = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    w = torch.zeros(64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sdpa.multihead(x, x, w, w, w, w, 0)       # no heads
+    with pytest.raises(ValueError):
+        sdpa.multihead(x, x, w, w, w, w, 2)       # CPU tensors are refused, never computed
+
+
 # ---- sdpa_decode: the same host-side checks, plus the workspace
 
 def dcall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=2, H=2, Lq=1, Lk=128,

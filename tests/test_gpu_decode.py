@@ -103,7 +103,8 @@ def test_workspace_too_small_raises():
     assert e.value.status == sdpa.SDPA_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("dtype,d,Lq", [("f32", 64, 1), ("bf16", 32, 2), ("bf16", 64, 33)])
+@pytest.mark.parametrize("dtype,d,Lq", [("f32", 64, 1), ("bf16", 32, 2), ("bf16", 64, 33),
+                                     ("bf16", 128, 1), ("bf16", 512, 1)])
 def test_other_shapes_run_the_forward_kernels(dtype, d, Lq):
     """No split path: sdpa_decode must give exactly sdpa_forward(causal=0)."""
     B, H, Lk = 2, 2, 300

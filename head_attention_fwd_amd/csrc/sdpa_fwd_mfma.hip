@@ -1112,10 +1112,12 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
                          int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                          hipStream_t stream)
 {
-    constexpr int NW = SDPA_MFMA_WAVES;
-    // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB;
-    // D = 16: 128-key tiles, so that each wave copies one whole 1 KiB slice.
-    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 4);
+    // D = 16: 2-wave workgroups (64 query rows) with 64-key tiles, so that each
+    // wave copies one whole 1 KiB slice and, at 12 KiB of LDS and 98 VGPRs, a CU
+    // holds 8 of them (2048 slots; 4-wave workgroups with 128-key tiles: 1024).
+    constexpr int NW = D <= 16 ? 2 : SDPA_MFMA_WAVES;
+    // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB.
+    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 2);
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);

@@ -220,9 +220,12 @@ def main():
         nbytes = perfmodel.min_bytes(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
                                      elem=2 if c.dtype == "bf16" else 4, radius=c.radius)
     # Arithmetic of the path: the matrix cores (bf16 products, fp32 sums) for
-    # bf16 with d_k = d_v in {16, 32, 64, 128} (and the decode and multi-head
-    # entry points); fp32 on the vector units otherwise.
-    mfma_path = c.entry in ("decode", "multihead") or (
+    # bf16 with d_k = d_v in {16, 32, 64, 128} (restricted or not) or in
+    # {256, 512} (unrestricted), and the decode and multi-head entry points;
+    # fp32 on the vector units otherwise.
+    wide_mfma = (c.dtype == "bf16" and c.d_k == c.d_v and c.d_k in (256, 512)
+                 and c.entry != "restricted")
+    mfma_path = c.entry in ("decode", "multihead") or wide_mfma or (
         c.dtype == "bf16" and c.d_k == c.d_v and c.d_k in (16, 32, 64, 128))
     arith = "bf16" if mfma_path else "f32"
     hbm_bound = flops / nbytes < (PEAK_TFLOPS[arith] * 1e12) / (PEAK_HBM_GBS * 1e9)
@@ -410,6 +413,8 @@ def main():
     elif c.entry == "restricted":
         roof["kernel"] = ("sdpa_fwd_mfma_band_kernel" if mfma_path else
                           "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 128 else "sdpa_fwd_generic_kernel")
+    elif wide_mfma:
+        roof["kernel"] = "sdpa_fwd_mfma_wide_kernel"
     else:
         roof["kernel"] = ("sdpa_fwd_mfma_kernel" if mfma_path else
                           "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 128 else "sdpa_fwd_generic_kernel")

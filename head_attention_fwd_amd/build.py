@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libsdpa.so")
-SOURCES = ["sdpa_api.hip", "sdpa_fwd_generic.hip", "sdpa_fwd_mfma.hip", "sdpa_proj_gemm.hip"]
+SOURCES = ["sdpa_api.hip", "sdpa_fwd_generic.hip", "sdpa_fwd_mfma.hip", "sdpa_fwd_mfma_wide.hip",
+           "sdpa_proj_gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -114,6 +114,9 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
         return hip_status(sdpa::launch_mfma(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
                                             (int)d_k, s));
     }
+    if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 256 || d_k == 512) && radius < 0)
+        return hip_status(sdpa::launch_mfma_wide(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
+                                                 (int)d_k, s));
     return hip_status(sdpa::launch_generic(Q, K, V, key_lengths, causal ? 1 : 0, radius, out, B, H,
                                            Lq, Lk, (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
 }

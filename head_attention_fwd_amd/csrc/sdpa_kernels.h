@@ -27,6 +27,11 @@ hipError_t launch_mfma(const void *Q, const void *K, const void *V,
 
 // As launch_mfma, restricted self-attention: key j is legal for query i only
 // when |i - j| <= radius (radius >= 0).
+hipError_t launch_mfma_wide(const void *Q, const void *K, const void *V,
+                            const int32_t *key_lengths, int causal, void *out,
+                            int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
+                            hipStream_t stream);
+
 hipError_t launch_mfma_band(const void *Q, const void *K, const void *V,
                             const int32_t *key_lengths, int causal, int64_t radius, void *out,
                             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,

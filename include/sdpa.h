@@ -36,9 +36,10 @@
  * deterministic run to run.
  *
  * Supported sizes.  SDPA_BF16: 1 <= d_k, d_v <= 512 (d_k = d_v in {16, 32, 64,
- * 128} runs on the matrix cores: the head sizes of the base and big models,
- * §3.2.2, and of Table 3 row (A) at d_model = 512, whose last row, h = 1,
- * d_k = d_v = 512, runs on the fp32 vector units).  SDPA_F32: 1 <= d_k, d_v <= 512.
+ * 128, 256, 512} runs on the matrix cores: the head sizes of the base and big
+ * models, §3.2.2, and of Table 3 row (A) at d_model = 512, down to its last
+ * row, h = 1, d_k = d_v = 512; restricted attention at 256 and 512 runs on the
+ * fp32 vector units).  SDPA_F32: 1 <= d_k, d_v <= 512.
  * B*H <= 2^31 - 1,
  * Lq, Lk <= 2^31 - 1.  B, H, Lq or Lk equal to 0 is an empty call (SDPA_OK,
  * nothing launched).

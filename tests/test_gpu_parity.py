@@ -78,6 +78,8 @@ RAGGED = [
 # d = 16 uses 128-key tiles and half of each 32-row output block).
 for _d in (16, 32, 128):
     RAGGED += [(B, H, Lq, Lk, _d, _d, c, ln) for (B, H, Lq, Lk, dk, dv, c, ln) in RAGGED[:10]]
+for _d in (256, 512):
+    RAGGED += [(B, H, Lq, Lk, _d, _d, c, ln) for (B, H, Lq, Lk, dk, dv, c, ln) in RAGGED[:10]]
 RAGGED += [
     (2, 2, 70, 90, 32, 32, True, [50, 90]),
     (2, 2, 70, 90, 128, 128, False, [90, 3]),
@@ -86,9 +88,13 @@ RAGGED += [
     # d = 64 causal: 32-key tiles up to 512 keys, 64-key tiles beyond
     (2, 2, 300, 512, 64, 64, True, [512, 129]),
     (2, 2, 300, 513, 64, 64, True, [513, 129]),
-    # head sizes 129 .. 512 (8 lanes per query row, 32 rows per workgroup)
+    # d = 256 and 512: the matrix-core kernel for wide heads (16 rows per wave,
+    # 64 per workgroup, 32-key tiles)
     (2, 2, 70, 90, 256, 256, True, None),
     (2, 1, 100, 130, 512, 512, False, [130, 17]),
+    (2, 3, 160, 700, 256, 256, True, [700, 33]),
+    (2, 1, 129, 95, 512, 512, True, [95, 0]),
+    # other head sizes up to 512: fp32 vector kernel (8 or 16 lanes per query row)
     (2, 2, 33, 40, 200, 320, True, [40, 0]),
     (3, 1, 65, 300, 512, 136, True, [300, 77, 1]),
     (1, 1, 1, 5, 129, 512, False, None),
@@ -130,7 +136,7 @@ def test_ragged_f32(case):
     assert_parity(got, ref, v, "f32", str(case))
 
 
-@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256, 512])
 def test_long_keys_sampled_rows(d):
     """A long key sequence (32768 keys) on the matrix-core kernel, non-causal with
     padding, rows sampled for the oracle."""

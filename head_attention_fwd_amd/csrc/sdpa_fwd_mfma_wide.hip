@@ -33,15 +33,27 @@
 //    i % 4 of the 4-element rows addressed by lanes 4e + i / 4 (e = 0..3), so
 //    lanes 4e + j addressing dims 4j .. 4j+3 of key row k0 + e hand lane i the
 //    4 keys k0 .. k0+3 of dim i.
-//  * K and V rows sit in LDS as in HBM, their 16-byte chunks XORed with the
-//    row index mod 16 (the 16 rows read by one instruction then fall on
-//    distinct chunk positions).  Two buffers: the copy of tile t+1 (HBM
+//  * K and V rows sit in LDS as in HBM, the 16-byte chunk index of row r
+//    XORed with f(r) = 2 (r mod 8) + (r / 8 mod 2).  f is injective on 16 rows
+//    (the 16 K rows one half-wave reads at one chunk land on 16 distinct
+//    positions) and keeps bit 0 of the chunk index apart from its higher bits
+//    on 8 consecutive rows (the 8 V rows x 2 adjacent chunks one half-wave
+//    reads in a transposing read land on 16 distinct positions).  Two buffers: the copy of tile t+1 (HBM
 //    straight into LDS, buffer_load ... lds) runs while tile t is multiplied;
 //    one barrier per tile.  The copy's buffer descriptor ends at the key
 //    length, so rows past it read as 0.
-//  * Softmax online in base 2 (p = exp2(s log2(e)/sqrt(d_k) - m), m the row's
-//    running maximum in the same units); the accumulator is rescaled only in
-//    tiles where some row's maximum grows (a wave-uniform branch).  The row
+//  * The LDS operand reads of both products run kPF MFMA steps ahead of their
+//    use, with scheduling fences between steps so that the compiler does not
+//    hoist more of them (at D = 512 the registers are already full).  Each
+//    K or V byte read from LDS feeds 16 multiply-adds (one per query row of
+//    the wave), so the products are bound by LDS bandwidth at about half the
+//    matrix-core rate.
+//  * Softmax online in base 2: p = exp2(s log2(e)/sqrt(d_k) - m), with m a
+//    reference maximum of the row in the same units, moved to the row's
+//    current maximum only when that exceeds m by more than kTau (so p stays
+//    below 2^kTau, harmless in fp32 and bf16); the common shift cancels in the
+//    final division by the row sum.  After the first tile the rescale of the
+//    accumulator (a wave-uniform branch) is rarely taken.  The row
 //    sum adds the bf16-rounded weights, i.e. the weights used in P V.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -63,6 +75,11 @@ constexpr int kWaves = 4;
 constexpr int kBM = 16 * kWaves;        // query rows per workgroup
 constexpr int kBN = 32;                 // keys per tile
 constexpr int kRsrcWord3 = 0x00020000;  // raw (stride 0) dword buffer access
+constexpr int kPF = 2;                  // LDS operand reads issued this many MFMA steps ahead
+constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+
+// Chunk swizzle of LDS row r (see the header comment).
+__device__ inline int chunk_xor(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 {
@@ -175,13 +192,13 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     const uint16_t *Kh = K + (int64_t)bh * Lk * D;
     const uint16_t *Vh = V + (int64_t)bh * Lk * D;
     // Copy offsets: lane L of slice j fills LDS row pos, physical chunk pc,
-    // which holds the row's chunk pc ^ (pos % 16).
+    // which holds the row's chunk pc ^ chunk_xor(pos).
     uint32_t coff[kSlicesPerWave];
 #pragma unroll
     for (int j = 0; j < kSlicesPerWave; ++j) {
         const int pos = kRowsPerSlice * (wave * kSlicesPerWave + j) + lane / kChunks;
         const int pc = lane % kChunks;
-        coff[j] = (uint32_t)(pos * kRowBytes + ((pc ^ (pos & 15)) << 4));
+        coff[j] = (uint32_t)(pos * kRowBytes + ((pc ^ chunk_xor(pos)) << 4));
     }
     auto issue = [&](int t) {
         const int64_t kv0 = (int64_t)t * kBN;
@@ -200,24 +217,37 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
         }
     };
 
-    // LDS operand offsets (bytes, before the per-step chunk XOR).
-    // K: row col (+16 for the second block), chunk 4s + 2h + grp/2 of step s,
-    // half grp % 2.
-    const int kxor_hi = (col & 12) << 4;                               // XOR on bits 6..7
+    // LDS operand offsets (bytes).  K, step s (dims 32s .. 32s+31): lane
+    // 16 grp + col reads row col (and col + 16 for the second block), chunks
+    // 4s + grp/2 and 4s + 2 + grp/2, half grp % 2.  The row's XOR splits into
+    // bits 0..1 (a per-lane constant) and bits 2..3, which permute the four
+    // steps s = 4i .. 4i+3: kofs[s % 4] + 256 (s / 4) is the address.
+    const int kx = chunk_xor(col);                                     // rows col and col + 16
     const uint32_t kbase = (uint32_t)(col * kRowBytes + 8 * (grp & 1));
-    const uint32_t klo0 = (uint32_t)((((grp >> 1)) ^ (col & 3)) << 4);
-    const uint32_t klo1 = (uint32_t)(((2 + (grp >> 1)) ^ (col & 3)) << 4);
-    // V: lane 16 grp + 4e + j addresses key row 4 grp + e (+16 for keys
-    // 16 .. 31), dims 16 db + 4j, i.e. chunk 2 db + j/2, half j % 2.
+    const uint32_t klo0 = (uint32_t)((((grp >> 1)) ^ (kx & 3)) << 4);
+    const uint32_t klo1 = (uint32_t)(((2 + (grp >> 1)) ^ (kx & 3)) << 4);
+    uint32_t kofs[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kofs[j][0] = kbase + klo0 + (uint32_t)(64 * (j ^ (kx >> 2)));
+        kofs[j][1] = kbase + klo1 + (uint32_t)(64 * (j ^ (kx >> 2)));
+    }
+    // V, block db (dims 16 db .. 16 db + 15): lane 16 grp + 4e + j addresses
+    // key row 4 grp + e (+16 for keys 16 .. 31), dims 16 db + 4j, i.e. chunk
+    // 2 db + j/2, half j % 2; the XOR's bit 0 is a per-lane constant, its bits
+    // 1..3 permute the eight blocks db = 8i .. 8i+7: vofs[db % 8] + 256 (db / 8).
     const int vrow = 4 * grp + ((lane >> 2) & 3);
     const int vj = lane & 3;
-    const uint32_t vbase = (uint32_t)(vrow * kRowBytes + 8 * (vj & 1) + ((((vj >> 1) ^ (vrow & 1))) << 4));
-    const int vxor_hi = (vrow & 14) << 4;                              // XOR on bits 5..7
+    const int vx = chunk_xor(vrow);                                    // rows vrow and vrow + 16
+    const uint32_t vbase = (uint32_t)(vrow * kRowBytes + 8 * (vj & 1) + ((((vj >> 1) ^ (vx & 1))) << 4));
+    uint32_t vofs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vofs[j] = vbase + (uint32_t)(32 * (j ^ ((vx >> 1) & 7)));
 
     f32x4_t o[kDB];
 #pragma unroll
     for (int i = 0; i < kDB; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;   // running maximum (scaled, base 2), same in the 4 lane groups
+    float m_run = -INFINITY;   // reference maximum (scaled, base 2), same in the 4 lane groups
     float l_run = 0.f;         // this lane's share of the row sum
 
     if (n_tiles > 0) issue(0);
@@ -228,17 +258,27 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
         const char *kb = (const char *)(lds + (t & 1) * 2 * kTileElems);
         const char *vb = kb + 2 * kTileElems;
 
-        // S^T of the two 16-key blocks
+        // S^T of the two 16-key blocks; K operands read kPF steps ahead
+        auto kread = [&](int s, u32x4_t &ra, u32x4_t &rb) {
+            const char *p0 = kb + kofs[s & 3][0] + 256 * (s >> 2);
+            const char *p1 = kb + kofs[s & 3][1] + 256 * (s >> 2);
+            const u32x2_t a0 = lds_read_b64((const uint16_t *)p0);
+            const u32x2_t a1 = lds_read_b64((const uint16_t *)p1);
+            const u32x2_t b0 = lds_read_b64((const uint16_t *)(p0 + 16 * kRowBytes));
+            const u32x2_t b1 = lds_read_b64((const uint16_t *)(p1 + 16 * kRowBytes));
+            ra = u32x4_t{a0.x, a0.y, a1.x, a1.y};
+            rb = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+        };
         f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+        u32x4_t ka[kPF + 1], kc[kPF + 1];
+#pragma unroll
+        for (int s = 0; s < kPF; ++s) kread(s, ka[s], kc[s]);
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
-            const uint32_t hi = (uint32_t)((64 * s) ^ kxor_hi);
-            const u32x2_t a0 = lds_read_b64((const uint16_t *)(kb + kbase + hi + klo0));
-            const u32x2_t a1 = lds_read_b64((const uint16_t *)(kb + kbase + hi + klo1));
-            const u32x2_t b0 = lds_read_b64((const uint16_t *)(kb + 16 * kRowBytes + kbase + hi + klo0));
-            const u32x2_t b1 = lds_read_b64((const uint16_t *)(kb + 16 * kRowBytes + kbase + hi + klo1));
-            s0 = mfma16(u32x4_t{a0.x, a0.y, a1.x, a1.y}, qf[s], s0);
-            s1 = mfma16(u32x4_t{b0.x, b0.y, b1.x, b1.y}, qf[s], s1);
+            if (s + kPF < kSteps) kread(s + kPF, ka[(s + kPF) % (kPF + 1)], kc[(s + kPF) % (kPF + 1)]);
+            s0 = mfma16(ka[s % (kPF + 1)], qf[s], s0);
+            s1 = mfma16(kc[s % (kPF + 1)], qf[s], s1);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // masks, row maximum, weights
@@ -256,7 +296,7 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool grow = mx > m_run;
+        const bool grow = mx > m_run + kTau;
         if (__builtin_amdgcn_ballot_w64(grow)) {
             // a row's first legal key has m_run = -inf: alpha = 0 (nothing to keep)
             const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
@@ -276,13 +316,21 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
             l_run += __builtin_bit_cast(float, pk[i] << 16) + __builtin_bit_cast(float, pk[i] & 0xffff0000u);
         const u32x4_t pb = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T; V operands read kPF blocks ahead
+        auto vread = [&](int db) {
+            const char *p = vb + vofs[db & 7] + 256 * (db >> 3);
+            const u32x2_t a0 = lds_read_tr((const uint16_t *)p);
+            const u32x2_t a1 = lds_read_tr((const uint16_t *)(p + 16 * kRowBytes));
+            return u32x4_t{a0.x, a0.y, a1.x, a1.y};
+        };
+        u32x4_t va[kPF + 1];
+#pragma unroll
+        for (int i = 0; i < kPF; ++i) va[i] = vread(i);
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-            const uint32_t off = vbase + (uint32_t)((32 * db) ^ vxor_hi);
-            const u32x2_t a0 = lds_read_tr((const uint16_t *)(vb + off));
-            const u32x2_t a1 = lds_read_tr((const uint16_t *)(vb + 16 * kRowBytes + off));
-            o[db] = mfma16(u32x4_t{a0.x, a0.y, a1.x, a1.y}, pb, o[db]);
+            if (db + kPF < kDB) va[(db + kPF) % (kPF + 1)] = vread(db + kPF);
+            o[db] = mfma16(va[db % (kPF + 1)], pb, o[db]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 

@@ -26,8 +26,8 @@
 //    4g + e (e < 4) and 16 + 4g + (e - 4) (e >= 4): the scores of a tile's two
 //    16-key blocks that a lane holds are then, rounded to bf16, exactly its B
 //    operand of O^T += V^T P^T over the tile's 32 keys, and P never leaves
-//    registers.  The same assignment orders the dims of each 32-dim step of
-//    the score product.
+//    registers.  In the score product the slots of lane group g are the 8
+//    consecutive dims 8g .. 8g+7 of each 32-dim step (one 16-byte read).
 //  * V^T (A operand, 16 dims x 32 keys) is read from row-major V in LDS with
 //    ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 //    i % 4 of the 4-element rows addressed by lanes 4e + i / 4 (e = 0..3), so
@@ -35,10 +35,11 @@
 //    4 keys k0 .. k0+3 of dim i.
 //  * K and V rows sit in LDS as in HBM, the 16-byte chunk index of row r
 //    XORed with f(r) = 2 (r mod 8) + (r / 8 mod 2).  f is injective on 16 rows
-//    (the 16 K rows one half-wave reads at one chunk land on 16 distinct
-//    positions) and keeps bit 0 of the chunk index apart from its higher bits
-//    on 8 consecutive rows (the 8 V rows x 2 adjacent chunks one half-wave
-//    reads in a transposing read land on 16 distinct positions).  Two buffers: the copy of tile t+1 (HBM
+//    (the 16 K rows that 16 lanes read at one chunk land on 16 distinct
+//    positions, 256 bytes, every bank twice) and keeps bit 0 of the chunk
+//    index apart from its higher bits on 4 consecutive rows (the 4 V rows x 2
+//    adjacent chunks that 16 lanes read in a transposing read land on 8
+//    distinct positions modulo 128 bytes).  Two buffers: the copy of tile t+1 (HBM
 //    straight into LDS, buffer_load ... lds) runs while tile t is multiplied;
 //    one barrier per tile.  The copy's buffer descriptor ends at the key
 //    length, so rows past it read as 0.
@@ -93,9 +94,9 @@ __device__ inline u32x2_t lds_read_tr(const uint16_t *p)
     return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p));
 }
 
-__device__ inline u32x2_t lds_read_b64(const uint16_t *p)
+__device__ inline u32x4_t lds_read_b128(const char *p)
 {
-    return *(const __attribute__((address_space(3))) u32x2_t *)(
+    return *(const __attribute__((address_space(3))) u32x4_t *)(
         (__attribute__((address_space(3))) const void *)p);
 }
 
@@ -172,21 +173,18 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     if (causal && q0 + kBM < kv_end) kv_end = q0 + kBM;
     const int n_tiles = (int)((kv_end + kBN - 1) / kBN);
 
-    // Q operand: the lane's query row, dims 32s + 4 grp .. +3 and
-    // 32s + 16 + 4 grp .. +3 of every step s; rows past Lq read 0.
+    // Q operand: the lane's query row, dims 32s + 8 grp .. +7 of every step s;
+    // rows past Lq read 0.
     u32x4_t qf[kSteps];
     {
         int64_t rows = Lq - q0w;
         rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
         const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(Q + ((int64_t)bh * Lq + q0w) * D), (short)0, (int)rows * kRowBytes, kRsrcWord3);
-        const uint32_t qoff = (uint32_t)(col * kRowBytes + 8 * grp);
+        const uint32_t qoff = (uint32_t)(col * kRowBytes + 16 * grp);
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-            const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff + 64 * s, 0, 0);
-            const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rq, qoff + 64 * s + 32, 0, 0);
-            qf[s] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        }
+        for (int s = 0; s < kSteps; ++s)
+            qf[s] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * s, 0, 0);
     }
 
     const uint16_t *Kh = K + (int64_t)bh * Lk * D;
@@ -218,20 +216,15 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     };
 
     // LDS operand offsets (bytes).  K, step s (dims 32s .. 32s+31): lane
-    // 16 grp + col reads row col (and col + 16 for the second block), chunks
-    // 4s + grp/2 and 4s + 2 + grp/2, half grp % 2.  The row's XOR splits into
-    // bits 0..1 (a per-lane constant) and bits 2..3, which permute the four
-    // steps s = 4i .. 4i+3: kofs[s % 4] + 256 (s / 4) is the address.
+    // 16 grp + col reads 16 bytes, chunk 4s + grp of row col (and col + 16 for
+    // the second block).  The row's XOR splits into bits 0..1 (a per-lane
+    // constant) and bits 2..3, which permute the four steps s = 4i .. 4i+3:
+    // kofs[s % 4] + 256 (s / 4) is the address.
     const int kx = chunk_xor(col);                                     // rows col and col + 16
-    const uint32_t kbase = (uint32_t)(col * kRowBytes + 8 * (grp & 1));
-    const uint32_t klo0 = (uint32_t)((((grp >> 1)) ^ (kx & 3)) << 4);
-    const uint32_t klo1 = (uint32_t)(((2 + (grp >> 1)) ^ (kx & 3)) << 4);
-    uint32_t kofs[4][2];
+    uint32_t kofs[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        kofs[j][0] = kbase + klo0 + (uint32_t)(64 * (j ^ (kx >> 2)));
-        kofs[j][1] = kbase + klo1 + (uint32_t)(64 * (j ^ (kx >> 2)));
-    }
+    for (int j = 0; j < 4; ++j)
+        kofs[j] = (uint32_t)(col * kRowBytes + 16 * (grp ^ (kx & 3)) + 64 * (j ^ (kx >> 2)));
     // V, block db (dims 16 db .. 16 db + 15): lane 16 grp + 4e + j addresses
     // key row 4 grp + e (+16 for keys 16 .. 31), dims 16 db + 4j, i.e. chunk
     // 2 db + j/2, half j % 2; the XOR's bit 0 is a per-lane constant, its bits
@@ -260,14 +253,9 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
 
         // S^T of the two 16-key blocks; K operands read kPF steps ahead
         auto kread = [&](int s, u32x4_t &ra, u32x4_t &rb) {
-            const char *p0 = kb + kofs[s & 3][0] + 256 * (s >> 2);
-            const char *p1 = kb + kofs[s & 3][1] + 256 * (s >> 2);
-            const u32x2_t a0 = lds_read_b64((const uint16_t *)p0);
-            const u32x2_t a1 = lds_read_b64((const uint16_t *)p1);
-            const u32x2_t b0 = lds_read_b64((const uint16_t *)(p0 + 16 * kRowBytes));
-            const u32x2_t b1 = lds_read_b64((const uint16_t *)(p1 + 16 * kRowBytes));
-            ra = u32x4_t{a0.x, a0.y, a1.x, a1.y};
-            rb = u32x4_t{b0.x, b0.y, b1.x, b1.y};
+            const char *p = kb + kofs[s & 3] + 256 * (s >> 2);
+            ra = lds_read_b128(p);
+            rb = lds_read_b128(p + 16 * kRowBytes);
         };
         f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
         u32x4_t ka[kPF + 1], kc[kPF + 1];

@@ -123,8 +123,10 @@ __device__ inline void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint16_t *
 // s_waitcnt vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
 
+// Waves per SIMD: D = 512 takes all 256 VGPRs and 128 KiB of LDS (one
+// workgroup per CU); D = 256 fits two workgroups per CU (64 KiB of LDS each).
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(512 / D, 512 / D)))
 void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                                const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths,
                                int causal, uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk,

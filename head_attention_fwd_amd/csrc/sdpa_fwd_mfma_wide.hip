@@ -33,13 +33,13 @@
 //    i % 4 of the 4-element rows addressed by lanes 4e + i / 4 (e = 0..3), so
 //    lanes 4e + j addressing dims 4j .. 4j+3 of key row k0 + e hand lane i the
 //    4 keys k0 .. k0+3 of dim i.
-//  * K and V rows sit in LDS as in HBM, the 16-byte chunk index of row r
-//    XORed with f(r) = 2 (r mod 8) + (r / 8 mod 2).  f is injective on 16 rows
-//    (the 16 K rows that 16 lanes read at one chunk land on 16 distinct
-//    positions, 256 bytes, every bank twice) and keeps bit 0 of the chunk
-//    index apart from its higher bits on 4 consecutive rows (the 4 V rows x 2
-//    adjacent chunks that 16 lanes read in a transposing read land on 8
-//    distinct positions modulo 128 bytes).  Two buffers: the copy of tile t+1 (HBM
+//  * K and V rows sit in LDS as in HBM with their 16-byte chunk indices
+//    XORed by the row: K rows by r mod 16 (the 16 K rows that 16 lanes read
+//    at one chunk, and any 8 consecutive of them, land on distinct positions),
+//    V rows by f(r) = 2 (r mod 8) + (r / 8 mod 2), which keeps bit 0 of the
+//    chunk index apart from its higher bits (the 4 V rows x 2 adjacent chunks
+//    that 16 lanes read in a transposing read land on 8 distinct positions
+//    modulo 128 bytes).  The counters show no LDS bank conflicts.  Two buffers: the copy of tile t+1 (HBM
 //    straight into LDS, buffer_load ... lds) runs while tile t is multiplied;
 //    one barrier per tile.  The copy's buffer descriptor ends at the key
 //    length, so rows past it read as 0.
@@ -79,7 +79,7 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw (stride 0) dword buffer access
 constexpr int kPF = 2;                  // LDS operand reads issued this many MFMA steps ahead
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
 
-// Chunk swizzle of LDS row r (see the header comment).
+// Chunk swizzle of V row r (see the header comment).
 __device__ inline int chunk_xor(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi)
@@ -194,11 +194,13 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     // Copy offsets: lane L of slice j fills LDS row pos, physical chunk pc,
     // which holds the row's chunk pc ^ chunk_xor(pos).
     uint32_t coff[kSlicesPerWave];
+    int cpos[kSlicesPerWave];
 #pragma unroll
     for (int j = 0; j < kSlicesPerWave; ++j) {
         const int pos = kRowsPerSlice * (wave * kSlicesPerWave + j) + lane / kChunks;
         const int pc = lane % kChunks;
-        coff[j] = (uint32_t)(pos * kRowBytes + ((pc ^ chunk_xor(pos)) << 4));
+        cpos[j] = pos;
+        coff[j] = (uint32_t)(pos * kRowBytes + ((pc ^ (pos & 15)) << 4));   // K: XOR with r mod 16
     }
     auto issue = [&](int t) {
         const int64_t kv0 = (int64_t)t * kBN;
@@ -213,7 +215,9 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
 #pragma unroll
         for (int j = 0; j < kSlicesPerWave; ++j) {
             copy_to_lds(rk, kb + (wave * kSlicesPerWave + j) * 512, coff[j]);
-            copy_to_lds(rv, kb + kTileElems + (wave * kSlicesPerWave + j) * 512, coff[j]);
+            // V: XOR with chunk_xor(r) instead of r mod 16
+            const uint32_t vo = coff[j] ^ (uint32_t)(((cpos[j] & 15) ^ chunk_xor(cpos[j])) << 4);
+            copy_to_lds(rv, kb + kTileElems + (wave * kSlicesPerWave + j) * 512, vo);
         }
     };
 
@@ -222,7 +226,7 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     // the second block).  The row's XOR splits into bits 0..1 (a per-lane
     // constant) and bits 2..3, which permute the four steps s = 4i .. 4i+3:
     // kofs[s % 4] + 256 (s / 4) is the address.
-    const int kx = chunk_xor(col);                                     // rows col and col + 16
+    const int kx = col;                                                // rows col and col + 16
     uint32_t kofs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)

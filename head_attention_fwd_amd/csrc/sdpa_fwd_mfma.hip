@@ -441,18 +441,22 @@ struct Attn {
     }
 
     // Block b of a fully legal tile (every row holds a finite reference
-    // maximum), after its weights were taken against the reference (bsum = the
-    // row's block sum): only if a row's block sum passes kSumMax (a score grew
-    // by more than log2(kSumMax / 32) over the reference) does that row move its
-    // reference to the block maximum and recompute the block.  P.V of block b-1
-    // is already issued, so moving a reference only rescales the accumulator
-    // and the row sum.
+    // maximum), after its weights were taken against the reference (bsum = this
+    // lane's part of the row's block sum, 16 of its 32 keys): only if either
+    // half of a row's block sum passes kSumMax (a score grew by more than
+    // log2(kSumMax / 16) over the reference) does that row move its reference
+    // to the block maximum and recompute the block.  The decision is taken per
+    // row, for both lane halves l32 and l32 + 32 together: they feed the same
+    // P.V products and share the row sum, so they must keep one reference.
+    // P.V of block b-1 is already issued, so moving a reference only rescales
+    // the accumulator and the row sum.
     __device__ __forceinline__ void finish_max_free(const f32x16_t &s, bf16x8_t *p, float bsum)
     {
         constexpr float kSumMax = 1048576.0f;   // 2^20
-        const bool grow = !(bsum <= kSumMax);
-        if (__builtin_expect(__any(grow), 0)) {
+        const uint64_t lanes = __builtin_amdgcn_ballot_w64(!(bsum <= kSumMax));
+        if (__builtin_expect(lanes != 0, 0)) {
             asm volatile("" ::: "memory");   // keep the rare path a real branch
+            const bool grow = ((lanes >> l32) | (lanes >> (l32 + 32))) & 1;
             const float mxs = block_max(s);
             if (grow) {
                 scale_pending(__builtin_amdgcn_exp2f(m_run - mxs), nullptr);

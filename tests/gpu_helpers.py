@@ -37,13 +37,20 @@ def torch_dtype(name):
     return torch.bfloat16 if name == "bf16" else torch.float32
 
 
-def run(q, k, v, key_lengths=None, causal=False, dtype="bf16"):
-    """Upload, run sdpa.forward, synchronize, return float64 numpy output."""
+def run(q, k, v, key_lengths=None, causal=False, dtype="bf16", fill=None):
+    """Upload, run sdpa.forward, synchronize, return float64 numpy output.
+
+    fill: if given, the output buffer is allocated here and filled with this
+    value first (NaN shows any element the kernel leaves unwritten)."""
     td = torch_dtype(dtype)
     dq, dk, dv = to_dev(q, td), to_dev(k, td), to_dev(v, td)
     kl = None if key_lengths is None else torch.as_tensor(
         np.asarray(key_lengths, dtype=np.int32)).to(require_gpu())
-    out = sdpa.forward(dq, dk, dv, key_lengths=kl, causal=causal)
+    out = None
+    if fill is not None:
+        B, H, Lq, _ = q.shape
+        out = torch.full((B, H, Lq, v.shape[3]), fill, dtype=td, device=require_gpu())
+    out = sdpa.forward(dq, dk, dv, key_lengths=kl, causal=causal, out=out)
     torch.cuda.synchronize()
     return out.to(torch.float32).cpu().numpy().astype(np.float64)
 

@@ -1,10 +1,12 @@
 """GPU parity: libsdpa against the fp64 oracle on the same seeded inputs.
 
-Full element-by-element comparison on every configuration the oracle finishes
-in seconds, sampled rows (computed one by one by the oracle) on the long causal
-configuration, and ragged / degenerate shapes that cross tile boundaries.
-All calls go through the C ABI via the Python binding.
+Full element-by-element comparison on every configuration (the two long causal
+ones included, in the benchmark's launch configuration), and ragged /
+degenerate shapes that cross tile boundaries.  All calls go through the C ABI
+via the Python binding.
 """
+import sys
+
 import numpy as np
 import pytest
 
@@ -44,18 +46,31 @@ def _sample_rows(B, H, Lq, n_random, seed):
 
 
 @pytest.mark.parametrize("name", ["long_causal_bf16", "long_causal_d128_bf16"])
-def test_long_causal_sampled_rows(name):
+def test_long_causal_full(name):
     """The long causal configurations at full size, in the launch configuration the
-    benchmark times; the oracle recomputes a sample of rows one by one."""
+    benchmark times (grouped longest-first causal order), compared with the oracle
+    element by element.  The output starts as NaN, so a query tile the work
+    order skipped would fail.  Reports max |gpu - oracle| / max |oracle| per band
+    of rows: late causal rows average thousands of values and are small, so the
+    bars (scaled by max |V|) alone would be a weak signal there."""
     x = workloads.generate(name)
     c = x.config
-    announce("config %s (full size)" % name)
-    got = run(x.q, x.k, x.v, None, True, "bf16")
-    rows = _sample_rows(c.B, c.H, c.Lq, n_random=8, seed=7)
-    ref, _ = oracle.attention_rows(x.q, x.k, x.v, rows, causal=True)
-    sel = got[rows[:, 0], rows[:, 1], rows[:, 2]]
-    assert_parity(sel, ref, x.v, "bf16", name + " sampled rows")
-    assert np.all(np.isfinite(got))
+    announce("config %s (full size, every element)" % name)
+    got = run(x.q, x.k, x.v, None, True, "bf16", fill=float("nan"))
+    ref = oracle.attention(x.q, x.k, x.v, causal=True)
+    bands = [(0, 64), (64, 512), (512, 2048), (2048, c.Lq)]
+    for lo, hi in bands:
+        e = np.abs(got[:, :, lo:hi] - ref[:, :, lo:hi])
+        r = np.abs(ref[:, :, lo:hi])
+        rel_max = float(e.max() / r.max())
+        rel_mean = float(e.mean() / r.mean())
+        sys.stdout.write("[%s] rows %d-%d: max|d| %.3g (%.3g of max|O|), mean|d| %.3g "
+                         "(%.3g of mean|O|)\n" % (name, lo, hi - 1, float(e.max()), rel_max,
+                                                  float(e.mean()), rel_mean))
+        # bf16 rounds each weight and the output to 8 significant bits
+        # (relative error <= 2^-8 each): a few such units per row
+        assert rel_mean <= 2.0 ** -6, (lo, hi, rel_mean)
+    assert_parity(got, ref, x.v, "bf16", name)
 
 
 # Ragged and degenerate shapes on both kernels: (B, H, Lq, Lk, d_k, d_v, causal, lengths)

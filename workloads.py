@@ -195,6 +195,36 @@ def draw(B: int, H: int, Lq: int, Lk: int, d_k: int, d_v: int, *, dtype: str = "
     return q, k, v, kl
 
 
+def draw_spiked(B: int, H: int, Lq: int, Lk: int, d: int, *, dtype: str = "bf16", seed: int = 0,
+                spikes=(), lift: float = 3.0, qk_scale: float = 1.0):
+    """Inputs whose scores jump far above the running maximum part-way along the keys.
+
+    Recipe: the same generator; Q, K (standard normal times ``qk_scale``) and V
+    (standard normal) in that order, then one direction u per (b, h) (standard
+    normal, normalised to length 1).  Every Q row gets ``lift * u`` added; for
+    each (j, t) in ``spikes`` key row j becomes ``t * sqrt(d) / lift * u``, so
+    that its score against a query row is about t (in nats) times
+    (q . u) / lift, i.e. near t for most rows and spread around it.  Rounded to
+    float32 and, for bf16, to bfloat16 (nearest even), as ``draw``.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, H, Lq, d)) * qk_scale
+    k = rng.standard_normal((B, H, Lk, d)) * qk_scale
+    v = rng.standard_normal((B, H, Lk, d))
+    u = rng.standard_normal((B, H, d))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    q += lift * u[:, :, None, :]
+    for j, t in spikes:
+        if 0 <= j < Lk:
+            k[:, :, j, :] = (t * np.sqrt(d) / lift) * u
+
+    def store(a):
+        a = a.astype(np.float32)
+        return round_to_bf16(a) if dtype == "bf16" else a
+
+    return store(q), store(k), store(v)
+
+
 @dataclasses.dataclass
 class MultiHeadInputs:
     config: Config

@@ -7,6 +7,7 @@ thin Python binding of that library; it loads head_attention_fwd_amd/libsdpa.so
 on first use and raises if it is missing.
 """
 from ._binding import (  # noqa: F401
+    DECODE_NOALLOC_SCRATCH_BYTES,
     EXPORTED,
     LIBRARY,
     SDPA_BF16,
@@ -14,16 +15,19 @@ from ._binding import (  # noqa: F401
     SDPA_ERR_BAD_SHAPE,
     SDPA_ERR_HIP,
     SDPA_ERR_NULL_POINTER,
+    SDPA_ERR_SCRATCH_LIMIT,
     SDPA_ERR_UNSUPPORTED,
     SDPA_ERR_WORKSPACE,
     SDPA_F32,
     SDPA_OK,
     SdpaError,
     decode,
+    decode_noalloc,
     forward,
     load_library,
     multihead,
     sdpa_decode,
+    sdpa_decode_noalloc,
     sdpa_decode_workspace_bytes,
     restricted,
     sdpa_forward,

@@ -19,12 +19,17 @@ SDPA_ERR_UNSUPPORTED = 3
 SDPA_ERR_ALIAS = 4
 SDPA_ERR_HIP = 5
 SDPA_ERR_WORKSPACE = 6
+SDPA_ERR_SCRATCH_LIMIT = 7
+
+#: SDPA_DECODE_NOALLOC_SCRATCH_BYTES of include/sdpa.h: the static device
+#: scratch of sdpa_decode_noalloc, per device.
+DECODE_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 SDPA_F32 = 0
 SDPA_BF16 = 1
 
 #: Symbols include/sdpa.h declares.
-EXPORTED = ("sdpa_decode", "sdpa_decode_workspace_bytes", "sdpa_forward",
+EXPORTED = ("sdpa_decode", "sdpa_decode_noalloc", "sdpa_decode_workspace_bytes", "sdpa_forward",
             "sdpa_forward_restricted", "sdpa_last_hip_error", "sdpa_multihead_forward",
             "sdpa_multihead_workspace_bytes", "sdpa_status_str")
 
@@ -63,6 +68,9 @@ def load_library(path: str = LIBRARY):
     lib.sdpa_decode.restype = ctypes.c_int
     lib.sdpa_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                 vp, i64, vp]
+    lib.sdpa_decode_noalloc.restype = ctypes.c_int
+    lib.sdpa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                        ctypes.c_int, vp]
     lib.sdpa_decode_workspace_bytes.restype = i64
     lib.sdpa_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int]
     lib.sdpa_status_str.restype = ctypes.c_char_p
@@ -116,6 +124,14 @@ def sdpa_decode(Q: int, K: int, V: int, key_lengths: int, out: int, B: int, H: i
     return load_library().sdpa_decode(Q or None, K or None, V or None, key_lengths or None,
                                       out or None, B, H, Lq, Lk, d_k, d_v, int(dtype),
                                       workspace or None, workspace_bytes, stream or None)
+
+
+def sdpa_decode_noalloc(Q: int, K: int, V: int, key_lengths: int, out: int, B: int, H: int,
+                        Lq: int, Lk: int, d_k: int, d_v: int, dtype: int, stream: int) -> int:
+    """Raw C call; pointers and the stream are integers (0 = NULL).  Returns the status."""
+    return load_library().sdpa_decode_noalloc(Q or None, K or None, V or None,
+                                              key_lengths or None, out or None, B, H, Lq, Lk,
+                                              d_k, d_v, int(dtype), stream or None)
 
 
 def sdpa_decode_workspace_bytes(B: int, H: int, Lq: int, Lk: int, d_k: int, d_v: int,
@@ -313,4 +329,31 @@ def decode(q, k, v, key_lengths=None, out=None, workspace=None):
                          0 if key_lengths is None else key_lengths.data_ptr(), out.data_ptr(),
                          B, H, Lq, Lk, d_k, d_v, dtype, ws_ptr, ws_bytes, stream)
     _raise(st, "sdpa_decode")
+    return out
+
+
+def decode_noalloc(q, k, v, out, key_lengths=None):
+    """sdpa_decode_noalloc: decode() without a workspace and without any allocation.
+
+    The split partial results go to the library's static device scratch
+    (DECODE_NOALLOC_SCRATCH_BYTES per device; larger requests raise SdpaError
+    with SDPA_ERR_SCRATCH_LIMIT).  out (the [B,H,Lq,d_v] result) is required and
+    key_lengths must be None or an int32 [B] tensor on the inputs' device, so that
+    nothing is allocated here either.  Calls on one device that may overlap in
+    time race on that scratch.  Returns out.
+    """
+    import torch
+
+    if out is None:
+        raise ValueError("decode_noalloc needs a preallocated out tensor")
+    if key_lengths is not None and not isinstance(key_lengths, torch.Tensor):
+        raise ValueError("decode_noalloc needs key_lengths as a device tensor (or None)")
+    (B, H, Lq, Lk, d_k, d_v), dtype, key_lengths, out = _check(q, k, v, key_lengths, out)
+    dev = q.device
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = sdpa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 0 if key_lengths is None else key_lengths.data_ptr(),
+                                 out.data_ptr(), B, H, Lq, Lk, d_k, d_v, dtype, stream)
+    _raise(st, "sdpa_decode_noalloc")
     return out

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "sdpa.h"
 #include "sdpa_kernels.h"
@@ -152,6 +153,45 @@ int64_t split_workspace_bytes(int64_t n_bh, int64_t Lq, const SplitPlan &sp)
     return 4 * (64 + 2) * n_bh * sp.n_split * Lq;
 }
 
+// ---- device scratch of sdpa_decode_noalloc
+//
+// The key-split partial results of sdpa_decode_noalloc live in this array: one
+// copy per device (each GPU the library runs on holds it until the process
+// ends), so the entry point allocates nothing.  In host code `scratch` is only
+// a host-side stand-in; its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+constexpr int64_t kScratchBytes = SDPA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device (null: not looked up)
+
+// The device address of `scratch` on device `dev`, looked up with that device
+// current on the first call for it.
+hipError_t device_scratch(int dev, void **ptr)
+{
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        hipError_t err = hipGetDevice(&cur);
+        if (err != hipSuccess) return err;
+        if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 // ---- multi-head attention: projections around the attention (§3.2.2)
 
 // Largest buffer a projection product addresses (32-bit offsets, with room for
@@ -229,6 +269,9 @@ const char *sdpa_status_str(sdpa_status s)
     case SDPA_ERR_ALIAS: return "out overlaps an input buffer";
     case SDPA_ERR_HIP: return "a HIP runtime call failed (see sdpa_last_hip_error)";
     case SDPA_ERR_WORKSPACE: return "the workspace is missing, too small, or overlaps another buffer";
+    case SDPA_ERR_SCRATCH_LIMIT:
+        return "the call needs more scratch than the library's static device scratch holds "
+               "(sdpa_decode_noalloc: see SDPA_DECODE_NOALLOC_SCRATCH_BYTES; use sdpa_decode)";
     }
     return "unknown sdpa_status";
 }
@@ -380,6 +423,30 @@ sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
     if (B * H * sp.n_split > kMaxWorkgroups || B * H * Lq > kMaxWorkgroups) return SDPA_ERR_BAD_SHAPE;
     return hip_status(sdpa::launch_split_mfma_d64(Q, K, V, key_lengths, out, B, H, Lq, Lk, sp.chunk,
                                                   sp.n_split, workspace, s));
+}
+
+sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
+                                const int32_t *key_lengths, void *out,
+                                int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream)
+{
+    Sizes z;
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    if (st != SDPA_OK || z.empty) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!split_applies(Lq, d_k, d_v, dtype))
+        return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dtype, s);
+    const SplitPlan sp = split_plan(B * H, Lk);
+    const int64_t need = split_workspace_bytes(B * H, Lq, sp);
+    if (need > kScratchBytes) return SDPA_ERR_SCRATCH_LIMIT;
+    if (B * H * sp.n_split > kMaxWorkgroups || B * H * Lq > kMaxWorkgroups) return SDPA_ERR_BAD_SHAPE;
+    int dev = -1;
+    hipError_t err = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    void *ws = nullptr;
+    if (err == hipSuccess) err = device_scratch(dev, &ws);
+    if (err != hipSuccess) return hip_status(err);
+    return hip_status(sdpa::launch_split_mfma_d64(Q, K, V, key_lengths, out, B, H, Lq, Lk, sp.chunk,
+                                                  sp.n_split, ws, s));
 }
 
 }  // extern "C"

@@ -71,7 +71,8 @@ typedef enum sdpa_status {
     SDPA_ERR_UNSUPPORTED = 3,    /* (dtype, d_k, d_v) combination not built */
     SDPA_ERR_ALIAS = 4,          /* out overlaps Q, K, V or key_lengths */
     SDPA_ERR_HIP = 5,            /* a HIP call failed; see sdpa_last_hip_error() */
-    SDPA_ERR_WORKSPACE = 6       /* sdpa_decode: workspace NULL, too small, or overlapping */
+    SDPA_ERR_WORKSPACE = 6,      /* sdpa_decode: workspace NULL, too small, or overlapping */
+    SDPA_ERR_SCRATCH_LIMIT = 7   /* sdpa_decode_noalloc: needs more than its static scratch */
 } sdpa_status;
 
 typedef enum sdpa_dtype {
@@ -205,6 +206,34 @@ sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
  */
 int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                                     int64_t d_k, int64_t d_v, sdpa_dtype dtype);
+
+/*
+ * sdpa_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same result as
+ * sdpa_decode (same kernels, same chunking); the key-split partial results go
+ * to a static device array of the library (SDPA_DECODE_NOALLOC_SCRATCH_BYTES
+ * bytes, one copy per device, held until the process ends), whose device
+ * address is looked up on the first call on each device (the device of
+ * `stream`, or the current device for the null stream).  The call makes no
+ * hipMalloc, hipFree or other allocating call.
+ *
+ * Arguments, layouts, arithmetic and errors as for sdpa_decode, plus
+ * SDPA_ERR_SCRATCH_LIMIT (checked on the host before any HIP call) when the
+ * split path would need more than SDPA_DECODE_NOALLOC_SCRATCH_BYTES of partial
+ * results (4 * (d_v + 2) * B * H * Lq * n_chunks bytes, as
+ * sdpa_decode_workspace_bytes reports); shapes outside the split path need no
+ * scratch.  Every call on one device shares that device's array: calls that
+ * may overlap in time on one device (two streams, two host threads without
+ * stream order) race and give undefined results.  Nothing in the array needs
+ * to start at zero (each call writes every partial result it reads).
+ */
+#define SDPA_DECODE_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+
+sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
+                                const int32_t *key_lengths, void *out,
+                                int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *sdpa_status_str(sdpa_status status);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(6):
+    for st in range(8):
         s = sdpa.sdpa_status_str(st)
         assert isinstance(s, str) and s
     assert sdpa.sdpa_status_str(0) == "success"
@@ -160,6 +160,46 @@ def test_decode_empty_calls():
     assert dcall(Lq=0, ws=0) == sdpa.SDPA_OK
     assert dcall(Q=0, K=0, V=0, O=0, H=0, ws=0) == sdpa.SDPA_OK
     assert sdpa.sdpa_status_str(sdpa.SDPA_ERR_WORKSPACE).startswith("the workspace")
+
+
+# ---- sdpa_decode_noalloc: sdpa_decode's checks, the static scratch's limit
+
+def ncall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=4, H=16, Lq=1, Lk=8192, dk=64, dv=64,
+          dtype=sdpa.SDPA_BF16):
+    return sdpa.sdpa_decode_noalloc(Q, K, V, kl, O, B, H, Lq, Lk, dk, dv, dtype, 0)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER, encoding="utf-8").read()
+    m = re.search(r"#define SDPA_DECODE_NOALLOC_SCRATCH_BYTES \((\d+) \* (\d+) \* (\d+)\)", text)
+    assert m, "SDPA_DECODE_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == sdpa.DECODE_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(Q=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(O=0), sdpa.SDPA_ERR_NULL_POINTER),
+    (dict(B=-1), sdpa.SDPA_ERR_BAD_SHAPE),
+    (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(O=FAKE_K + 64), sdpa.SDPA_ERR_ALIAS),
+    # 2048 heads x 32 rows in one chunk each: 17.3 MB of partial results
+    (dict(Q=1 << 32, K=2 << 32, V=3 << 32, O=4 << 32, B=1, H=2048, Lq=32, Lk=256),
+     sdpa.SDPA_ERR_SCRATCH_LIMIT),
+])
+def test_noalloc_prelaunch_validation(kw, expected):
+    assert ncall(**kw) == expected
+
+
+def test_noalloc_limit_is_the_workspace_size():
+    ws = sdpa.sdpa_decode_workspace_bytes
+    assert ws(1, 2048, 32, 256, 64, 64, sdpa.SDPA_BF16) > sdpa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert ws(4, 16, 1, 8192, 64, 64, sdpa.SDPA_BF16) <= sdpa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert "static device scratch" in sdpa.sdpa_status_str(sdpa.SDPA_ERR_SCRATCH_LIMIT)
+
+
+def test_noalloc_empty_calls():
+    assert ncall(B=0) == sdpa.SDPA_OK
+    assert ncall(Q=0, K=0, V=0, O=0, Lq=0) == sdpa.SDPA_OK
 
 
 # ---- sdpa_forward_restricted: sdpa_forward's checks plus the radius

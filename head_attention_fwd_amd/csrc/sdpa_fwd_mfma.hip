@@ -81,34 +81,20 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 
-// Build-time shape of the kernel (tuned on MI355X; see the launcher).
-#ifndef SDPA_MFMA_WAVES
-#define SDPA_MFMA_WAVES 4         // waves per workgroup (32 query rows each)
-#endif
-#ifndef SDPA_MFMA_KEY_BLOCKS
-#define SDPA_MFMA_KEY_BLOCKS 2    // 32-key blocks per LDS tile
-#endif
-#ifndef SDPA_STORE_LDS
-#define SDPA_STORE_LDS 1
-#endif
-#ifndef SDPA_SPLIT_KEY_BLOCKS
-#define SDPA_SPLIT_KEY_BLOCKS 1   // 32-key blocks per LDS tile of the key-split kernel
-#endif
-#ifndef SDPA_SHORT_CAUSAL_KEYS
-#define SDPA_SHORT_CAUSAL_KEYS 512   // d = 64 causal launches up to this many keys take 32-key tiles
-#endif
-#ifndef SDPA_CAUSAL_HEAD_GROUP
-#define SDPA_CAUSAL_HEAD_GROUP 4  // causal order: heads per group on an XCD (0: all of its heads)
-#endif
-#ifndef SDPA_MFMA_WAVES_PER_SIMD
-#define SDPA_MFMA_WAVES_PER_SIMD 3   // register budget at D = 64: 3 waves per SIMD
-#endif
+// Shape of the kernels (each value measured on MI355X against its neighbours).
+constexpr int kWaves = 4;              // waves per workgroup (32 query rows each); d = 16: 2
+constexpr int kKeyBlocks = 2;          // 32-key blocks per LDS tile (d = 128: 1)
+constexpr int kSplitKeyBlocks = 1;     // 32-key blocks per LDS tile of the key-split kernel
+constexpr int kShortCausalKeys = 512;  // d = 64 causal launches up to this many keys take 32-key tiles
+constexpr int kCausalHeadGroup = 4;    // causal order: heads per group on an XCD
+constexpr int kWavesPerSimd64 = 3;     // register budget at d = 64 with 64-key tiles
+constexpr int kBandKeyBlocks64 = 1;    // restricted attention, d = 64: 32-key tiles (finer band edges)
 // Waves per SIMD the register budget is set for, by head size: D = 128 needs
 // 64 accumulator and 32 Q-operand registers (2 waves), D = 32 and D = 16 fit 4;
 // D = 64 with 32-key tiles (one score block in flight) fits 4 as well.
 template <int D, int NB = 2>
 struct Occupancy {
-    static constexpr int kWaves = D >= 128 ? 2 : (D >= 64 ? (NB == 1 ? 4 : SDPA_MFMA_WAVES_PER_SIMD) : 4);
+    static constexpr int kWaves = D >= 128 ? 2 : (D >= 64 ? (NB == 1 ? 4 : kWavesPerSimd64) : 4);
 };
 
 // 16-byte chunk swizzles of a row of D bf16 values (D/8 chunks), XORed into
@@ -879,7 +865,6 @@ __device__ __forceinline__ void attend_query_tile(
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(O + tile_base), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
-#if SDPA_STORE_LDS
     // The wave's 32 x D output tile goes through LDS so that every store
     // instruction writes 512/D whole rows (1 KiB contiguous): written in the
     // accumulator layout (lane: row l32, 8-byte pieces of 16-byte chunk
@@ -910,19 +895,6 @@ __device__ __forceinline__ void attend_query_tile(
         const u32x4_t w = *(const u32x4_t *)((const char *)stage + r * kRowBytes + ((c ^ oswz(r)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(r * kRowBytes + c * 16), 0, 0);
     }
-#else
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int rq4 = 0; rq4 < 4; ++rq4) {
-            if (32 * db + 8 * rq4 >= kD) continue;
-            u32x2_t w;
-            w[0] = pack_bf16x2(st.acc[db][4 * rq4 + 0] * inv, st.acc[db][4 * rq4 + 1] * inv);
-            w[1] = pack_bf16x2(st.acc[db][4 * rq4 + 2] * inv, st.acc[db][4 * rq4 + 3] * inv);
-            __builtin_amdgcn_raw_buffer_store_b64(
-                w, ro, (uint32_t)(l32 * kRowBytes + (db * 32 + rq4 * 8 + g * 4) * 2), 0, 0);
-        }
-#endif
 }
 
 // Work decomposition: one query tile (qt, head bh) per workgroup.  The
@@ -935,7 +907,7 @@ __device__ __forceinline__ void attend_query_tile(
 //    first (qt descending), which fills the slots greedily longest-first and
 //    leaves only short tiles for the end of the grid.  When 8 divides the head
 //    count each XCD takes its own run of heads; when a head's K and V reach
-//    1 MiB, in groups of SDPA_CAUSAL_HEAD_GROUP heads one after the other,
+//    1 MiB, in groups of kCausalHeadGroup heads one after the other,
 //    longest first within a group: fewer heads in flight keep more of their
 //    K/V rows in the XCD's L2 (on 8 heads of 8192 keys per XCD: 4 at a time
 //    fetched 550 MiB per launch into L2, all 8 at once 1188 MiB, one at a time
@@ -971,8 +943,7 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::k
             // once a head's K and V reach 1 MiB (smaller ones share the L2
             // anyway, and all heads at once balance better)
             const bool big = (uint64_t)Lk * (4 * D) >= (1u << 20);
-            const uint32_t G = (big && SDPA_CAUSAL_HEAD_GROUP > 0 && hx % SDPA_CAUSAL_HEAD_GROUP == 0)
-                                   ? SDPA_CAUSAL_HEAD_GROUP : hx;
+            const uint32_t G = (big && hx % kCausalHeadGroup == 0) ? kCausalHeadGroup : hx;
             const uint32_t grp = j / (G * n_qtiles), r = j % (G * n_qtiles);
             bh = (w & 7) * hx + grp * G + r % G;
             qt = n_qtiles - 1 - r / G;
@@ -1031,7 +1002,7 @@ __global__ __launch_bounds__(64) void sdpa_split_mfma_d64_kernel(
 {
     // One wave, 32-key tiles: 24 KiB of LDS, so 6 workgroups (waves) per CU
     // keep the cache streaming.
-    constexpr int NW = 1, NB = SDPA_SPLIT_KEY_BLOCKS, D = 64;
+    constexpr int NW = 1, NB = kSplitKeyBlocks, D = 64;
     using A = Attn<NW, NB, D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride + A::kLdsPad];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
@@ -1119,9 +1090,9 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     // D = 16: 2-wave workgroups (64 query rows) with 64-key tiles, so that each
     // wave copies one whole 1 KiB slice and, at 12 KiB of LDS and 98 VGPRs, a CU
     // holds 8 of them (2048 slots; 4-wave workgroups with 128-key tiles: 1024).
-    constexpr int NW = D <= 16 ? 2 : SDPA_MFMA_WAVES;
+    constexpr int NW = D <= 16 ? 2 : kWaves;
     // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB.
-    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 2);
+    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? kKeyBlocks : 2);
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
@@ -1131,7 +1102,7 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
         // waves per SIMD (24 KiB of LDS, 127 VGPRs), so that every query tile of
         // the base model's decoder is resident at once, and the tiles that
         // cross the diagonal are half as long.
-        if (causal && Lk <= SDPA_SHORT_CAUSAL_KEYS) {
+        if (causal && Lk <= kShortCausalKeys) {
             hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, 1, D>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths, causal,
                                (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh);
@@ -1150,11 +1121,8 @@ hipError_t launch_mfma_band_d(const void *Q, const void *K, const void *V, const
                               int causal, int64_t radius, void *out, int64_t B, int64_t H, int64_t Lq,
                               int64_t Lk, hipStream_t stream)
 {
-    constexpr int NW = SDPA_MFMA_WAVES;
-#ifndef SDPA_BAND_NB64
-#define SDPA_BAND_NB64 1   // d = 64: 32-key tiles at 4 waves per SIMD (finer band edges)
-#endif
-    constexpr int NB = D >= 128 ? 1 : (D == 64 ? SDPA_BAND_NB64 : (D >= 32 ? SDPA_MFMA_KEY_BLOCKS : 4));
+    constexpr int NW = kWaves;
+    constexpr int NB = D >= 128 ? 1 : (D == 64 ? kBandKeyBlocks64 : (D >= 32 ? kKeyBlocks : 4));
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);

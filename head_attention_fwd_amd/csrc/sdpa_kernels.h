@@ -10,9 +10,10 @@
 
 namespace sdpa {
 
-// Any 1 <= d_k, d_v <= 128; elements are fp32 (is_bf16 = false) or bf16.
-// fp32 arithmetic throughout; one lane per query row.  radius >= 0: restricted
-// self-attention (|i - j| <= radius); radius < 0: no restriction.
+// Any 1 <= d_k, d_v <= 512; elements are fp32 (is_bf16 = false) or bf16.
+// fp32 arithmetic throughout on the vector units: one lane per query row up to
+// d = 128, 8 (d <= 256) or 16 (d <= 512) lanes per query row above.  radius >= 0:
+// restricted self-attention (|i - j| <= radius); radius < 0: no restriction.
 hipError_t launch_generic(const void *Q, const void *K, const void *V,
                           const int32_t *key_lengths, int causal, int64_t radius, void *out,
                           int64_t B, int64_t H, int64_t Lq, int64_t Lk,
@@ -25,13 +26,15 @@ hipError_t launch_mfma(const void *Q, const void *K, const void *V,
                        int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
                        hipStream_t stream);
 
-// As launch_mfma, restricted self-attention: key j is legal for query i only
-// when |i - j| <= radius (radius >= 0).
+// bf16, d_k = d_v = d with d in {256, 512}, on the matrix cores (16 query rows
+// per wave, v_mfma_f32_16x16x32_bf16); hipErrorInvalidValue for any other d.
 hipError_t launch_mfma_wide(const void *Q, const void *K, const void *V,
                             const int32_t *key_lengths, int causal, void *out,
                             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
                             hipStream_t stream);
 
+// As launch_mfma, restricted self-attention: key j is legal for query i only
+// when |i - j| <= radius (radius >= 0).
 hipError_t launch_mfma_band(const void *Q, const void *K, const void *V,
                             const int32_t *key_lengths, int causal, int64_t radius, void *out,
                             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,

@@ -46,12 +46,8 @@
 
 #include "sdpa_kernels.h"
 
-#ifndef SDPA_GEMM_BIG_GN
-#define SDPA_GEMM_BIG_GN 4         // waves along n in the large tile (2: 4 waves, 4: 8 waves)
-#endif
-#ifndef SDPA_GEMM_BIG_TILES
-#define SDPA_GEMM_BIG_TILES 1024   // 256 x 128 tiles from this many on (else 128 x 128)
-#endif
+constexpr int kBigTileWavesN = 4;   // waves along n in the large tile (8 waves, 256 x 256)
+constexpr int kBigTileCount = 1024; // large tiles once a product has this many 256 x 128 tiles (else 128 x 128)
 
 namespace sdpa {
 namespace {
@@ -386,8 +382,8 @@ hipError_t launch_proj_gemm(const void *A, int a_mode, const GemmShape &shape,
     int64_t big_tiles = 0;
     for (int i = 0; i < segs.count; ++i) big_tiles += (segs.seg[i].N + 127) / 128;
     big_tiles *= (shape.M + 255) / 256;
-    if (big_tiles >= SDPA_GEMM_BIG_TILES)
-        return launch_shape<4, 2, SDPA_GEMM_BIG_GN>(A, a_mode, shape, segs, c_mode, stream);
+    if (big_tiles >= kBigTileCount)
+        return launch_shape<4, 2, kBigTileWavesN>(A, a_mode, shape, segs, c_mode, stream);
     return launch_shape<2, 2, 2>(A, a_mode, shape, segs, c_mode, stream);
 }
 

@@ -85,19 +85,24 @@ def test_restricted_bf16(case):
                     assert np.all(got[b, :, i] == 0.0), (b, i)
 
 
-@pytest.mark.parametrize("case", [
+GENERIC_CASES = [
     (2, 3, 100, 77, 8, 8, True, [77, 5], 3),
     (2, 2, 130, 130, 64, 64, False, None, 20),
     (1, 2, 90, 120, 16, 48, False, [100], 7),
     (1, 1, 200, 200, 128, 40, True, None, 65),
     (1, 2, 150, 150, 512, 512, False, [140], 20),
-])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+]
+# fp32 for every case; bf16 only where the head sizes have no matrix-core layout
+# (bf16 with d_k = d_v in {16, 32, 64, 128} runs the band kernel, covered above)
+GENERIC_RUNS = [(c, dt) for c in GENERIC_CASES for dt in ("f32", "bf16")
+                if not (dt == "bf16" and c[4] == c[5] and c[4] in (16, 32, 64, 128))]
+
+
+@pytest.mark.parametrize("case,dtype", GENERIC_RUNS,
+                         ids=["x".join(map(str, c[:6])) + "-" + dt for c, dt in GENERIC_RUNS])
 def test_restricted_generic_kernel(case, dtype):
     """fp32 inputs, and bf16 head sizes without a matrix-core layout."""
     B, H, Lq, Lk, dk, dv, causal, lengths, radius = case
-    if dtype == "bf16" and dk == dv and dk in (32, 64, 128):
-        pytest.skip("matrix-core head size: covered above")
     q, k, v, _ = workloads.draw(B, H, Lq, Lk, dk, dv, dtype=dtype, seed=Lq * 3 + radius)
     announce("restricted %s %s" % (dtype, case))
     got = run_restricted(q, k, v, radius, lengths, causal, dtype)

@@ -11,9 +11,18 @@ headline lines.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                   [--no-cpu-baseline] [--rotate R] [--settle-ms MS]
+  python bench.py --copy-mib 512      (calibration: a plain device copy)
+  python bench.py --gemm-probe 8192   (calibration: a bf16 GEMM through torch)
 
 After the W warmup steps, untimed steps continue until the GPU has been busy for
 --settle-ms (default 150 ms), so that the K timed steps see the settled clock.
+
+Besides the metric, the line carries: the roofline of the dominant kernel (with
+the measured HBM traffic per launch and its ratio to the algorithmic bytes while
+the counters match the kernel source), the oracle on the host cores beside it
+(all cores and one thread, with the CPU model), the GPU output compared with
+the oracle's values on the oracle's sample of rows ("parity"), and the shader
+clock sampled during the timed window.
 
 FLOPs are algorithmic: (2*d_k + 2*d_v) per (query, key) pair the mask allows
 (page "Attention Is All You Need/paper/es", §4, Table 1: O(n^2 d) per layer),
@@ -68,11 +77,34 @@ def measured_traffic(config_name):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(x, target_seconds=15.0):
+def host_cpu():
+    """CPU model of this host (from /proc/cpuinfo) and the cores this process may use."""
+    model, fam, mod = "unknown", None, None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model == "unknown":
+                    model = v
+                elif k == "cpu family" and fam is None:
+                    fam = v
+                elif k == "model" and mod is None:
+                    mod = v
+    except OSError:
+        pass
+    if fam is not None and mod is not None:
+        model = "%s (family %s, model %s)" % (model, fam, mod)
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(x, target_seconds=15.0, one_thread_seconds=4.0):
     """The fp64 oracle, as it is, on a bounded random sample of the workload's rows.
 
     Rows (b, h, i) are drawn uniformly, so FLOPs/s on the sample estimate the
-    oracle's throughput on the whole workload.  Runs on the host cores only.
+    oracle's throughput on the whole workload.  Runs on the host cores only; a
+    second, smaller sample on one thread.  Returns the record and, for the
+    parity check of the GPU output, the sampled rows and the oracle's values.
     """
     import oracle
 
@@ -99,56 +131,144 @@ def cpu_baseline(x, target_seconds=15.0):
     oracle.default()   # build/load outside the timed region
     # fp64 copies made once, outside the timed region (the oracle's input type)
     q64, k64, v64 = (np.ascontiguousarray(a, dtype=np.float64) for a in (x.q, x.k, x.v))
-    # calibrate on growing samples (small ones are dominated by fixed costs), then
-    # size the measured sample for about target_seconds of oracle work
-    n = max(threads * 4, 64)
-    for budget in (0.5, 2.0, target_seconds):
-        rows = sample(n)
+
+    def timed(rows, nthreads):
         t0 = time.perf_counter()
-        oracle.attention_rows(q64, k64, v64, rows, key_lengths=x.key_lengths, causal=c.causal,
-                              nthreads=threads, radius=c.radius)
-        dt = time.perf_counter() - t0
-        if budget == target_seconds:
-            break
-        nxt = 2.0 if budget == 0.5 else target_seconds
-        n = int(n * max(1.0, nxt / max(dt, 1e-3)))
-        n = max(64, min(n, c.B * c.H * c.Lq))
+        out, _ = oracle.attention_rows(q64, k64, v64, rows, key_lengths=x.key_lengths,
+                                       causal=c.causal, nthreads=nthreads, radius=c.radius)
+        return time.perf_counter() - t0, out
+
+    def sized(nthreads, seconds):
+        # calibrate on growing samples (small ones are dominated by fixed costs),
+        # then size the measured sample for about `seconds` of oracle work
+        n = max(nthreads * 4, 64)
+        for budget in (0.5, 2.0, seconds):
+            rows = sample(n)
+            dt, out = timed(rows, nthreads)
+            if budget == seconds:
+                break
+            nxt = min(2.0, seconds) if budget == 0.5 else seconds
+            n = int(n * max(1.0, nxt / max(dt, 1e-3)))
+            n = max(64, min(n, c.B * c.H * c.Lq))
+        return rows, dt, out
+
+    rows, dt, out = sized(threads, target_seconds)
     f = row_flops(rows)
+    rows1, dt1, _ = sized(1, one_thread_seconds)
+    f1 = row_flops(rows1)
     del q64, k64, v64
-    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d uniformly drawn query rows (%.3g of the workload's FLOPs, %.1f s), "
-                      "fp64 C oracle with OpenMP" % (n, f / perfmodel.flops(
-                          c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
-                          radius=c.radius), dt)}
+    model, _ = host_cpu()
+    total = perfmodel.flops(c.B, c.H, c.Lq, c.Lk, c.d_k, c.d_v, c.causal, x.key_lengths,
+                            radius=c.radius)
+    rec = {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": "%d uniformly drawn query rows (%.3g of the workload's FLOPs, %.1f s), "
+                     "fp64 C oracle with OpenMP" % (len(rows), f / total, dt),
+           "cpu_model": model,
+           "value_1thread": f1 / dt1 / 1e12,
+           "sample_1thread": "%d other uniformly drawn query rows (%.1f s) on one thread"
+                             % (len(rows1), dt1)}
+    return rec, rows, out
 
 
 def cpu_baseline_multihead(x, target_seconds=15.0):
     """The fp64 oracle's MultiHead, as it is, on the first B' batch entries of the
-    workload (B' sized for about target_seconds), FLOPs counted like the GPU's."""
+    workload (B' sized for about target_seconds), FLOPs counted like the GPU's.
+    Returns the record, B' and the oracle's output for those entries."""
     import oracle
 
     c = x.config
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     oracle.default()
 
-    def run(nb):
+    def run(nb, nthreads=threads):
         kl = None if x.key_lengths is None else x.key_lengths[:nb]
         args = [np.ascontiguousarray(a[:nb], dtype=np.float64) for a in (x.xq, x.xkv)]
         t0 = time.perf_counter()
-        oracle.multihead(args[0], args[1], x.wq, x.wk, x.wv, x.wo, c.H, key_lengths=kl,
-                         causal=c.causal, nthreads=threads)
+        out = oracle.multihead(args[0], args[1], x.wq, x.wk, x.wv, x.wo, c.H, key_lengths=kl,
+                               causal=c.causal, nthreads=nthreads)
         return time.perf_counter() - t0, perfmodel.multihead_flops(
-            nb, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v, c.causal, kl)
+            nb, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v, c.causal, kl), out
 
-    dt, f = run(1)
+    dt, f, out = run(1)
     nb = int(max(1, min(c.B, round(target_seconds / max(dt, 1e-3)))))
     if nb > 1:
-        dt, f = run(nb)
+        dt, f, out = run(nb)
     total = perfmodel.multihead_flops(c.B, c.Lq, c.Lk, c.d_model, c.H, c.d_k, c.d_v, c.causal,
                                       x.key_lengths)
-    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "the first %d of %d batch entries (%.3g of the workload's FLOPs, %.1f s), "
-                      "fp64 C oracle with OpenMP" % (nb, c.B, f / total, dt)}
+    model, _ = host_cpu()
+    rec = {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": "the first %d of %d batch entries (%.3g of the workload's FLOPs, %.1f s), "
+                     "fp64 C oracle with OpenMP" % (nb, c.B, f / total, dt),
+           "cpu_model": model, "value_1thread": None,
+           "sample_1thread": "not measured: one batch entry's projections and attention "
+                             "take minutes on one thread"}
+    return rec, nb, out
+
+
+def parity_record(got, ref, v_absmax, dtype, what):
+    """The GPU output against the oracle's values on the same inputs, with the bars
+    of the parity tests (fp32: max |d| <= 1e-5; bf16: max |d| <= 2e-2 max|V|, mean
+    |d| <= 2e-3)."""
+    err = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    max_abs, mean_abs = float(err.max()), float(err.mean())
+    if dtype == "f32":
+        bar = {"max_abs": 1e-5}
+        ok = max_abs <= 1e-5
+    else:
+        bar = {"max_abs": 2e-2 * v_absmax, "mean_abs": 2e-3}
+        ok = max_abs <= bar["max_abs"] and mean_abs <= bar["mean_abs"]
+    return {"max_abs": max_abs, "mean_abs": mean_abs, "rows": what, "bar": bar, "ok": bool(ok),
+            "max_rel_to_max_out": max_abs / max(float(np.abs(ref).max()), 1e-30)}
+
+
+class ClockSampler:
+    """Samples the shader clock the driver reports (sysfs pp_dpm_sclk, the line
+    marked current) from a host thread while the GPU works."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                with open(p, encoding="ascii") as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            return float(line.split(":")[1].strip().split("M")[0])
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "n": len(v),
+                "source": "sysfs pp_dpm_sclk (current level), sampled every 2 ms during the "
+                          "timed window"}
 
 
 def copy_calibration(torch, dev, args):
@@ -171,6 +291,37 @@ def copy_calibration(torch, dev, args):
                       "GB_per_s_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def gemm_probe(torch, dev, args):
+    """Calibration, not the product: a large bf16 GEMM through torch (hipBLASLt),
+    N x N x N, to show what a dense matrix-core kernel reaches on this GPU (its
+    rate, and under rocprofv3 counters its clock and matrix-core busy share)."""
+    n = args.gemm_probe
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(args.warmup):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t_busy = time.perf_counter()
+    while (time.perf_counter() - t_busy) * 1e3 < args.settle_ms:
+        for _ in range(5):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    with ClockSampler() as clk:
+        t0.record()
+        for _ in range(args.steps):
+            torch.matmul(a, b, out=c)
+        t1.record()
+        torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"probe": "bf16 GEMM C = A B through torch.matmul (hipBLASLt), calibration only",
+                      "N": n, "ms_per_gemm": ms, "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12,
+                      "frac_of_peak": 2.0 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+                      "clock": clk.summary()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +335,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(calibrates the HBM byte counters of rocprofv3)")
+    ap.add_argument("--gemm-probe", type=int, default=0,
+                    help="instead of attention, time a bf16 N x N x N GEMM through torch "
+                         "(calibration: what a dense matrix-core kernel reaches on this GPU)")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="time the K steps as one replay of a captured HIP graph (no host "
                          "launch cost between steps); auto: on for the decode workloads, whose "
@@ -205,6 +359,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_mib:
         copy_calibration(torch, dev, args)
+        return
+    if args.gemm_probe:
+        gemm_probe(torch, dev, args)
         return
     x = workloads.generate(args.config)
     c = x.config
@@ -316,6 +473,7 @@ def main():
         torch.cuda.synchronize()
 
     use_graph = args.graph == "on" or (args.graph == "auto" and c.entry in ("decode", "multihead"))
+    clk = None
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     if use_graph:
@@ -347,20 +505,22 @@ def main():
                                    e.view(torch.int16) if e.dtype == torch.bfloat16 else e):
                     raise RuntimeError("graph replay differs from the eager result")
         torch.cuda.synchronize()        # barrier (one rank) + synchronize
-        t0 = time.perf_counter()
-        with torch.cuda.stream(gs):
-            start.record(gs)
-            graph.replay()
-            end.record(gs)
-        torch.cuda.synchronize()
+        with ClockSampler() as clk:
+            t0 = time.perf_counter()
+            with torch.cuda.stream(gs):
+                start.record(gs)
+                graph.replay()
+                end.record(gs)
+            torch.cuda.synchronize()
     else:
         torch.cuda.synchronize()        # barrier (one rank) + synchronize
-        t0 = time.perf_counter()
-        start.record(stream)
-        for n in range(args.steps):
-            step(n)
-        end.record(stream)
-        torch.cuda.synchronize()
+        with ClockSampler() as clk:
+            t0 = time.perf_counter()
+            start.record(stream)
+            for n in range(args.steps):
+                step(n)
+            end.record(stream)
+            torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
 
@@ -420,11 +580,24 @@ def main():
                           "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 128 else "sdpa_fwd_generic_kernel")
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
+    roof["traffic_ratio"] = None if traffic is None else traffic / nbytes
     roof["kernel_ms"] = kern_ms
 
-    cpu = None
+    # The output of input set 0 (written by the timed steps) against the oracle's
+    # values on the rows the CPU baseline computes: the line checks itself.
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_multihead(x) if c.entry == "multihead" else cpu_baseline(x)
+        o_host = sets[0][1].float().cpu().numpy()
+        if c.entry == "multihead":
+            cpu, nb, ref = cpu_baseline_multihead(x)
+            parity = parity_record(o_host[:nb], ref, float(np.abs(ref).max()), c.dtype,
+                                   "the first %d of %d batch entries" % (nb, c.B))
+        else:
+            cpu, rows, ref = cpu_baseline(x)
+            got = o_host[rows[:, 0], rows[:, 1], rows[:, 2]]
+            parity = parity_record(got, ref, float(np.abs(x.v).max()), c.dtype,
+                                   "%d uniformly drawn query rows (the CPU baseline's sample)"
+                                   % len(rows))
 
     rec = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
@@ -444,6 +617,8 @@ def main():
         "frac_of_peak": value / PEAK_TFLOPS[arith],
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": parity,
+        "clock": None if clk is None else clk.summary(),
         "launch_us": launch_us,
         "warm": warm,
         "wall_s_timed": wall,

@@ -122,21 +122,30 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
                                            Lq, Lk, (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
 }
 
-// The key-split path of sdpa_decode: bf16, d = 64, one 32-row wave per chunk.
+// The matrix-core path of sdpa_decode: bf16, d_k = d_v in {64, 128}, one 32-row
+// wave per chunk of keys.
 bool split_applies(int64_t Lq, int64_t d_k, int64_t d_v, sdpa_dtype dtype)
 {
-    return dtype == SDPA_BF16 && d_k == 64 && d_v == 64 && Lq >= 1 && Lq <= 32;
+    return dtype == SDPA_BF16 && d_k == d_v && (d_k == 64 || d_k == 128) && Lq >= 1 && Lq <= 32;
 }
 
-// Chunks per head: enough workgroups to fill the chip (about 1536: three
-// one-wave workgroups per CU, two rounds) but at least two 64-key tiles per
-// chunk.  chunk is a multiple of 64; n_split * chunk >= Lk; n_split >= 1.
+// Chunks per head.  With many heads (at least kWgHeads: four waves per head
+// then give every CU a few waves), n_split = 0: each head's keys are split
+// over the four waves of one workgroup and merged in LDS.  Otherwise enough
+// chunks for about 1536 one-wave workgroups (three per CU, two rounds), at
+// least two 64-key tiles per chunk, merged by a second kernel (n_split = 1:
+// one chunk covers the head, no merge).  chunk is a multiple of 64;
+// n_split * chunk >= Lk.
+#ifndef SDPA_DECODE_WG_HEADS
+#define SDPA_DECODE_WG_HEADS 256
+#endif
 struct SplitPlan {
     int64_t chunk, n_split;
 };
 SplitPlan split_plan(int64_t n_bh, int64_t Lk)
 {
     constexpr int64_t kTarget = 1536, kTile = 64, kMinChunk = 2 * kTile;
+    if (n_bh >= SDPA_DECODE_WG_HEADS) return SplitPlan{Lk, 0};
     int64_t want = (kTarget + n_bh - 1) / n_bh;
     const int64_t most = (Lk + kMinChunk - 1) / kMinChunk;
     if (want > most) want = most;
@@ -147,10 +156,11 @@ SplitPlan split_plan(int64_t n_bh, int64_t Lk)
     return SplitPlan{chunk, (Lk + chunk - 1) / chunk > 0 ? (Lk + chunk - 1) / chunk : 1};
 }
 
-// fp32 acc [d_v = 64] plus m and l per (split, query row).
-int64_t split_workspace_bytes(int64_t n_bh, int64_t Lq, const SplitPlan &sp)
+// Partial results (fp32 acc [d_v], m and l per split and query row); none
+// when one chunk covers each head.
+int64_t split_workspace_bytes(int64_t n_bh, int64_t Lq, int64_t d_v, const SplitPlan &sp)
 {
-    return 4 * (64 + 2) * n_bh * sp.n_split * Lq;
+    return sp.n_split <= 1 ? 0 : 4 * (d_v + 2) * n_bh * sp.n_split * Lq;
 }
 
 // ---- device scratch of sdpa_decode_noalloc
@@ -397,7 +407,7 @@ int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk
     if (B == 0 || H == 0 || Lq == 0) return 0;
     if (!split_applies(Lq, d_k, d_v, dtype)) return 0;
     const SplitPlan sp = split_plan(B * H, Lk);
-    return split_workspace_bytes(B * H, Lq, sp);
+    return split_workspace_bytes(B * H, Lq, d_v, sp);
 }
 
 sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
@@ -414,15 +424,17 @@ sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
         return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dtype, s);
 
     const SplitPlan sp = split_plan(B * H, Lk);
-    const int64_t need = split_workspace_bytes(B * H, Lq, sp);
-    if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
-    if (overlaps(workspace, need, Q, z.nq) || overlaps(workspace, need, K, z.nk) ||
-        overlaps(workspace, need, V, z.nv) || overlaps(workspace, need, out, z.no) ||
-        overlaps(workspace, need, key_lengths, 4 * B))
-        return SDPA_ERR_WORKSPACE;
+    const int64_t need = split_workspace_bytes(B * H, Lq, d_v, sp);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+        if (overlaps(workspace, need, Q, z.nq) || overlaps(workspace, need, K, z.nk) ||
+            overlaps(workspace, need, V, z.nv) || overlaps(workspace, need, out, z.no) ||
+            overlaps(workspace, need, key_lengths, 4 * B))
+            return SDPA_ERR_WORKSPACE;
+    }
     if (B * H * sp.n_split > kMaxWorkgroups || B * H * Lq > kMaxWorkgroups) return SDPA_ERR_BAD_SHAPE;
-    return hip_status(sdpa::launch_split_mfma_d64(Q, K, V, key_lengths, out, B, H, Lq, Lk, sp.chunk,
-                                                  sp.n_split, workspace, s));
+    return hip_status(sdpa::launch_decode(Q, K, V, key_lengths, out, B, H, Lq, Lk, (int)d_k, sp.chunk,
+                                          sp.n_split, need > 0 ? workspace : nullptr, s));
 }
 
 sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
@@ -437,16 +449,18 @@ sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
     if (!split_applies(Lq, d_k, d_v, dtype))
         return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dtype, s);
     const SplitPlan sp = split_plan(B * H, Lk);
-    const int64_t need = split_workspace_bytes(B * H, Lq, sp);
+    const int64_t need = split_workspace_bytes(B * H, Lq, d_v, sp);
     if (need > kScratchBytes) return SDPA_ERR_SCRATCH_LIMIT;
     if (B * H * sp.n_split > kMaxWorkgroups || B * H * Lq > kMaxWorkgroups) return SDPA_ERR_BAD_SHAPE;
-    int dev = -1;
-    hipError_t err = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
     void *ws = nullptr;
-    if (err == hipSuccess) err = device_scratch(dev, &ws);
-    if (err != hipSuccess) return hip_status(err);
-    return hip_status(sdpa::launch_split_mfma_d64(Q, K, V, key_lengths, out, B, H, Lq, Lk, sp.chunk,
-                                                  sp.n_split, ws, s));
+    if (need > 0) {
+        int dev = -1;
+        hipError_t err = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+        if (err == hipSuccess) err = device_scratch(dev, &ws);
+        if (err != hipSuccess) return hip_status(err);
+    }
+    return hip_status(sdpa::launch_decode(Q, K, V, key_lengths, out, B, H, Lq, Lk, (int)d_k, sp.chunk,
+                                          sp.n_split, ws, s));
 }
 
 }  // extern "C"

@@ -994,15 +994,17 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::k
 
 // Key-split kernel: one wave per workgroup, 32 query rows (Lq <= 32) against
 // one chunk of keys; workgroup w takes split s = w % n_split of head
-// bh = w / n_split and writes its partial result (SplitOut).  No causal mask.
-__global__ __launch_bounds__(64) void sdpa_split_mfma_d64_kernel(
+// bh = w / n_split and writes its partial result (SplitOut), or, with one
+// chunk per head (SPLIT = false), O itself.  No causal mask.
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(64) void sdpa_split_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, uint16_t *__restrict__ O,
     int H, int64_t Lq, int64_t Lk, float scale_log2, SplitOut so)
 {
-    // One wave, 32-key tiles: 24 KiB of LDS, so 6 workgroups (waves) per CU
-    // keep the cache streaming.
-    constexpr int NW = 1, NB = kSplitKeyBlocks, D = 64;
+    // One wave, 32-key tiles: 24 KiB of LDS at d = 64 (six workgroups per CU
+    // keep the cache streaming), 48 KiB at d = 128.
+    constexpr int NW = 1, NB = kSplitKeyBlocks;
     using A = Attn<NW, NB, D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride + A::kLdsPad];
     uint16_t *kbuf[A::kBuffers], *vbuf[A::kBuffers];
@@ -1017,14 +1019,153 @@ __global__ __launch_bounds__(64) void sdpa_split_mfma_d64_kernel(
     const int64_t kv_lo = (int64_t)(u % so.n_split) * so.chunk;
     int64_t kv_hi = kv_lo + so.chunk;
     kv_hi = kv_hi < Lk ? kv_hi : Lk;
-    attend_query_tile<NW, NB, D, true>(kbuf, vbuf, Q, K, V, key_lengths, 0, nullptr, H, Lq, Lk,
-                                    scale_log2, bh, 0, 0, lane, kv_lo, kv_hi, so, u);
+    attend_query_tile<NW, NB, D, SPLIT>(kbuf, vbuf, Q, K, V, key_lengths, 0, O, H, Lq, Lk,
+                                        scale_log2, bh, 0, 0, lane, kv_lo, kv_hi, so, u);
 }
 
-// Merge of the split partial results: block = one wave, lane d = output dim d
-// of row i of head bh (block bh * Lq + i).  Lane s of each group of 64 splits
-// loads that split's m and l (all loads of a group at once); with
-// M = max_s m_s and w_s = exp2(m_s - M) (0 for a split without legal keys):
+// Decode step with the keys of one head split over the four waves of one
+// workgroup (many heads: no partial results leave the workgroup).  Wave w takes
+// keys [w c, (w + 1) c) of its head (c = the head's key length over four, in
+// whole 32-key tiles) with a two-buffer ring of its own in LDS, then writes its
+// partial result (reference maximum m, weight sum l, unnormalised sum of
+// weighted V rows, all per query row) into that LDS space; after a barrier the
+// workgroup merges them:
+//   O = sum_w e^(m_w - M) acc_w / sum_w e^(m_w - M) l_w,   M = max_w m_w
+// (base 2 in the kernel; a wave without keys contributes nothing; no key at
+// all gives 0).  Lq <= 32 rows, no causal mask.
+constexpr int kDecodeWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecodeWaves) void sdpa_decode_wg_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths,
+    uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2)
+{
+    constexpr int NW = kDecodeWaves, BN = 32;
+    using A = Attn<1, 1, D>;
+    constexpr int kD = D, kRowBytes = A::kRowBytes, kKB = A::kKB, kDB = A::kDB;
+    constexpr int kWaveLds = 2 * A::kBufStride;           // two K+V tile buffers per wave
+    static_assert(32 * kD * 4 + 2 * 32 * 4 <= 2 * kWaveLds, "a wave's partial result fits its LDS");
+    constexpr int kCopies = 2 * A::kBufStride / 1024;       // copy instructions per tile (K and V)
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NW * kWaveLds];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const uint32_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    int64_t len = Lk;
+    if (key_lengths) {
+        const int64_t l = key_lengths[b];
+        len = l < 0 ? 0 : (l > Lk ? Lk : l);
+    }
+    const int64_t c = ((len + NW - 1) / NW + BN - 1) / BN * BN;
+    const int64_t kv_lo = wave * c;
+    int64_t n = (kv_lo + c < len ? kv_lo + c : len) - kv_lo;
+    n = n < 0 ? 0 : n;
+    const int nt = (int)((n + BN - 1) / BN);
+
+    A st;
+    st.causal = 0;
+    st.scale_log2 = scale_log2;
+    st.g = g;
+    st.q0w = 0;
+    st.l32 = l32;
+    st.wave = 0;
+    st.len = n;
+    st.n_tiles = nt;
+    st.Kh = K + ((int64_t)bh * Lk + kv_lo) * kD;
+    st.Vh = V + ((int64_t)bh * Lk + kv_lo) * kD;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb) {
+            const int pos = bk * 32 + l32;
+            st.koff[bk][kb] = 2 * (pos * kD + (((2 * kb + g) ^ swz<D>(pos)) << 3));
+        }
+    {
+        const int i = lane & 15;
+        const int G1 = (lane >> 4) & 1;
+        const int row = 8 * g + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+            const int col = 32 * db + 16 * G1 + 4 * (i & 3);
+            st.voff[db] = 2 * (row * kD + ((((col >> 3) ^ swz_v<D>(row))) << 3) + (col & 7));
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    st.ld.init(0, lane);
+
+    uint16_t *const mine = lds + wave * kWaveLds;
+    uint16_t *kb[2] = {mine, mine + A::kBufStride};
+    uint16_t *vb[2] = {mine + A::kTileElems, mine + A::kBufStride + A::kTileElems};
+    int64_t rows_here = Lq < 32 ? Lq : 32;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Q + (int64_t)bh * Lq * kD), (short)0, (int)rows_here * kRowBytes, kBufferRsrcWord3);
+    if (nt > 0) st.ld.issue(st.Kh, st.Vh, 0, n, kb[0], vb[0]);
+    if (nt > 1) st.ld.issue(st.Kh, st.Vh, BN, n, kb[1], vb[1]);
+#pragma unroll
+    for (int kb2 = 0; kb2 < kKB; ++kb2)
+        st.qf[kb2] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
+            rq, (uint32_t)(l32 * kRowBytes + (kb2 * 16 + g * 8) * 2), 0, 0));
+#pragma unroll
+    for (int kb2 = 0; kb2 < kKB; ++kb2) asm volatile("" ::"v"(st.qf[kb2]));
+    for (int t = 0; t < nt; ++t) {
+        // this wave's copies of tile t have landed (those of tile t+1 may not)
+        if (t + 1 < nt) wait_vmem_keep<kCopies>();
+        else wait_vmem_keep<0>();
+        const int64_t rem = n - (int64_t)t * BN;
+        st.tile_blocks_masked(kb[t & 1], vb[t & 1], (int)(rem < BN ? rem : BN));
+        // the tile's operands are in registers (the products consumed them):
+        // its buffer takes tile t+2
+        if (t + 2 < nt) st.ld.issue(st.Kh, st.Vh, (int64_t)(t + 2) * BN, n, kb[t & 1], vb[t & 1]);
+    }
+
+    // this wave's partial result into its own LDS space: acc [32 rows][D], m [32], l [32]
+    acc_read_fence();
+    const float l_tot = sum_across_halves(st.l_run);
+    float *part = (float *)mine;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            part[l32 * kD + 32 * db + 8 * (r >> 2) + 4 * g + (r & 3)] = st.acc[db][r];
+    if (g == 0) {
+        part[32 * kD + l32] = st.m_run;
+        part[32 * kD + 32 + l32] = l_tot;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rows_here * kD; idx += 64 * NW) {
+        const int i = idx / kD, d = idx % kD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ((const float *)(lds + w * kWaveLds))[32 * kD + i]);
+        float num = 0.f, den = 0.f;
+        if (M > -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float *pw = (const float *)(lds + w * kWaveLds);
+                const float mw = pw[32 * kD + i];
+                const float e = mw > -INFINITY ? __builtin_amdgcn_exp2f(mw - M) : 0.f;
+                num += e * pw[i * kD + d];
+                den += e * pw[32 * kD + 32 + i];
+            }
+        }
+        const float o = den > 0.f ? num / den : 0.f;
+        O[((int64_t)bh * Lq + i) * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
+    }
+}
+
+// Merge of the split partial results: block = one wave for row i of head bh
+// (block bh * Lq + i); lane t handles output dims t, t + 64, ...  Lane s of
+// each group of 64 splits loads that split's m and l (all loads of a group at
+// once); with M = max_s m_s and w_s = exp2(m_s - M) (0 for a split without
+// legal keys):
 //   O = sum_s w_s acc_s / sum_s w_s l_s   (0 if no split has a key).
 __device__ inline float wave_max(float x)
 {
@@ -1039,25 +1180,28 @@ __device__ inline float wave_sum(float x)
     return x;
 }
 
-__global__ __launch_bounds__(64) void sdpa_split_merge_d64_kernel(
+template <int D>
+__global__ __launch_bounds__(64) void sdpa_split_merge_kernel(
     const float *__restrict__ acc, const float *__restrict__ m, const float *__restrict__ l,
     uint16_t *__restrict__ O, int64_t Lq, uint32_t n_split)
 {
-    constexpr int kD = 64;
-    const int d = threadIdx.x;
+    constexpr int kD = D, kPer = D / 64;   // output dims per lane
+    const int t = threadIdx.x;
     const int64_t row = blockIdx.x;                 // bh * Lq + i
     const int64_t bh = row / Lq, i = row % Lq;
     const int64_t u0 = bh * n_split;
     float M = -INFINITY;
     for (uint32_t s0 = 0; s0 < n_split; s0 += 64)
-        if (s0 + d < n_split) M = fmaxf(M, m[(u0 + s0 + d) * Lq + i]);
+        if (s0 + t < n_split) M = fmaxf(M, m[(u0 + s0 + t) * Lq + i]);
     M = wave_max(M);
-    float num = 0.f, den = 0.f;
+    float num[kPer], den = 0.f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) num[e] = 0.f;
     if (M > -INFINITY) {
         for (uint32_t s0 = 0; s0 < n_split; s0 += 64) {
             float w = 0.f;
-            if (s0 + d < n_split) {
-                const int64_t r = (u0 + s0 + d) * Lq + i;
+            if (s0 + t < n_split) {
+                const int64_t r = (u0 + s0 + t) * Lq + i;
                 const float ms = m[r];
                 if (ms > -INFINITY) {
                     w = __builtin_amdgcn_exp2f(ms - M);
@@ -1065,21 +1209,68 @@ __global__ __launch_bounds__(64) void sdpa_split_merge_d64_kernel(
                 }
             }
             const uint32_t n = n_split - s0 < 64 ? n_split - s0 : 64;
-            const float *a = acc + ((u0 + s0) * Lq + i) * kD + d;
-            for (uint32_t t0 = 0; t0 < n; t0 += 8) {   // 8 independent loads in flight
-                float x[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = t0 + j < n ? a[(int64_t)(t0 + j) * Lq * kD] : 0.f;
+            const float *a = acc + ((u0 + s0) * Lq + i) * kD + t;
+            for (uint32_t t0 = 0; t0 < n; t0 += 8) {   // 8 independent loads in flight per dim
+                float x[8][kPer];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    num += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w),
-                                                                               (t0 + j) & 63)) * x[j];
+#pragma unroll
+                    for (int e = 0; e < kPer; ++e)
+                        x[j][e] = t0 + j < n ? a[(int64_t)(t0 + j) * Lq * kD + 64 * e] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float wj = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (t0 + j) & 63));
+#pragma unroll
+                    for (int e = 0; e < kPer; ++e) num[e] += wj * x[j][e];
+                }
             }
         }
         den = wave_sum(den);
     }
-    const float o = den > 0.f ? num / den : 0.f;
-    O[row * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const float o = den > 0.f ? num[e] / den : 0.f;
+        O[row * kD + t + 64 * e] = __builtin_bit_cast(uint16_t, (__bf16)o);
+    }
+}
+
+template <int D>
+hipError_t launch_decode_d(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                           void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t chunk,
+                           int64_t n_split, void *workspace, hipStream_t stream)
+{
+    const int64_t n_bh = B * H;
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    if (n_split == 0) {
+        // Many heads: the keys of each head split over the four waves of its
+        // workgroup, merged in LDS.
+        hipLaunchKernelGGL((sdpa_decode_wg_kernel<D>), dim3((uint32_t)n_bh), dim3(64 * kDecodeWaves), 0,
+                           stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                           key_lengths, (uint16_t *)out, (int)H, Lq, Lk, scale_log2);
+        return hipGetLastError();
+    }
+    if (n_split == 1) {
+        // One chunk per head: each one-wave workgroup writes O itself; no
+        // partial results, no merge.
+        const SplitOut whole{nullptr, nullptr, nullptr, Lk, 1u};
+        hipLaunchKernelGGL((sdpa_split_mfma_kernel<D, false>), dim3((uint32_t)n_bh), dim3(64), 0, stream,
+                           (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths,
+                           (uint16_t *)out, (int)H, Lq, Lk, scale_log2, whole);
+        return hipGetLastError();
+    }
+    const int64_t n_rows = n_bh * n_split * Lq;
+    float *ws = (float *)workspace;
+    const SplitOut so{ws, ws + n_rows * D, ws + n_rows * (D + 1), chunk, (uint32_t)n_split};
+    hipLaunchKernelGGL((sdpa_split_mfma_kernel<D, true>), dim3((uint32_t)(n_bh * n_split)), dim3(64), 0,
+                       stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths,
+                       nullptr, (int)H, Lq, Lk, scale_log2, so);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((sdpa_split_merge_kernel<D>), dim3((uint32_t)(n_bh * Lq)), dim3(64), 0, stream,
+                       (const float *)so.acc, (const float *)so.m, (const float *)so.l, (uint16_t *)out,
+                       Lq, (uint32_t)n_split);
+    return hipGetLastError();
 }
 
 template <int D>
@@ -1162,25 +1353,15 @@ hipError_t launch_mfma(const void *Q, const void *K, const void *V, const int32_
     }
 }
 
-hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
-                                 const int32_t *key_lengths, void *out, int64_t B, int64_t H,
-                                 int64_t Lq, int64_t Lk, int64_t chunk, int64_t n_split,
-                                 void *workspace, hipStream_t stream)
+hipError_t launch_decode(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                         void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
+                         int64_t chunk, int64_t n_split, void *workspace, hipStream_t stream)
 {
-    const int64_t n_bh = B * H, n_rows = n_bh * n_split * Lq;
-    float *ws = (float *)workspace;
-    constexpr int kD = 64;
-    const SplitOut so{ws, ws + n_rows * kD, ws + n_rows * (kD + 1), chunk, (uint32_t)n_split};
-    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)kD));
-    hipLaunchKernelGGL(sdpa_split_mfma_d64_kernel, dim3((uint32_t)(n_bh * n_split)), dim3(64), 0, stream,
-                       (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths,
-                       (int)H, Lq, Lk, scale_log2, so);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(sdpa_split_merge_d64_kernel, dim3((uint32_t)(n_bh * Lq)), dim3(64), 0, stream,
-                       (const float *)so.acc, (const float *)so.m, (const float *)so.l, (uint16_t *)out,
-                       Lq, (uint32_t)n_split);
-    return hipGetLastError();
+    switch (d) {
+    case 64: return launch_decode_d<64>(Q, K, V, key_lengths, out, B, H, Lq, Lk, chunk, n_split, workspace, stream);
+    case 128: return launch_decode_d<128>(Q, K, V, key_lengths, out, B, H, Lq, Lk, chunk, n_split, workspace, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace sdpa

@@ -40,14 +40,16 @@ hipError_t launch_mfma_band(const void *Q, const void *K, const void *V,
                             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
                             hipStream_t stream);
 
-// bf16, d_k = d_v = 64, Lq <= 32, no causal mask: keys split into n_split chunks
-// of `chunk` keys per head (chunk a multiple of 64, n_split * chunk >= Lk),
-// partial results in `workspace` (4 * 66 * B * H * n_split * Lq bytes), then
-// merged into out.  Two kernels on `stream`.
-hipError_t launch_split_mfma_d64(const void *Q, const void *K, const void *V,
-                                 const int32_t *key_lengths, void *out, int64_t B, int64_t H,
-                                 int64_t Lq, int64_t Lk, int64_t chunk, int64_t n_split,
-                                 void *workspace, hipStream_t stream);
+// Decode step, bf16, d_k = d_v = d in {64, 128}, Lq <= 32, no causal mask.
+// n_split == 0: one four-wave workgroup per head, its keys split over the
+// waves and merged in LDS (workspace unused).  n_split == 1: one one-wave
+// workgroup per head writes out directly (workspace unused).  n_split > 1: keys split into n_split chunks of `chunk` keys per head
+// (chunk a multiple of 64, n_split * chunk >= Lk), partial results in
+// `workspace` (4 * (d + 2) * B * H * n_split * Lq bytes), then merged into out
+// (two kernels on `stream`).
+hipError_t launch_decode(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                         void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
+                         int64_t chunk, int64_t n_split, void *workspace, hipStream_t stream);
 
 // Projection products of multi-head attention, C = A W on the matrix cores
 // (bf16, fp32 accumulation), tiles of 128 x 128 or 256 x 256 elements of C

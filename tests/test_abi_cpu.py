@@ -114,7 +114,9 @@ def test_python_multihead_rejects_bad_arguments_without_gpu():
 
 # ---- sdpa_decode: the same host-side checks, plus the workspace
 
-def dcall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=2, H=2, Lq=1, Lk=128,
+# Default shape: keys split over three chunks (a workspace is needed), every
+# buffer inside its 64 KiB slot of fake addresses.
+def dcall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=1, H=1, Lq=1, Lk=300,
           dk=64, dv=64, dtype=sdpa.SDPA_BF16, ws=0x1000000, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = sdpa.sdpa_decode_workspace_bytes(B, H, Lq, Lk, dk, dv, dtype)
@@ -133,7 +135,16 @@ def test_decode_workspace_bytes():
     assert ws(4, 16, 1, 8192, 64, 64, f32) == 0
     assert ws(4, 16, 1, 8192, 32, 32, bf) == 0
     assert ws(0, 16, 1, 8192, 64, 64, bf) == 0          # empty call
-    assert ws(4, 16, 1, 0, 64, 64, bf) == 4 * 66 * 64   # no keys: one (empty) chunk
+    assert ws(4, 16, 1, 0, 64, 64, bf) == 0             # no keys: one (empty) chunk, no merge
+    assert ws(1, 1, 1, 100, 64, 64, bf) == 0            # one chunk per head: no merge
+    # d = 128 takes the same path: 4 * (d_v + 2) bytes per split and row
+    one128 = ws(4, 8, 1, 8192, 128, 128, bf)
+    assert one128 > 0 and one128 % (4 * 130 * 32) == 0
+    # at least 256 heads: one four-wave workgroup per head, merged in LDS
+    assert ws(64, 8, 1, 256, 64, 64, bf) == 0
+    assert ws(64, 8, 32, 1024, 128, 128, bf) == 0
+    assert ws(2, 100, 1, 1025, 64, 64, bf) > 0          # 200 heads: keys split over workgroups
+    assert ws(4, 16, 1, 8192, 256, 256, bf) == 0        # head size outside the path
     # sizes the entry point rejects
     assert ws(-1, 16, 1, 8192, 64, 64, bf) == -1
     assert ws(4, 16, 1, 8192, 513, 64, bf) == -1
@@ -147,7 +158,7 @@ def test_decode_workspace_bytes():
     (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(O=FAKE_Q), sdpa.SDPA_ERR_ALIAS),
     (dict(ws=0), sdpa.SDPA_ERR_WORKSPACE),
-    (dict(ws_bytes=1024), sdpa.SDPA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), sdpa.SDPA_ERR_WORKSPACE),        # the plan needs 792 bytes
     (dict(ws=FAKE_V + 64), sdpa.SDPA_ERR_WORKSPACE),     # overlaps V
     (dict(ws=FAKE_O - 64), sdpa.SDPA_ERR_WORKSPACE),     # overlaps out
 ])
@@ -182,8 +193,8 @@ def test_noalloc_scratch_size_matches_header():
     (dict(B=-1), sdpa.SDPA_ERR_BAD_SHAPE),
     (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(O=FAKE_K + 64), sdpa.SDPA_ERR_ALIAS),
-    # 2048 heads x 32 rows in one chunk each: 17.3 MB of partial results
-    (dict(Q=1 << 32, K=2 << 32, V=3 << 32, O=4 << 32, B=1, H=2048, Lq=32, Lk=256),
+    # 255 heads x 32 rows in seven chunks each, d = 128: 29.7 MB of partial results
+    (dict(Q=1 << 32, K=2 << 32, V=3 << 32, O=4 << 32, B=1, H=255, Lq=32, Lk=8192, dk=128, dv=128),
      sdpa.SDPA_ERR_SCRATCH_LIMIT),
 ])
 def test_noalloc_prelaunch_validation(kw, expected):
@@ -192,7 +203,7 @@ def test_noalloc_prelaunch_validation(kw, expected):
 
 def test_noalloc_limit_is_the_workspace_size():
     ws = sdpa.sdpa_decode_workspace_bytes
-    assert ws(1, 2048, 32, 256, 64, 64, sdpa.SDPA_BF16) > sdpa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert ws(1, 255, 32, 8192, 128, 128, sdpa.SDPA_BF16) > sdpa.DECODE_NOALLOC_SCRATCH_BYTES
     assert ws(4, 16, 1, 8192, 64, 64, sdpa.SDPA_BF16) <= sdpa.DECODE_NOALLOC_SCRATCH_BYTES
     assert "static device scratch" in sdpa.sdpa_status_str(sdpa.SDPA_ERR_SCRATCH_LIMIT)
 

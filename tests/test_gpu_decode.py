@@ -1,10 +1,12 @@
 """GPU parity of sdpa_decode (decode-step attention over a long key/value cache)
 against the fp64 oracle with causal = 0, through the C ABI.
 
-The key-split path (bf16, d = 64, Lq <= 32) is checked on cache lengths that
-cross the 64-key tiles and the chunk boundaries, with key lengths that end
-inside a chunk, at a chunk boundary, at 0 and past Lk; the other shapes must run
-the forward kernels and give exactly sdpa_forward's result.
+The matrix-core decode path (bf16, d_k = d_v in {64, 128}, Lq <= 32) is checked
+on cache lengths that cross the key tiles and the chunk boundaries, with key
+lengths that end inside a chunk, at a chunk boundary, at 0 and past Lk, both
+with keys split over workgroups (log-sum-exp merge) and with one workgroup per
+head (many heads, short caches: no merge); the other shapes must run the
+forward kernels and give exactly sdpa_forward's result.
 """
 import numpy as np
 import pytest
@@ -37,21 +39,38 @@ SPLIT_CASES = [
     (2, 2, 32, 2048, [2048, 129]),               # a full wave of query rows
     (1, 1, 1, 1, None),                          # one key
     (1, 1, 3, 63, None),                         # less than one tile
-    (64, 8, 1, 256, "uniform"),                  # base model decode step, many heads
     (1, 1, 1, 32768 + 5, None),                  # one head: many chunks
+]
+# at least 256 heads: each head's keys split over the four waves of one
+# workgroup and merged in LDS, no workspace; lengths that leave some waves
+# without keys (1..96 keys) or all of them (0)
+DIRECT_CASES = [
+    (64, 8, 1, 256, "uniform"),                  # base model decode step
+    (64, 8, 7, 1000, [1000, 0, 33, 999] * 16),   # several rows, lengths 0 and in the tail
+    (128, 4, 32, 1024, "uniform"),
+    (512, 1, 1, 65, None),
+    (256, 1, 3, 100, [5, 96, 97, 1] * 64),
+    (4, 64, 1, 8192 + 3, [8192 + 3, 4000, 31, 8192]),   # long caches, 256 heads
 ]
 
 
-@pytest.mark.parametrize("case", SPLIT_CASES, ids=[str(c[:4]) for c in SPLIT_CASES])
-def test_split_path_parity(case):
+def _split_ids(cases, d):
+    return ["d%d-%s" % (d, c[:4]) for c in cases]
+
+
+@pytest.mark.parametrize("case,d", [(c, d) for d in (64, 128) for c in SPLIT_CASES + DIRECT_CASES],
+                         ids=_split_ids(SPLIT_CASES + DIRECT_CASES, 64) +
+                         _split_ids(SPLIT_CASES + DIRECT_CASES, 128))
+def test_split_path_parity(case, d):
     B, H, Lq, Lk, lengths = case
-    seed = 1000 + B * 7 + Lq * 13 + Lk
-    q, k, v, _ = workloads.draw(B, H, Lq, Lk, 64, 64, dtype="bf16", seed=seed)
+    seed = 1000 + B * 7 + Lq * 13 + Lk + d
+    q, k, v, _ = workloads.draw(B, H, Lq, Lk, d, d, dtype="bf16", seed=seed)
     if lengths == "uniform":
         lengths = list(np.random.default_rng(seed).integers(1, Lk, size=B, endpoint=True))
-    need = sdpa.sdpa_decode_workspace_bytes(B, H, Lq, Lk, 64, 64, sdpa.SDPA_BF16)
-    assert need > 0
-    announce("decode split B=%d H=%d Lq=%d Lk=%d" % (B, H, Lq, Lk))
+    need = sdpa.sdpa_decode_workspace_bytes(B, H, Lq, Lk, d, d, sdpa.SDPA_BF16)
+    if case in DIRECT_CASES:
+        assert need == 0
+    announce("decode d=%d B=%d H=%d Lq=%d Lk=%d" % (d, B, H, Lq, Lk))
     got = decode(q, k, v, lengths)
     ref = oracle.attention(q, k, v, key_lengths=lengths, causal=False)
     assert_parity(got, ref, v, "bf16", "decode %s" % (case[:4],))
@@ -104,7 +123,7 @@ def test_workspace_too_small_raises():
 
 
 @pytest.mark.parametrize("dtype,d,Lq", [("f32", 64, 1), ("bf16", 32, 2), ("bf16", 64, 33),
-                                     ("bf16", 128, 1), ("bf16", 512, 1)])
+                                     ("bf16", 128, 33), ("bf16", 512, 1)])
 def test_other_shapes_run_the_forward_kernels(dtype, d, Lq):
     """No split path: sdpa_decode must give exactly sdpa_forward(causal=0)."""
     B, H, Lk = 2, 2, 300

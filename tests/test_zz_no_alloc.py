@@ -26,12 +26,13 @@ def _inputs(B, H, Lq, Lk, d, lengths, seed):
     return (q, k, v), (dq, dk, dv), kl
 
 
-# (B, H, Lq, Lk, d, lengths): the long decode step, then a smaller one with
-# padding (both on the key-split path), then a head size outside it
+# (B, H, Lq, Lk, d, lengths): the long decode step, then smaller ones with
+# padding (on the key-split path, d = 64 and 128), then a head size outside it
 CALLS = [
     (4, 16, 1, 8192, 64, None),
     (2, 4, 5, 3000, 64, [3000, 1234]),
     (1, 2, 3, 700, 128, [650]),
+    (1, 2, 3, 300, 256, [250]),
 ]
 
 
@@ -62,13 +63,13 @@ def test_noalloc_scratch_limit():
     """A split plan larger than the static scratch is refused before any launch,
     and the output is left untouched."""
     dev = require_gpu()
-    B, H, Lq, Lk = 1, 2048, 32, 256
-    need = sdpa.sdpa_decode_workspace_bytes(B, H, Lq, Lk, 64, 64, sdpa.SDPA_BF16)
+    B, H, Lq, Lk, d = 1, 255, 32, 8192, 128
+    need = sdpa.sdpa_decode_workspace_bytes(B, H, Lq, Lk, d, d, sdpa.SDPA_BF16)
     assert need > sdpa.DECODE_NOALLOC_SCRATCH_BYTES
-    q = torch.zeros((B, H, Lq, 64), dtype=torch.bfloat16, device=dev)
-    k = torch.zeros((B, H, Lk, 64), dtype=torch.bfloat16, device=dev)
+    q = torch.zeros((B, H, Lq, d), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((B, H, Lk, d), dtype=torch.bfloat16, device=dev)
     v = torch.zeros_like(k)
-    out = torch.full((B, H, Lq, 64), 7.0, dtype=torch.bfloat16, device=dev)
+    out = torch.full((B, H, Lq, d), 7.0, dtype=torch.bfloat16, device=dev)
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.decode_noalloc(q, k, v, out)
     assert e.value.status == sdpa.SDPA_ERR_SCRATCH_LIMIT

@@ -140,6 +140,18 @@ CONFIGS = {
         "one new position against caches of up to 256 positions", "bf16",
         B=64, H=8, Lq=1, Lk=256, d_k=64, d_v=64, causal=False, key_len_range=(64, 256),
         scale=1.0, seed=6, entry="decode"),
+    # Table 3 row (A), h = 4 heads of d_k = d_v = 128, decode steps
+    "decode_long_d128_bf16": Config(
+        "decode_long_d128_bf16", "decode step after the long sequence, h = 4 heads of "
+        "d_k = d_v = 128 (Table 3 row A): one new position per head against an 8192-key cache, "
+        "inputs scaled by 0.5", "bf16",
+        B=4, H=4, Lq=1, Lk=8192, d_k=128, d_v=128, causal=False, key_len_range=None,
+        scale=0.5, seed=17, entry="decode"),
+    "decode_base_d128_bf16": Config(
+        "decode_base_d128_bf16", "base-model decode step with h = 4 heads of d_k = d_v = 128 "
+        "(Table 3 row A): 64 sequences, caches of up to 256 positions", "bf16",
+        B=64, H=4, Lq=1, Lk=256, d_k=128, d_v=128, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=18, entry="decode"),
 }
 
 #: Configuration order used by tests and reports (smallest first): the five
@@ -149,7 +161,8 @@ ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
          "rowA_h16_d32_encoder_bf16", "rowA_h32_d16_encoder_bf16", "rowA_h1_d512_encoder_bf16",
          "long_causal_d128_bf16", "restricted_long_bf16",
          "restricted_long_causal_bf16", "mha_base_encoder_bf16", "mha_big_cross_bf16",
-         "mha_long_causal_bf16", "decode_base_bf16", "decode_long_bf16"]
+         "mha_long_causal_bf16", "decode_base_bf16", "decode_long_bf16", "decode_base_d128_bf16",
+         "decode_long_d128_bf16"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:

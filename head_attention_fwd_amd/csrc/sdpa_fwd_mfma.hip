@@ -98,23 +98,32 @@ struct Occupancy {
 };
 
 // 16-byte chunk swizzles of a row of D bf16 values (D/8 chunks), XORed into
-// the chunk index (for D = 128 only its low three bits, within each half row).
-// K (and Q) rows: rows r and r' that a wave reads in the same LDS cycle get
-// different chunk positions (D >= 64: injective on any 8 consecutive rows and
-// on the 8 even or 8 odd rows of any 16 consecutive rows; D = 32, four rows per
-// 256 bytes: rows r and r + 4 differ).
+// the chunk index.  The LDS serves 64 banks of 4 bytes per cycle: 16 lanes of
+// a 16-byte read, 32 lanes of an 8-byte one.  K (and Q) rows: the 16 rows that
+// the 16 lanes of one cycle read get distinct bank ranges.  D = 128: rows of
+// 256 bytes all start at bank 0, so 16 rows need 16 distinct chunk positions
+// (row mod 16).  D = 64: two rows per 256 bytes; injective on any 8
+// consecutive rows and on the 8 even or 8 odd rows of any 16 consecutive rows.
+// D = 32, four rows per 256 bytes: rows r and r + 4 differ.
 template <int D>
 __device__ inline int swz(int row)
 {
     // D = 16: rows of 32 bytes; 8 consecutive rows at one chunk already cover
     // 8 distinct bank groups
-    return D >= 64 ? (row ^ (row >> 3)) & 7 : (D >= 32 ? (row >> 2) & 3 : 0);
+    return D >= 128 ? row & 15 : (D >= 64 ? (row ^ (row >> 3)) & 7 : (D >= 32 ? (row >> 2) & 3 : 0));
 }
 
-// V rows: the 4 rows one ds_read_b64_tr_b16 group touches get disjoint chunk
-// pairs (D = 32: the two 16-dim halves of a row stay apart).
+// V rows: the 4 rows that one 16-lane group of ds_read_b64_tr_b16 touches (32
+// bytes, two chunks, of each) get disjoint bank ranges, and so do the two
+// groups of one cycle.  D = 128: each row's 64-byte quarter q moves to quarter
+// q ^ (row mod 4), so 4 rows x 64 bytes cover all 64 banks.  D = 64: chunk
+// pairs XOR (row mod 4) * 2 (two rows per 256 bytes).  D = 32: the two 16-dim
+// halves of a row stay apart.
 template <int D>
-__device__ inline int swz_v(int row) { return D >= 64 ? (row & 3) << 1 : (D >= 32 ? (row & 1) << 1 : 0); }
+__device__ inline int swz_v(int row)
+{
+    return D >= 128 ? (row & 3) << 2 : (D >= 64 ? (row & 3) << 1 : (D >= 32 ? (row & 1) << 1 : 0));
+}
 
 // Key row order fed to the score MFMA: swap bits 2 and 3 (an involution).
 __device__ inline int pi32(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }

@@ -13,6 +13,7 @@ headline lines.
                   [--no-cpu-baseline] [--rotate R] [--settle-ms MS]
   python bench.py --copy-mib 512      (calibration: a plain device copy)
   python bench.py --gemm-probe 8192   (calibration: a bf16 GEMM through torch)
+  python bench.py --overlap-probe 20000   (calibration: matrix-core / VALU overlap)
 
 After the W warmup steps, untimed steps continue until the GPU has been busy for
 --settle-ms (default 150 ms), so that the K timed steps see the settled clock.
@@ -322,6 +323,58 @@ def gemm_probe(torch, dev, args):
                       "clock": clk.summary()}), flush=True)
 
 
+def overlap_probe(torch, dev, args):
+    """Calibration, not the product: how far a matrix-core stream and a vector-ALU
+    stream from different waves on one SIMD run at the same time (kernels in
+    libsdpa_calib.so): times of the matrix stream alone, the vector stream alone
+    and both together, with the accumulators in VGPRs or accumulation registers."""
+    import ctypes
+    from head_attention_fwd_amd import build as hb
+    if not os.path.exists(hb.CALIB_LIBRARY):
+        raise RuntimeError("libsdpa_calib.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(hb.CALIB_LIBRARY)
+    lib.sdpa_calib_overlap.restype = ctypes.c_int
+    lib.sdpa_calib_overlap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p]
+    n_wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    iters = args.overlap_probe
+
+    def timed(mode, which):
+        def go():
+            rc = lib.sdpa_calib_overlap(mode, which, out.data_ptr(), n_wg, iters, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("sdpa_calib_overlap: hipError %d" % rc)
+        for _ in range(3):
+            go()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        with ClockSampler() as clk:
+            t0.record(stream)
+            for _ in range(40):
+                go()
+            t1.record(stream)
+            torch.cuda.synchronize()
+        return {"ms": t0.elapsed_time(t1) / 40, "clock": clk.summary()}
+
+    # settle the clock first (both streams, untimed)
+    t_busy = time.perf_counter()
+    while (time.perf_counter() - t_busy) * 1e3 < max(args.settle_ms, 300.0):
+        if lib.sdpa_calib_overlap(0, 2, out.data_ptr(), n_wg, iters, stream.cuda_stream) != 0:
+            raise RuntimeError("sdpa_calib_overlap failed")
+        torch.cuda.synchronize()
+    res = {}
+    for mode, name in ((0, "vgpr_accumulators"), (1, "accumulation_registers")):
+        r = {k: timed(mode, w) for k, w in (("matrix_only", 0), ("vector_only", 1), ("both", 2))}
+        r["both_over_sum"] = r["both"]["ms"] / (r["matrix_only"]["ms"] + r["vector_only"]["ms"])
+        res[name] = r
+    print(json.dumps({"probe": "matrix-core / vector-ALU overlap on one SIMD, calibration only",
+                      "workgroups": n_wg, "waves": "4 matrix + 4 vector per CU",
+                      "per_iteration": "4 v_mfma_f32_32x32x16_bf16 / 32 v_fma_f32",
+                      "iterations": iters, **res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +391,9 @@ def main():
     ap.add_argument("--gemm-probe", type=int, default=0,
                     help="instead of attention, time a bf16 N x N x N GEMM through torch "
                          "(calibration: what a dense matrix-core kernel reaches on this GPU)")
+    ap.add_argument("--overlap-probe", type=int, default=0,
+                    help="instead of attention, run the matrix-core / vector-ALU overlap probe "
+                         "with this many iterations (calibration; libsdpa_calib.so)")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="time the K steps as one replay of a captured HIP graph (no host "
                          "launch cost between steps); auto: on for the decode workloads, whose "
@@ -362,6 +418,9 @@ def main():
         return
     if args.gemm_probe:
         gemm_probe(torch, dev, args)
+        return
+    if args.overlap_probe:
+        overlap_probe(torch, dev, args)
         return
     x = workloads.generate(args.config)
     c = x.config

@@ -7,6 +7,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libsdpa.so")
+# calibration kernels for the measurements (bench.py --overlap-probe), not the attention path
+CALIB_LIBRARY = os.path.join(HERE, "libsdpa_calib.so")
+CALIB_SOURCES = ["sdpa_calib.hip"]
 SOURCES = ["sdpa_api.hip", "sdpa_fwd_generic.hip", "sdpa_fwd_mfma.hip", "sdpa_fwd_mfma_wide.hip",
            "sdpa_proj_gemm.hip"]
 ARCH = "gfx950"
@@ -23,11 +26,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into head_attention_fwd_amd/libsdpa.so."""
+def _hipcc(sources, target, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    tmp = target + ".tmp%d" % os.getpid()
+    cmd = [hipcc] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,11 +38,18 @@ def build(verbose: bool = False) -> str:
             if "packed-fp32-ops" not in l and l.strip()]
     if res.returncode != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError("hipcc failed building libsdpa.so")
+        raise RuntimeError("hipcc failed building %s" % os.path.basename(target))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, target)
+    return target
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source of the attention path into head_attention_fwd_amd/libsdpa.so,
+    and the calibration kernels into libsdpa_calib.so."""
+    _hipcc(CALIB_SOURCES, CALIB_LIBRARY, verbose)
+    return _hipcc(SOURCES, LIBRARY, verbose)
 
 
 if __name__ == "__main__":

@@ -104,13 +104,13 @@ struct Occupancy {
 // 256 bytes all start at bank 0, so 16 rows need 16 distinct chunk positions
 // (row mod 16).  D = 64: two rows per 256 bytes; injective on any 8
 // consecutive rows and on the 8 even or 8 odd rows of any 16 consecutive rows.
-// D = 32, four rows per 256 bytes: rows r and r + 4 differ.
+// D = 32, four rows per 256 bytes: rows r and r + 4 differ.  D = 16, eight rows
+// per 256 bytes: rows r and r + 8 differ.
 template <int D>
 __device__ inline int swz(int row)
 {
-    // D = 16: rows of 32 bytes; 8 consecutive rows at one chunk already cover
-    // 8 distinct bank groups
-    return D >= 128 ? row & 15 : (D >= 64 ? (row ^ (row >> 3)) & 7 : (D >= 32 ? (row >> 2) & 3 : 0));
+    // D = 16: rows of 32 bytes (two chunks); rows r and r + 8 swap chunks
+    return D >= 128 ? row & 15 : (D >= 64 ? (row ^ (row >> 3)) & 7 : (D >= 32 ? (row >> 2) & 3 : (row >> 3) & 1));
 }
 
 // V rows: the 4 rows that one 16-lane group of ds_read_b64_tr_b16 touches (32

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string.h>
+
 #include <initializer_list>
 #include <mutex>
 
@@ -15,6 +17,19 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// The C ABI declares enum parameters, but a caller may pass any integer there;
+// in C++ an enum object holding a value outside its enumerators' range may not
+// be read as the enum, so the entry points take its bytes as an int first.
+static_assert(sizeof(sdpa_dtype) == sizeof(int) && sizeof(sdpa_status) == sizeof(int),
+              "enums of the C ABI are int-sized");
+template <class E>
+int enum_value(const E &e)
+{
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
 
 constexpr int64_t kMaxHeadDim = 512;
 constexpr int64_t kMaxDim = INT32_MAX;
@@ -48,7 +63,7 @@ sdpa_status hip_status(hipError_t err)
 
 // Size checks shared by every entry point (no pointers involved).
 sdpa_status check_sizes(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_k, int64_t d_v,
-                        sdpa_dtype dtype)
+                        int dtype)
 {
     if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || d_k < 1 || d_v < 1) return SDPA_ERR_BAD_SHAPE;
     if (dtype != SDPA_F32 && dtype != SDPA_BF16) return SDPA_ERR_UNSUPPORTED;
@@ -75,7 +90,7 @@ struct Sizes {
 // Everything sdpa_forward checks before any HIP call.
 sdpa_status validate(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                      const void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d_k,
-                     int64_t d_v, sdpa_dtype dtype, Sizes &z)
+                     int64_t d_v, int dtype, Sizes &z)
 {
     const sdpa_status st = check_sizes(B, H, Lq, Lk, d_k, d_v, dtype);
     if (st != SDPA_OK) return st;
@@ -99,7 +114,7 @@ sdpa_status validate(const void *Q, const void *K, const void *V, const int32_t 
 // query row only (restricted self-attention).
 sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                             int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                            int64_t d_k, int64_t d_v, sdpa_dtype dtype, hipStream_t s,
+                            int64_t d_k, int64_t d_v, int dtype, hipStream_t s,
                             int64_t radius = -1)
 {
     // A radius that reaches every (query, key) pair restricts nothing: the
@@ -124,28 +139,25 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
 
 // The matrix-core path of sdpa_decode: bf16, d_k = d_v in {64, 128}, one 32-row
 // wave per chunk of keys.
-bool split_applies(int64_t Lq, int64_t d_k, int64_t d_v, sdpa_dtype dtype)
+bool split_applies(int64_t Lq, int64_t d_k, int64_t d_v, int dtype)
 {
     return dtype == SDPA_BF16 && d_k == d_v && (d_k == 64 || d_k == 128) && Lq >= 1 && Lq <= 32;
 }
 
-// Chunks per head.  With many heads (at least kWgHeads: four waves per head
-// then give every CU a few waves), n_split = 0: each head's keys are split
+// Chunks per head.  With many heads (at least kWgHeads = 256: four waves per
+// head then give every CU a few waves), n_split = 0: each head's keys are split
 // over the four waves of one workgroup and merged in LDS.  Otherwise enough
 // chunks for about 1536 one-wave workgroups (three per CU, two rounds), at
 // least two 64-key tiles per chunk, merged by a second kernel (n_split = 1:
 // one chunk covers the head, no merge).  chunk is a multiple of 64;
 // n_split * chunk >= Lk.
-#ifndef SDPA_DECODE_WG_HEADS
-#define SDPA_DECODE_WG_HEADS 256
-#endif
 struct SplitPlan {
     int64_t chunk, n_split;
 };
 SplitPlan split_plan(int64_t n_bh, int64_t Lk)
 {
-    constexpr int64_t kTarget = 1536, kTile = 64, kMinChunk = 2 * kTile;
-    if (n_bh >= SDPA_DECODE_WG_HEADS) return SplitPlan{Lk, 0};
+    constexpr int64_t kWgHeads = 256, kTarget = 1536, kTile = 64, kMinChunk = 2 * kTile;
+    if (n_bh >= kWgHeads) return SplitPlan{Lk, 0};
     int64_t want = (kTarget + n_bh - 1) / n_bh;
     const int64_t most = (Lk + kMinChunk - 1) / kMinChunk;
     if (want > most) want = most;
@@ -217,7 +229,7 @@ struct MhPlan {
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 sdpa_status mh_plan(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model, int64_t h, int64_t d_k,
-                    int64_t d_v, sdpa_dtype dtype, MhPlan &p)
+                    int64_t d_v, int dtype, MhPlan &p)
 {
     if (B < 0 || Lq < 0 || Lk < 0 || d_model < 1 || h < 1 || d_k < 1 || d_v < 1)
         return SDPA_ERR_BAD_SHAPE;
@@ -269,9 +281,9 @@ sdpa::GemmSegment segment(const void *W, void *C, int64_t N, int64_t d, int64_t 
 
 extern "C" {
 
-const char *sdpa_status_str(sdpa_status s)
+const char *sdpa_status_str(sdpa_status status)
 {
-    switch (s) {
+    switch (enum_value(status)) {
     case SDPA_OK: return "success";
     case SDPA_ERR_NULL_POINTER: return "a required pointer (Q, K, V or out) is NULL";
     case SDPA_ERR_BAD_SHAPE: return "invalid shape: a size is negative or exceeds the limits";
@@ -293,18 +305,20 @@ sdpa_status sdpa_forward(const void *Q, const void *K, const void *V,
                          int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                          int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream)
 {
+    const int dt = enum_value(dtype);
     Sizes z;
-    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dt, z);
     if (st != SDPA_OK || z.empty) return st;
-    return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dtype,
+    return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dt,
                            (hipStream_t)stream);
 }
 
 int64_t sdpa_multihead_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk, int64_t d_model,
                                        int64_t h, int64_t d_k, int64_t d_v, sdpa_dtype dtype)
 {
+    const int dt = enum_value(dtype);
     MhPlan p;
-    if (mh_plan(B, Lq, Lk, d_model, h, d_k, d_v, dtype, p) != SDPA_OK) return -1;
+    if (mh_plan(B, Lq, Lk, d_model, h, d_k, d_v, dt, p) != SDPA_OK) return -1;
     return p.total;
 }
 
@@ -315,8 +329,9 @@ sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *
                                    sdpa_dtype dtype, void *workspace, int64_t workspace_bytes,
                                    void *stream)
 {
+    const int dt = enum_value(dtype);
     MhPlan p;
-    const sdpa_status st = mh_plan(B, Lq, Lk, d_model, h, d_k, d_v, dtype, p);
+    const sdpa_status st = mh_plan(B, Lq, Lk, d_model, h, d_k, d_v, dt, p);
     if (st != SDPA_OK) return st;
     if (B == 0 || Lq == 0) return SDPA_OK;   // empty output
     if (!Xq || !Wq || !Wk || !Wv || !Wo || !out || (Lk > 0 && !Xkv)) return SDPA_ERR_NULL_POINTER;
@@ -391,21 +406,23 @@ sdpa_status sdpa_forward_restricted(const void *Q, const void *K, const void *V,
                                     void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                                     int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream)
 {
+    const int dt = enum_value(dtype);
     if (radius < 0) return SDPA_ERR_BAD_SHAPE;
     Sizes z;
-    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dt, z);
     if (st != SDPA_OK || z.empty) return st;
-    return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dtype,
+    return forward_kernels(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, d_k, d_v, dt,
                            (hipStream_t)stream, radius);
 }
 
 int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                                     int64_t d_k, int64_t d_v, sdpa_dtype dtype)
 {
-    const sdpa_status st = check_sizes(B, H, Lq, Lk, d_k, d_v, dtype);
+    const int dt = enum_value(dtype);
+    const sdpa_status st = check_sizes(B, H, Lq, Lk, d_k, d_v, dt);
     if (st != SDPA_OK) return -1;
     if (B == 0 || H == 0 || Lq == 0) return 0;
-    if (!split_applies(Lq, d_k, d_v, dtype)) return 0;
+    if (!split_applies(Lq, d_k, d_v, dt)) return 0;
     const SplitPlan sp = split_plan(B * H, Lk);
     return split_workspace_bytes(B * H, Lq, d_v, sp);
 }
@@ -416,12 +433,13 @@ sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
                         int64_t d_k, int64_t d_v, sdpa_dtype dtype,
                         void *workspace, int64_t workspace_bytes, void *stream)
 {
+    const int dt = enum_value(dtype);
     Sizes z;
-    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dt, z);
     if (st != SDPA_OK || z.empty) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (!split_applies(Lq, d_k, d_v, dtype))
-        return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dtype, s);
+    if (!split_applies(Lq, d_k, d_v, dt))
+        return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dt, s);
 
     const SplitPlan sp = split_plan(B * H, Lk);
     const int64_t need = split_workspace_bytes(B * H, Lq, d_v, sp);
@@ -442,12 +460,13 @@ sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
                                 int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                                 int64_t d_k, int64_t d_v, sdpa_dtype dtype, void *stream)
 {
+    const int dt = enum_value(dtype);
     Sizes z;
-    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dtype, z);
+    const sdpa_status st = validate(Q, K, V, key_lengths, out, B, H, Lq, Lk, d_k, d_v, dt, z);
     if (st != SDPA_OK || z.empty) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (!split_applies(Lq, d_k, d_v, dtype))
-        return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dtype, s);
+    if (!split_applies(Lq, d_k, d_v, dt))
+        return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dt, s);
     const SplitPlan sp = split_plan(B * H, Lk);
     const int64_t need = split_workspace_bytes(B * H, Lq, d_v, sp);
     if (need > kScratchBytes) return SDPA_ERR_SCRATCH_LIMIT;

@@ -25,7 +25,8 @@ def test_config_full(name):
     x = workloads.generate(name)
     c = x.config
     announce("config %s" % name)
-    got = run(x.q, x.k, x.v, x.key_lengths, c.causal, c.dtype)
+    # NaN-filled output: an element the kernels leave unwritten fails
+    got = run(x.q, x.k, x.v, x.key_lengths, c.causal, c.dtype, fill=float("nan"))
     ref = oracle.attention(x.q, x.k, x.v, key_lengths=x.key_lengths, causal=c.causal)
     assert_parity(got, ref, x.v, c.dtype, name)
 

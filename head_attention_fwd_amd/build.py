@@ -10,8 +10,8 @@ LIBRARY = os.path.join(HERE, "libsdpa.so")
 # calibration kernels for the measurements (bench.py --overlap-probe), not the attention path
 CALIB_LIBRARY = os.path.join(HERE, "libsdpa_calib.so")
 CALIB_SOURCES = ["sdpa_calib.hip"]
-SOURCES = ["sdpa_api.hip", "sdpa_fwd_generic.hip", "sdpa_fwd_mfma.hip", "sdpa_fwd_mfma_wide.hip",
-           "sdpa_proj_gemm.hip"]
+SOURCES = ["sdpa_api.hip", "sdpa_decode_row.hip", "sdpa_fwd_generic.hip", "sdpa_fwd_mfma.hip",
+           "sdpa_fwd_mfma_wide.hip", "sdpa_proj_gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -137,8 +137,9 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
                                            Lq, Lk, (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
 }
 
-// The matrix-core path of sdpa_decode: bf16, d_k = d_v in {64, 128}, one 32-row
-// wave per chunk of keys.
+// The dedicated paths of sdpa_decode: bf16, d_k = d_v in {64, 128}, at most 32
+// query rows; a single query row takes the vector-unit kernel, more rows the
+// matrix-core one (a 32-row wave per chunk of keys).
 bool split_applies(int64_t Lq, int64_t d_k, int64_t d_v, int dtype)
 {
     return dtype == SDPA_BF16 && d_k == d_v && (d_k == 64 || d_k == 128) && Lq >= 1 && Lq <= 32;
@@ -168,11 +169,55 @@ SplitPlan split_plan(int64_t n_bh, int64_t Lk)
     return SplitPlan{chunk, (Lk + chunk - 1) / chunk > 0 ? (Lk + chunk - 1) / chunk : 1};
 }
 
+// Plan of the single-row kernel (steps of 4096 / d keys).  With many heads (at
+// least 256) one chunk covers each head; otherwise chunks of four waves with at
+// least two steps per wave, enough of them for about 2048 waves (two per
+// SIMD), merged by a second kernel.  A head in one chunk takes two waves when
+// it has at most four steps of keys, else four.  chunk is a whole number of
+// steps per wave; n_split * chunk >= Lk.
+struct DecodePlan {
+    bool row;        // single-row kernel (else the matrix-core decode kernels)
+    int waves;       // single-row kernel: waves per workgroup
+    SplitPlan sp;
+};
+DecodePlan row_plan(int64_t n_bh, int64_t Lk, int64_t d)
+{
+    constexpr int64_t kWgHeads = 256, kTargetWaves = 2048, kNw = 4;
+    const int64_t step = 4096 / d, steps = (Lk + step - 1) / step;
+    const DecodePlan whole{true, steps <= 4 ? 2 : 4, SplitPlan{Lk, 1}};
+    if (n_bh >= kWgHeads) return whole;
+    int64_t spw = (n_bh * steps + kTargetWaves - 1) / kTargetWaves;
+    spw = spw < 2 ? 2 : spw;
+    const int64_t n_split = (steps + kNw * spw - 1) / (kNw * spw);
+    if (n_split <= 1) return whole;
+    int64_t cs = (steps + n_split - 1) / n_split;   // steps per chunk, a multiple of kNw
+    cs = (cs + kNw - 1) / kNw * kNw;
+    return DecodePlan{true, (int)kNw, SplitPlan{cs * step, (steps + cs - 1) / cs}};
+}
+
+// The plan of one sdpa_decode call on a dedicated path.
+DecodePlan decode_plan(int64_t n_bh, int64_t Lq, int64_t Lk, int64_t d)
+{
+    if (Lq == 1) return row_plan(n_bh, Lk, d);
+    return DecodePlan{false, 0, split_plan(n_bh, Lk)};
+}
+
 // Partial results (fp32 acc [d_v], m and l per split and query row); none
 // when one chunk covers each head.
 int64_t split_workspace_bytes(int64_t n_bh, int64_t Lq, int64_t d_v, const SplitPlan &sp)
 {
     return sp.n_split <= 1 ? 0 : 4 * (d_v + 2) * n_bh * sp.n_split * Lq;
+}
+
+sdpa_status launch_decode_plan(const DecodePlan &dp, const void *Q, const void *K, const void *V,
+                               const int32_t *key_lengths, void *out, int64_t B, int64_t H, int64_t Lq,
+                               int64_t Lk, int d, void *workspace, hipStream_t s)
+{
+    if (dp.row)
+        return hip_status(sdpa::launch_decode_row(Q, K, V, key_lengths, out, B, H, Lk, d, dp.waves,
+                                                  dp.sp.chunk, dp.sp.n_split, workspace, s));
+    return hip_status(sdpa::launch_decode(Q, K, V, key_lengths, out, B, H, Lq, Lk, d, dp.sp.chunk,
+                                          dp.sp.n_split, workspace, s));
 }
 
 // ---- device scratch of sdpa_decode_noalloc
@@ -423,8 +468,7 @@ int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk
     if (st != SDPA_OK) return -1;
     if (B == 0 || H == 0 || Lq == 0) return 0;
     if (!split_applies(Lq, d_k, d_v, dt)) return 0;
-    const SplitPlan sp = split_plan(B * H, Lk);
-    return split_workspace_bytes(B * H, Lq, d_v, sp);
+    return split_workspace_bytes(B * H, Lq, d_v, decode_plan(B * H, Lq, Lk, d_k).sp);
 }
 
 sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
@@ -441,7 +485,8 @@ sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
     if (!split_applies(Lq, d_k, d_v, dt))
         return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dt, s);
 
-    const SplitPlan sp = split_plan(B * H, Lk);
+    const DecodePlan dp = decode_plan(B * H, Lq, Lk, d_k);
+    const SplitPlan &sp = dp.sp;
     const int64_t need = split_workspace_bytes(B * H, Lq, d_v, sp);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
@@ -451,8 +496,8 @@ sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
             return SDPA_ERR_WORKSPACE;
     }
     if (B * H * sp.n_split > kMaxWorkgroups || B * H * Lq > kMaxWorkgroups) return SDPA_ERR_BAD_SHAPE;
-    return hip_status(sdpa::launch_decode(Q, K, V, key_lengths, out, B, H, Lq, Lk, (int)d_k, sp.chunk,
-                                          sp.n_split, need > 0 ? workspace : nullptr, s));
+    return launch_decode_plan(dp, Q, K, V, key_lengths, out, B, H, Lq, Lk, (int)d_k,
+                              need > 0 ? workspace : nullptr, s);
 }
 
 sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
@@ -467,7 +512,8 @@ sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
     hipStream_t s = (hipStream_t)stream;
     if (!split_applies(Lq, d_k, d_v, dt))
         return forward_kernels(Q, K, V, key_lengths, 0, out, B, H, Lq, Lk, d_k, d_v, dt, s);
-    const SplitPlan sp = split_plan(B * H, Lk);
+    const DecodePlan dp = decode_plan(B * H, Lq, Lk, d_k);
+    const SplitPlan &sp = dp.sp;
     const int64_t need = split_workspace_bytes(B * H, Lq, d_v, sp);
     if (need > kScratchBytes) return SDPA_ERR_SCRATCH_LIMIT;
     if (B * H * sp.n_split > kMaxWorkgroups || B * H * Lq > kMaxWorkgroups) return SDPA_ERR_BAD_SHAPE;
@@ -478,8 +524,7 @@ sdpa_status sdpa_decode_noalloc(const void *Q, const void *K, const void *V,
         if (err == hipSuccess) err = device_scratch(dev, &ws);
         if (err != hipSuccess) return hip_status(err);
     }
-    return hip_status(sdpa::launch_decode(Q, K, V, key_lengths, out, B, H, Lq, Lk, (int)d_k, sp.chunk,
-                                          sp.n_split, ws, s));
+    return launch_decode_plan(dp, Q, K, V, key_lengths, out, B, H, Lq, Lk, (int)d_k, ws, s);
 }
 
 }  // extern "C"

@@ -1276,9 +1276,16 @@ hipError_t launch_decode_d(const void *Q, const void *K, const void *V, const in
                        nullptr, (int)H, Lq, Lk, scale_log2, so);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    return launch_decode_merge(ws, out, n_bh, Lq, n_split, D, stream);
+}
+
+template <int D>
+hipError_t launch_merge_d(const float *ws, void *out, int64_t n_bh, int64_t Lq, int64_t n_split,
+                          hipStream_t stream)
+{
+    const int64_t n_rows = n_bh * n_split * Lq;
     hipLaunchKernelGGL((sdpa_split_merge_kernel<D>), dim3((uint32_t)(n_bh * Lq)), dim3(64), 0, stream,
-                       (const float *)so.acc, (const float *)so.m, (const float *)so.l, (uint16_t *)out,
-                       Lq, (uint32_t)n_split);
+                       ws, ws + n_rows * D, ws + n_rows * (D + 1), (uint16_t *)out, Lq, (uint32_t)n_split);
     return hipGetLastError();
 }
 
@@ -1360,6 +1367,14 @@ hipError_t launch_mfma(const void *Q, const void *K, const void *V, const int32_
     case 128: return launch_mfma_d<128>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_decode_merge(const float *ws, void *out, int64_t n_bh, int64_t Lq, int64_t n_split,
+                               int d, hipStream_t stream)
+{
+    if (d == 64) return launch_merge_d<64>(ws, out, n_bh, Lq, n_split, stream);
+    if (d == 128) return launch_merge_d<128>(ws, out, n_bh, Lq, n_split, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const void *Q, const void *K, const void *V, const int32_t *key_lengths,

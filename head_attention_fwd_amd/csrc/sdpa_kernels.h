@@ -51,6 +51,22 @@ hipError_t launch_decode(const void *Q, const void *K, const void *V, const int3
                          void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
                          int64_t chunk, int64_t n_split, void *workspace, hipStream_t stream);
 
+// Decode step with one query row per head (Lq = 1), bf16, d_k = d_v = d in
+// {64, 128}, on the vector units: workgroups of `waves` (2 or 4) waves, one
+// per (head, chunk of `chunk` keys), n_split chunks per head (n_split * chunk
+// >= Lk).  n_split == 1: each workgroup writes its head's row of out
+// (workspace unused); n_split > 1: partial results in `workspace` (4 * (d + 2)
+// * B * H * n_split bytes), then merged into out (two kernels on `stream`).
+hipError_t launch_decode_row(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
+                             void *out, int64_t B, int64_t H, int64_t Lk, int d, int waves, int64_t chunk,
+                             int64_t n_split, void *workspace, hipStream_t stream);
+
+// Merge of key-split partial results (floats in `ws`: acc [R][d], m [R], l [R]
+// with R = n_bh * n_split * Lq, row (head, split, query row) at (bh * n_split
+// + s) * Lq + i) into out [n_bh][Lq][d] (bf16); d in {64, 128}.
+hipError_t launch_decode_merge(const float *ws, void *out, int64_t n_bh, int64_t Lq, int64_t n_split,
+                               int d, hipStream_t stream);
+
 // Projection products of multi-head attention, C = A W on the matrix cores
 // (bf16, fp32 accumulation), tiles of 128 x 128 or 256 x 256 elements of C
 // (chosen by the launcher from the problem size), k in steps of 32.

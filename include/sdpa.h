@@ -171,14 +171,17 @@ int64_t sdpa_multihead_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk, int64_
  * positions generated so far, given by key_lengths[b], the cache length
  * including the new positions).
  *
- * For bf16 with d_k = d_v = 64 and 1 <= Lq <= 32 the keys of every (b, h) are
- * split into chunks that run in parallel on the matrix cores; each chunk writes
- * its partial result (per query row: reference maximum m, weight sum l and the
- * unnormalised weighted sum of V) to `workspace`, and a second kernel merges
- * the chunks: O = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c with
- * M = max_c m_c (base 2 in the kernel; a chunk without legal keys contributes
- * nothing; no legal key at all gives 0).  Any other (dtype, d_k, d_v, Lq) runs
- * the sdpa_forward kernels and needs no workspace.
+ * For bf16 with d_k = d_v in {64, 128} and 1 <= Lq <= 32 the keys of every
+ * (b, h) are split into chunks that run in parallel (one query row: dot
+ * products on the vector units; 2 to 32 rows: the matrix cores).  When a
+ * head's keys span several chunks, each chunk writes its partial result (per
+ * query row: reference maximum m, weight sum l and the unnormalised weighted
+ * sum of V) to `workspace`, and a second kernel merges the chunks:
+ * O = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c with M = max_c m_c
+ * (base 2 in the kernel; a chunk without legal keys contributes nothing; no
+ * legal key at all gives 0); with one chunk per head (many heads or a short
+ * cache) one kernel writes O and no workspace is used.  Any other (dtype, d_k,
+ * d_v, Lq) runs the sdpa_forward kernels and needs no workspace.
  *
  * Arguments as for sdpa_forward (no causal flag), plus
  *   workspace        device scratch of at least sdpa_decode_workspace_bytes()
@@ -187,7 +190,7 @@ int64_t sdpa_multihead_workspace_bytes(int64_t B, int64_t Lq, int64_t Lk, int64_
  *                    overlap Q, K, V, key_lengths or out;
  *   workspace_bytes  its size.
  * Two calls may share a workspace only if they run in stream order.
- * Returns SDPA_OK after the enqueue (two kernels on `stream`), or an error code;
+ * Returns SDPA_OK after the enqueue (one or two kernels on `stream`), or an error code;
  * SDPA_ERR_WORKSPACE if the workspace is needed and is NULL, too small or
  * overlapping.  Arithmetic and rounding as for sdpa_forward (the merge is fp32);
  * results are deterministic run to run.
@@ -200,9 +203,10 @@ sdpa_status sdpa_decode(const void *Q, const void *K, const void *V,
 
 /*
  * Bytes of workspace sdpa_decode needs for these sizes: 0 when it runs the
- * sdpa_forward kernels, otherwise 4 * (d_v + 2) * B * H * Lq * n_chunks, where
- * n_chunks depends on B * H and Lk only.  Returns -1 for sizes sdpa_decode
- * would reject with SDPA_ERR_BAD_SHAPE or SDPA_ERR_UNSUPPORTED.
+ * sdpa_forward kernels or one chunk covers each head, otherwise
+ * 4 * (d_v + 2) * B * H * Lq * n_chunks, where n_chunks depends on B * H, Lk,
+ * d_k and whether Lq is 1.  Returns -1 for sizes sdpa_decode would reject with
+ * SDPA_ERR_BAD_SHAPE or SDPA_ERR_UNSUPPORTED.
  */
 int64_t sdpa_decode_workspace_bytes(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                                     int64_t d_k, int64_t d_v, sdpa_dtype dtype);

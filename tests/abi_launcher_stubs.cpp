@@ -44,6 +44,15 @@ hipError_t launch_decode(const void *, const void *, const void *, const int32_t
 {
     return counted();
 }
+hipError_t launch_decode_row(const void *, const void *, const void *, const int32_t *, void *, int64_t,
+                             int64_t, int64_t, int, int, int64_t, int64_t, void *, hipStream_t)
+{
+    return counted();
+}
+hipError_t launch_decode_merge(const float *, void *, int64_t, int64_t, int64_t, int, hipStream_t)
+{
+    return counted();
+}
 hipError_t launch_proj_gemm(const void *, int, const GemmShape &, const GemmSegments &, int, hipStream_t)
 {
     return counted();

@@ -15,7 +15,7 @@ import head_attention_fwd_amd as sdpa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sdpa.h")
 
-FAKE_Q, FAKE_K, FAKE_V, FAKE_O = 0x10000, 0x20000, 0x30000, 0x40000
+FAKE_Q, FAKE_K, FAKE_V, FAKE_O = 0x1000000, 0x2000000, 0x3000000, 0x4000000
 
 
 def declared_functions():
@@ -114,10 +114,10 @@ def test_python_multihead_rejects_bad_arguments_without_gpu():
 
 # ---- sdpa_decode: the same host-side checks, plus the workspace
 
-# Default shape: keys split over three chunks (a workspace is needed), every
-# buffer inside its 64 KiB slot of fake addresses.
-def dcall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=1, H=1, Lq=1, Lk=300,
-          dk=64, dv=64, dtype=sdpa.SDPA_BF16, ws=0x1000000, ws_bytes=None):
+# Default shape: keys split over two chunks (a workspace is needed), every
+# buffer inside its 16 MiB slot of fake addresses.
+def dcall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=1, H=1, Lq=1, Lk=600,
+          dk=64, dv=64, dtype=sdpa.SDPA_BF16, ws=0x8000000, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = sdpa.sdpa_decode_workspace_bytes(B, H, Lq, Lk, dk, dv, dtype)
     return sdpa.sdpa_decode(Q, K, V, kl, O, B, H, Lq, Lk, dk, dv, dtype, ws, ws_bytes, 0)
@@ -126,25 +126,30 @@ def dcall(Q=FAKE_Q, K=FAKE_K, V=FAKE_V, kl=0, O=FAKE_O, B=1, H=1, Lq=1, Lk=300,
 def test_decode_workspace_bytes():
     ws = sdpa.sdpa_decode_workspace_bytes
     bf, f32 = sdpa.SDPA_BF16, sdpa.SDPA_F32
-    one = ws(4, 16, 1, 8192, 64, 64, bf)
-    assert one > 0 and one % (4 * 66 * 64) == 0        # 4 * (d_v + 2) * B * H * Lq * chunks
-    assert ws(4, 16, 5, 8192, 64, 64, bf) == 5 * one    # linear in Lq
-    assert ws(4, 16, 32, 8192, 64, 64, bf) == 32 * one
-    # the split path is bf16, d = 64, Lq <= 32 only; otherwise no workspace
+    # one query row: the vector-unit kernel, steps of 4096 / d keys, chunks of
+    # four waves with at least two steps per wave and about 2048 waves in all;
+    # 4 * (d_v + 2) bytes per head and chunk
+    assert ws(4, 16, 1, 8192, 64, 64, bf) == 4 * 66 * 64 * 8       # 128 steps, 8 chunks of 16
+    assert ws(4, 8, 1, 8192, 128, 128, bf) == 4 * 130 * 32 * 16    # 256 steps of 32 keys, 16 chunks
+    assert ws(1, 1, 1, 600, 64, 64, bf) == 4 * 66 * 2              # 10 steps: two chunks of 8
+    assert ws(2, 100, 1, 1025, 64, 64, bf) == 4 * 66 * 200 * 3     # 17 steps: three chunks of 8
+    assert ws(1, 1, 1, 512, 64, 64, bf) == 0                       # 8 steps: one chunk, no merge
+    assert ws(1, 1, 1, 100, 64, 64, bf) == 0
+    assert ws(64, 8, 1, 256, 64, 64, bf) == 0                      # at least 256 heads: one chunk
+    assert ws(64, 8, 1, 100000, 128, 128, bf) == 0
+    assert ws(4, 16, 1, 0, 64, 64, bf) == 0                        # no keys: one (empty) chunk
+    # 2 to 32 query rows: the matrix-core kernels, linear in Lq for a fixed plan
+    five = ws(4, 16, 5, 8192, 64, 64, bf)
+    assert five > 0 and five % (4 * 66 * 64 * 5) == 0              # 4 * (d_v + 2) * B * H * Lq * chunks
+    assert ws(4, 16, 32, 8192, 64, 64, bf) * 5 == five * 32
+    assert ws(4, 8, 2, 8192, 128, 128, bf) % (4 * 130 * 32 * 2) == 0
+    assert ws(64, 8, 32, 1024, 128, 128, bf) == 0                  # at least 256 heads: merged in LDS
+    # the dedicated paths are bf16, d in {64, 128}, Lq <= 32 only; otherwise no workspace
     assert ws(4, 16, 33, 8192, 64, 64, bf) == 0
     assert ws(4, 16, 1, 8192, 64, 64, f32) == 0
     assert ws(4, 16, 1, 8192, 32, 32, bf) == 0
-    assert ws(0, 16, 1, 8192, 64, 64, bf) == 0          # empty call
-    assert ws(4, 16, 1, 0, 64, 64, bf) == 0             # no keys: one (empty) chunk, no merge
-    assert ws(1, 1, 1, 100, 64, 64, bf) == 0            # one chunk per head: no merge
-    # d = 128 takes the same path: 4 * (d_v + 2) bytes per split and row
-    one128 = ws(4, 8, 1, 8192, 128, 128, bf)
-    assert one128 > 0 and one128 % (4 * 130 * 32) == 0
-    # at least 256 heads: one four-wave workgroup per head, merged in LDS
-    assert ws(64, 8, 1, 256, 64, 64, bf) == 0
-    assert ws(64, 8, 32, 1024, 128, 128, bf) == 0
-    assert ws(2, 100, 1, 1025, 64, 64, bf) > 0          # 200 heads: keys split over workgroups
-    assert ws(4, 16, 1, 8192, 256, 256, bf) == 0        # head size outside the path
+    assert ws(4, 16, 1, 8192, 256, 256, bf) == 0
+    assert ws(0, 16, 1, 8192, 64, 64, bf) == 0                     # empty call
     # sizes the entry point rejects
     assert ws(-1, 16, 1, 8192, 64, 64, bf) == -1
     assert ws(4, 16, 1, 8192, 513, 64, bf) == -1
@@ -158,7 +163,7 @@ def test_decode_workspace_bytes():
     (dict(dk=513), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(O=FAKE_Q), sdpa.SDPA_ERR_ALIAS),
     (dict(ws=0), sdpa.SDPA_ERR_WORKSPACE),
-    (dict(ws_bytes=100), sdpa.SDPA_ERR_WORKSPACE),        # the plan needs 792 bytes
+    (dict(ws_bytes=100), sdpa.SDPA_ERR_WORKSPACE),        # the plan needs 528 bytes
     (dict(ws=FAKE_V + 64), sdpa.SDPA_ERR_WORKSPACE),     # overlaps V
     (dict(ws=FAKE_O - 64), sdpa.SDPA_ERR_WORKSPACE),     # overlaps out
 ])

@@ -1,12 +1,13 @@
 """GPU parity of sdpa_decode (decode-step attention over a long key/value cache)
 against the fp64 oracle with causal = 0, through the C ABI.
 
-The matrix-core decode path (bf16, d_k = d_v in {64, 128}, Lq <= 32) is checked
-on cache lengths that cross the key tiles and the chunk boundaries, with key
-lengths that end inside a chunk, at a chunk boundary, at 0 and past Lk, both
-with keys split over workgroups (log-sum-exp merge) and with one workgroup per
-head (many heads, short caches: no merge); the other shapes must run the
-forward kernels and give exactly sdpa_forward's result.
+The dedicated decode paths (bf16, d_k = d_v in {64, 128}, Lq <= 32: the
+vector-unit kernel for one query row, the matrix-core kernels for more) are
+checked on cache lengths that cross the key tiles or steps and the chunk
+boundaries, with key lengths that end inside a chunk, at a chunk boundary, at
+0 and past Lk, both with keys split over workgroups (log-sum-exp merge) and
+with one workgroup per head (many heads, short caches: no merge); the other
+shapes must run the forward kernels and give exactly sdpa_forward's result.
 """
 import numpy as np
 import pytest
@@ -74,6 +75,50 @@ def test_split_path_parity(case, d):
     got = decode(q, k, v, lengths)
     ref = oracle.attention(q, k, v, key_lengths=lengths, causal=False)
     assert_parity(got, ref, v, "bf16", "decode %s" % (case[:4],))
+    if lengths is not None:
+        for b, ln in enumerate(lengths):
+            if ln <= 0:
+                assert np.all(got[b] == 0.0), "no legal key must give 0"
+
+
+# One query row (the vector-unit kernel: steps of 64 keys at d = 64, 32 at
+# d = 128): (B, H, Lk, lengths or None).  Few heads split their keys into
+# chunks of whole steps per wave (four-wave workgroups, merged by the second
+# kernel); 256 heads or more, or short caches, take one chunk each (two waves
+# up to four steps of keys, else four).
+ROW_CASES = [
+    (1, 1, 1, None),                             # one key
+    (1, 1, 31, None), (1, 1, 32, None), (1, 1, 33, None),   # around one step (d = 128)
+    (1, 1, 63, None), (1, 1, 64, None), (1, 1, 65, None),   # around one step (d = 64)
+    (1, 1, 129, None),                           # second wave: one key
+    (1, 1, 257, None),                           # third of four waves: one key
+    (1, 1, 1025, None),                          # two chunks (d = 64), the second with one key
+    (2, 3, 300, [300, 0]),                       # a sequence without keys
+    (3, 2, 1000, [1, 999, 5000]),                # one key, one short of Lk, past Lk
+    (1, 2, 4096, [512]),                         # the length on a chunk boundary
+    (1, 2, 4096, [513]),                         # one key into the next chunk
+    (1, 4, 32768 + 5, None),                     # many chunks per head
+    (64, 8, 256, "uniform"),                     # base model decode step: one chunk per head
+    (300, 1, 70, [0, 1, 64, 65, 70] * 60),       # 300 heads, one chunk each, waves without keys
+    (4, 64, 8192 + 3, [8192 + 3, 4000, 31, 8192]),
+]
+
+
+@pytest.mark.parametrize("case,d", [(c, d) for d in (64, 128) for c in ROW_CASES],
+                         ids=["d%d-%s" % (d, c[:3]) for d in (64, 128) for c in ROW_CASES])
+def test_single_row_parity(case, d):
+    B, H, Lk, lengths = case
+    seed = 4000 + B * 7 + H * 3 + Lk + d
+    q, k, v, _ = workloads.draw(B, H, 1, Lk, d, d, dtype="bf16", seed=seed)
+    if lengths == "uniform":
+        lengths = list(np.random.default_rng(seed).integers(1, Lk, size=B, endpoint=True))
+    need = sdpa.sdpa_decode_workspace_bytes(B, H, 1, Lk, d, d, sdpa.SDPA_BF16)
+    if B * H >= 256:
+        assert need == 0
+    announce("decode one row d=%d B=%d H=%d Lk=%d workspace %d" % (d, B, H, Lk, need))
+    got = decode(q, k, v, lengths)
+    ref = oracle.attention(q, k, v, key_lengths=lengths, causal=False)
+    assert_parity(got, ref, v, "bf16", "decode one row %s" % (case[:3],))
     if lengths is not None:
         for b, ln in enumerate(lengths):
             if ln <= 0:

@@ -95,23 +95,24 @@ def test_restricted_dominant_keys(d, causal):
     assert dev.type == "cuda"
 
 
-@pytest.mark.parametrize("Lq", [1, 5, 32])
-def test_decode_dominant_keys(Lq):
-    """Decode step (keys split over workgroups, log-sum-exp merge): dominant keys
-    inside chunks after the first and in chunks of their own."""
+@pytest.mark.parametrize("Lq,d", [(1, 64), (1, 128), (5, 64), (32, 64), (32, 128)])
+def test_decode_dominant_keys(Lq, d):
+    """Decode step (keys split over workgroups, log-sum-exp merge; one query
+    row on the vector-unit kernel): dominant keys inside chunks after the first
+    and in chunks of their own."""
     B, H, Lk = 2, 4, 5000
     spikes = SPIKES + ((3000, 160.0), (4999, 180.0))
-    q, k, v = _spiked(B, H, Lq, Lk, 64, seed=500 + Lq, spikes=spikes)
+    q, k, v = _spiked(B, H, Lq, Lk, d, seed=500 + Lq + d, spikes=spikes)
     lengths = [Lk, 3500]
     dev = require_gpu()
-    announce("dominant keys decode Lq=%d" % Lq)
+    announce("dominant keys decode Lq=%d d=%d" % (Lq, d))
     kl = torch.as_tensor(np.asarray(lengths, np.int32)).to(dev)
     out = sdpa.decode(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
                       to_dev(v, torch.bfloat16), key_lengths=kl)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
     ref = oracle.attention(q, k, v, key_lengths=lengths)
-    assert_parity(got, ref, v, "bf16", "decode Lq=%d" % Lq)
+    assert_parity(got, ref, v, "bf16", "decode Lq=%d d=%d" % (Lq, d))
 
 
 @pytest.mark.parametrize("d", [8, 64, 300])

@@ -14,6 +14,8 @@ headline lines.
   python bench.py --copy-mib 512      (calibration: a plain device copy)
   python bench.py --gemm-probe 8192   (calibration: a bf16 GEMM through torch)
   python bench.py --overlap-probe 20000   (calibration: matrix-core / VALU overlap)
+  python bench.py --config NAME --timeline   (per-workgroup phases of one cold launch,
+                                              from the timestamped build of the library)
 
 After the W warmup steps, untimed steps continue until the GPU has been busy for
 --settle-ms (default 150 ms), so that the K timed steps see the settled clock.
@@ -51,16 +53,19 @@ METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak (h=8/16, d_k=64) on 1 MI
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense peaks (matrix bf16; fp32 vector)
 PEAK_HBM_GBS = 8000.0
 DEFAULT_CONFIG = "long_causal_bf16"
-KERNEL_SOURCES = ["head_attention_fwd_amd/csrc/sdpa_fwd_mfma.hip",
-                  "head_attention_fwd_amd/csrc/sdpa_api.hip"]
+KERNEL_SOURCE_DIR = os.path.join(ROOT, "head_attention_fwd_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
+    """Hash of every source of the library (names and contents): a committed
+    counter figure applies only while it matches."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(KERNEL_SOURCE_DIR)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_SOURCE_DIR, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -272,6 +277,60 @@ class ClockSampler:
                           "timed window"}
 
 
+TIMELINE_FILES = ("fwd", "wide", "row")   # instrumented sources (readers sdpa_timeline_<name>)
+TIMELINE_WORKGROUPS, TIMELINE_EVENTS = 1 << 16, 4
+
+
+def timeline_capture(torch, lib, step, rotate, reps=3):
+    """Per-workgroup phases of single cold launches from libsdpa_timeline.so:
+    every workgroup's lane 0 of wave 0 stamps the device's 100 MHz real-time
+    counter at entry, when its first key tile is in, after its last tile and
+    after issuing its stores (csrc/sdpa_timeline.h).  Before each captured
+    launch every input set is run once, so the captured one (set 0) is the
+    least recently used.  Returns one record per repetition and instrumented
+    kernel file that ran."""
+    import ctypes
+    readers = {}
+    for name in TIMELINE_FILES:
+        fn = getattr(lib, "sdpa_timeline_" + name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+        readers[name] = fn
+    out = []
+    buf = np.zeros(TIMELINE_WORKGROUPS * TIMELINE_EVENTS, dtype=np.uint64)
+    for rep in range(reps):
+        for n in range(rotate):
+            step(n)
+        torch.cuda.synchronize()
+        for fn in readers.values():
+            assert fn(None, 0, 1) == 0, "clearing the timeline records failed"
+        step(0)
+        torch.cuda.synchronize()
+        for name, fn in readers.items():
+            assert fn(buf.ctypes.data, buf.nbytes, 0) == 0, "reading the timeline records failed"
+            t = buf.reshape(TIMELINE_WORKGROUPS, TIMELINE_EVENTS).astype(np.int64)
+            t = t[t[:, 0] > 0]
+            if len(t) == 0:
+                continue
+            t0 = t[:, 0].min()
+            us = lambda a: a / 100.0                       # 100 MHz counter
+            def pct(a, q):
+                return float(np.percentile(a, q)) if len(a) else None
+            ok1, ok2, ok3 = t[:, 1] > 0, (t[:, 1] > 0) & (t[:, 2] > 0), (t[:, 2] > 0) & (t[:, 3] > 0)
+            start = us(t[:, 0] - t0)
+            first = us(t[ok1, 1] - t[ok1, 0])
+            loop = us(t[ok2, 2] - t[ok2, 1])
+            epi = us(t[ok3, 3] - t[ok3, 2])
+            end = us(t[t[:, 3] > 0, 3] - t0)
+            out.append({"rep": rep, "file": name, "workgroups": int(len(t)),
+                        "start_us": {"p50": pct(start, 50), "max": float(start.max())},
+                        "first_tile_wait_us": {"p50": pct(first, 50), "p90": pct(first, 90)},
+                        "tile_loop_us": {"p50": pct(loop, 50), "p90": pct(loop, 90)},
+                        "epilogue_us": {"p50": pct(epi, 50), "p90": pct(epi, 90)},
+                        "end_us": {"p50": pct(end, 50), "max": float(end.max()) if len(end) else None}})
+    return out
+
+
 def copy_calibration(torch, dev, args):
     """A plain copy of known size: reads and writes args.copy_mib MiB per launch."""
     n = args.copy_mib << 20
@@ -398,6 +457,9 @@ def main():
                     help="time the K steps as one replay of a captured HIP graph (no host "
                          "launch cost between steps); auto: on for the decode workloads, whose "
                          "steps are two short launches")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup phases of single cold launches (timestamped build "
+                         "libsdpa_timeline.so) instead of the timed steps")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through (0: enough for >= 1 GiB on HBM-bound "
                          "workloads, 1 otherwise)")
@@ -410,6 +472,10 @@ def main():
 
     import torch
     import head_attention_fwd_amd as sdpa
+    if args.timeline:
+        # the timestamped build of the same sources, loaded in place of libsdpa.so
+        from head_attention_fwd_amd import _binding
+        _binding.load_library(os.path.join(ROOT, "head_attention_fwd_amd", "libsdpa_timeline.so"))
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     dev = torch.device("cuda:0")
@@ -531,6 +597,23 @@ def main():
             settle_steps += 1
         torch.cuda.synchronize()
 
+    if args.timeline:
+        recs = timeline_capture(torch, lib, step, rotate)
+        cols = ("workgroups", "start (p50 / max)", "first tile in (p50 / p90)",
+                "tile loop (p50 / p90)", "epilogue (p50 / p90)", "end (p50 / max)")
+        print("| launch | kernel file | " + " | ".join(cols) + " |")
+        print("|---|---|" + "---|" * len(cols))
+        f2 = lambda d, a, b: "%.2f / %.2f" % (d[a], d[b]) if d[a] is not None else "-"
+        for r in recs:
+            print("| %d | %s | %d | %s | %s | %s | %s | %s |" % (
+                r["rep"], r["file"], r["workgroups"], f2(r["start_us"], "p50", "max"),
+                f2(r["first_tile_wait_us"], "p50", "p90"), f2(r["tile_loop_us"], "p50", "p90"),
+                f2(r["epilogue_us"], "p50", "p90"), f2(r["end_us"], "p50", "max")))
+        print(json.dumps({"timeline": recs, "config": c.name, "entry": fn_name,
+                          "input_sets": rotate, "unit": "us",
+                          "clock": "s_memrealtime, 100 MHz, one device-wide counter"}), flush=True)
+        return
+
     use_graph = args.graph == "on" or (args.graph == "auto" and c.entry in ("decode", "multihead"))
     clk = None
     start = torch.cuda.Event(enable_timing=True)
@@ -625,7 +708,9 @@ def main():
                 "peak": PEAK_TFLOPS[arith], "unit": "TFLOP/s",
                 "frac": achieved_tflops / PEAK_TFLOPS[arith], "traffic": traffic}
     if c.entry == "decode":
-        roof["kernel"] = "sdpa_split_mfma_d64_kernel + sdpa_split_merge_d64_kernel"
+        roof["kernel"] = ("sdpa_decode_row_kernel (+ sdpa_split_merge_kernel when a head's keys span "
+                          "several chunks)" if c.Lq == 1 else
+                          "sdpa_decode_wg_kernel, or sdpa_split_mfma_kernel + sdpa_split_merge_kernel")
     elif c.entry == "multihead":
         roof["kernel"] = ("whole step: projection GEMMs (proj_gemm_kernel) + attention "
                           "(sdpa_fwd_mfma_kernel); per-kernel split in the rocprofv3 summary")

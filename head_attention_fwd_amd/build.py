@@ -2,6 +2,7 @@
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -10,6 +11,9 @@ LIBRARY = os.path.join(HERE, "libsdpa.so")
 # calibration kernels for the measurements (bench.py --overlap-probe), not the attention path
 CALIB_LIBRARY = os.path.join(HERE, "libsdpa_calib.so")
 CALIB_SOURCES = ["sdpa_calib.hip"]
+# the same sources with per-workgroup timestamps (SDPA_TIMELINE, csrc/sdpa_timeline.h),
+# loaded only by bench.py --timeline
+TIMELINE_LIBRARY = os.path.join(HERE, "libsdpa_timeline.so")
 SOURCES = ["sdpa_api.hip", "sdpa_decode_row.hip", "sdpa_fwd_generic.hip", "sdpa_fwd_mfma.hip",
            "sdpa_fwd_mfma_wide.hip", "sdpa_proj_gemm.hip"]
 ARCH = "gfx950"
@@ -26,10 +30,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def _hipcc(sources, target, verbose):
+def _hipcc(sources, target, verbose, extra=()):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = target + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
+    cmd = [hipcc] + HIPCC_FLAGS + list(extra) + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,9 +51,13 @@ def _hipcc(sources, target, verbose):
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source of the attention path into head_attention_fwd_amd/libsdpa.so,
-    and the calibration kernels into libsdpa_calib.so."""
-    _hipcc(CALIB_SOURCES, CALIB_LIBRARY, verbose)
-    return _hipcc(SOURCES, LIBRARY, verbose)
+    the same sources with timestamps into libsdpa_timeline.so, and the calibration
+    kernels into libsdpa_calib.so (three hipcc processes at once)."""
+    jobs = [(SOURCES, LIBRARY, ()), (SOURCES, TIMELINE_LIBRARY, ("-DSDPA_TIMELINE",)),
+            (CALIB_SOURCES, CALIB_LIBRARY, ())]
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        done = [ex.submit(_hipcc, src, tgt, verbose, extra) for src, tgt, extra in jobs]
+        return [f.result() for f in done][0]
 
 
 if __name__ == "__main__":

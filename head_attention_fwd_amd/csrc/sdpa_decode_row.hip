@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include "sdpa_kernels.h"
+#include "sdpa_timeline.h"
 
 namespace sdpa {
 namespace {
@@ -123,6 +124,7 @@ __global__ __launch_bounds__(64 * NW) void sdpa_decode_row_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane % kC, j = lane / kC;
+    SDPA_STAMP(0);
     const uint32_t u = blockIdx.x;   // head * n_split + chunk
     const uint32_t bh = u / n_split;
     const int64_t b = bh / H;
@@ -228,11 +230,13 @@ __global__ __launch_bounds__(64 * NW) void sdpa_decode_row_kernel(
     load(1, kb, vb);
     for (int s = 0; s < ns; s += 2) {
         step(s, ka, va);
+        if (s == 0) SDPA_STAMP(1);
         load(s + 2, ka, va);
         if (s + 1 < ns) step(s + 1, kb, vb);
         load(s + 3, kb, vb);
     }
 
+    SDPA_STAMP(2);
     // the wave's partial result: sums over the key groups
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = across_groups<kC, false>(acc[e]);
@@ -275,6 +279,7 @@ __global__ __launch_bounds__(64 * NW) void sdpa_decode_row_kernel(
             }
         }
     }
+    SDPA_STAMP(3);
 }
 
 template <int D, int NW>
@@ -310,3 +315,11 @@ hipError_t launch_decode_row(const void *Q, const void *K, const void *V, const 
 }
 
 }  // namespace sdpa
+
+#ifdef SDPA_TIMELINE
+// Timeline build only: the records of this file's kernel (sdpa_timeline.h).
+extern "C" int sdpa_timeline_row(void *host, int64_t bytes, int clear)
+{
+    return sdpa::timeline_io(host, bytes, clear);
+}
+#endif

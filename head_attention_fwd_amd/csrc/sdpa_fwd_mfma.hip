@@ -67,6 +67,7 @@
 #include <stdint.h>
 
 #include "sdpa_kernels.h"
+#include "sdpa_timeline.h"
 
 namespace sdpa {
 namespace {
@@ -448,10 +449,13 @@ struct Attn {
     __device__ __forceinline__ void finish_max_free(const f32x16_t &s, bf16x8_t *p, float bsum)
     {
         constexpr float kSumMax = 1048576.0f;   // 2^20
-        const uint64_t lanes = __builtin_amdgcn_ballot_w64(!(bsum <= kSumMax));
-        if (__builtin_expect(lanes != 0, 0)) {
+        const bool over = !(bsum <= kSumMax);
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) {
             asm volatile("" ::: "memory");   // keep the rare path a real branch
-            const bool grow = ((lanes >> l32) | (lanes >> (l32 + 32))) & 1;
+            // the row's decision: this lane's half or the other (lane l32 ^ 32)
+            const uint32_t o = over ? 1u : 0u;
+            const auto both = __builtin_amdgcn_permlane32_swap(o, o, false, false);
+            const bool grow = ((uint32_t)both[0] | (uint32_t)both[1]) != 0;
             const float mxs = block_max(s);
             if (grow) {
                 scale_pending(__builtin_amdgcn_exp2f(m_run - mxs), nullptr);
@@ -560,6 +564,7 @@ struct Attn {
         wait_vmem_keep<0>();
         __syncthreads();
         if (t == 0) {
+            SDPA_STAMP(1);
             read_q();
             __builtin_amdgcn_s_waitcnt(kWaitLds0);
         }
@@ -713,6 +718,7 @@ __device__ __forceinline__ void attend_query_tile(
     constexpr int BM = A::BM;
     constexpr int BN = A::BN;
     constexpr int kD = D, kRowBytes = A::kRowBytes, kKB = A::kKB, kDB = A::kDB;
+    SDPA_STAMP(0);
     const int g = lane >> 5;      // lane half
     const int l32 = lane & 31;
     const int64_t b = bh / H;
@@ -839,6 +845,7 @@ __device__ __forceinline__ void attend_query_tile(
     }
 
     st.run();
+    SDPA_STAMP(2);
 
     // ---- epilogue: O = acc / l, rounded to bf16
     acc_read_fence();
@@ -869,6 +876,7 @@ __device__ __forceinline__ void attend_query_tile(
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l_tot), rl,
                                                   (uint32_t)(l32 * 4), 0, 0);
         }
+        SDPA_STAMP(3);
         return;
     }
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;   // no legal key: output 0
@@ -904,6 +912,7 @@ __device__ __forceinline__ void attend_query_tile(
         const u32x4_t w = *(const u32x4_t *)((const char *)stage + r * kRowBytes + ((c ^ oswz(r)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(r * kRowBytes + c * 16), 0, 0);
     }
+    SDPA_STAMP(3);
 }
 
 // Work decomposition: one query tile (qt, head bh) per workgroup.  The
@@ -1061,6 +1070,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void sdpa_decode_wg_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5, l32 = lane & 31;
+    SDPA_STAMP(0);
     const uint32_t bh = blockIdx.x;
     const int64_t b = bh / H;
     int64_t len = Lk;
@@ -1128,6 +1138,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void sdpa_decode_wg_kernel(
         // this wave's copies of tile t have landed (those of tile t+1 may not)
         if (t + 1 < nt) wait_vmem_keep<kCopies>();
         else wait_vmem_keep<0>();
+        if (t == 0) SDPA_STAMP(1);
         const int64_t rem = n - (int64_t)t * BN;
         st.tile_blocks_masked(kb[t & 1], vb[t & 1], (int)(rem < BN ? rem : BN));
         // the tile's operands are in registers (the products consumed them):
@@ -1135,6 +1146,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void sdpa_decode_wg_kernel(
         if (t + 2 < nt) st.ld.issue(st.Kh, st.Vh, (int64_t)(t + 2) * BN, n, kb[t & 1], vb[t & 1]);
     }
 
+    SDPA_STAMP(2);
     // this wave's partial result into its own LDS space: acc [32 rows][D], m [32], l [32]
     acc_read_fence();
     const float l_tot = sum_across_halves(st.l_run);
@@ -1168,6 +1180,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void sdpa_decode_wg_kernel(
         const float o = den > 0.f ? num / den : 0.f;
         O[((int64_t)bh * Lq + i) * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
     }
+    SDPA_STAMP(3);
 }
 
 // Merge of the split partial results: block = one wave for row i of head bh
@@ -1389,3 +1402,11 @@ hipError_t launch_decode(const void *Q, const void *K, const void *V, const int3
 }
 
 }  // namespace sdpa
+
+#ifdef SDPA_TIMELINE
+// Timeline build only: the records of this file's kernels (sdpa_timeline.h).
+extern "C" int sdpa_timeline_fwd(void *host, int64_t bytes, int clear)
+{
+    return sdpa::timeline_io(host, bytes, clear);
+}
+#endif

@@ -69,6 +69,7 @@
 #include <stdint.h>
 
 #include "sdpa_kernels.h"
+#include "sdpa_timeline.h"
 
 namespace sdpa {
 namespace {
@@ -166,6 +167,7 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;      // query of the wave (accumulator column)
     const int grp = lane >> 4;      // lane group
+    SDPA_STAMP(0);
 
     // Work order: causal grids take the longest query tiles first; otherwise
     // each XCD (blockIdx % 8) takes a run of consecutive items, so the query
@@ -273,6 +275,7 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     for (int t = 0; t < n_tiles; ++t) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
+        if (t == 0) SDPA_STAMP(1);
         if (t + 1 < n_tiles) issue(t + 1);
         const char *kb = (const char *)(lds + (t & 1) * 2 * kTileElems);
         const char *vb = kb + 2 * kTileElems;
@@ -347,6 +350,7 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
         }
     }
 
+    SDPA_STAMP(2);
     // Row sum over the 4 lane groups; a row with no legal key gets 0.
     float l = l_run + __shfl_xor(l_run, 16);
     l += __shfl_xor(l, 32);
@@ -376,6 +380,7 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
         const u32x4_t v = *(const u32x4_t *)(stage + r * kRowBytes + ((c ^ (r & 15)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)(r * kRowBytes + c * 16), 0, 0);
     }
+    SDPA_STAMP(3);
 }
 
 template <int D>
@@ -404,3 +409,11 @@ hipError_t launch_mfma_wide(const void *Q, const void *K, const void *V, const i
 }
 
 }  // namespace sdpa
+
+#ifdef SDPA_TIMELINE
+// Timeline build only: the records of this file's kernel (sdpa_timeline.h).
+extern "C" int sdpa_timeline_wide(void *host, int64_t bytes, int clear)
+{
+    return sdpa::timeline_io(host, bytes, clear);
+}
+#endif

@@ -34,6 +34,21 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+TIMELINE_READERS = ("sdpa_timeline_fwd", "sdpa_timeline_wide", "sdpa_timeline_row")
+
+
+def test_timeline_build_exports_the_abi_and_its_readers():
+    """libsdpa_timeline.so (the same sources with per-workgroup stamps) has the
+    whole C ABI plus one record reader per instrumented source; the normal
+    library compiles the stamps out and has no reader."""
+    tl = ctypes.CDLL(os.path.join(os.path.dirname(sdpa.LIBRARY), "libsdpa_timeline.so"))
+    for name in declared_functions() + list(TIMELINE_READERS):
+        assert hasattr(tl, name), name
+    lib = ctypes.CDLL(sdpa.LIBRARY)
+    for name in TIMELINE_READERS:
+        assert not hasattr(lib, name), name
+
+
 def test_status_strings():
     for st in range(8):
         s = sdpa.sdpa_status_str(st)

@@ -12,7 +12,8 @@ headline lines.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                   [--no-cpu-baseline] [--rotate R] [--settle-ms MS]
   python bench.py --copy-mib 512      (calibration: a plain device copy)
-  python bench.py --gemm-probe 8192   (calibration: a bf16 GEMM through torch)
+  python bench.py --gemm-probe 8192   (calibration: a bf16 GEMM through torch;
+                                       also M,K,N, e.g. 32768,1024,3072)
   python bench.py --overlap-probe 20000   (calibration: matrix-core / VALU overlap)
   python bench.py --config NAME --timeline   (per-workgroup phases of one cold launch,
                                               from the timestamped build of the library)
@@ -352,13 +353,15 @@ def copy_calibration(torch, dev, args):
 
 
 def gemm_probe(torch, dev, args):
-    """Calibration, not the product: a large bf16 GEMM through torch (hipBLASLt),
-    N x N x N, to show what a dense matrix-core kernel reaches on this GPU (its
-    rate, and under rocprofv3 counters its clock and matrix-core busy share)."""
-    n = args.gemm_probe
-    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
-    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
-    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    """Calibration, not the product: a bf16 GEMM through torch (hipBLASLt), N x N x N
+    or M x K x N ("M,K,N"), to show what a dense matrix-core kernel reaches on
+    this GPU (its rate, and under rocprofv3 counters its clock and matrix-core
+    busy share), e.g. on the shapes of the multi-head projections."""
+    dims = [int(x) for x in str(args.gemm_probe).split(",")]
+    m, k, n = dims * 3 if len(dims) == 1 else dims
+    a = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(k, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(m, n, device=dev, dtype=torch.bfloat16)
     for _ in range(args.warmup):
         torch.matmul(a, b, out=c)
     torch.cuda.synchronize()
@@ -376,9 +379,10 @@ def gemm_probe(torch, dev, args):
         t1.record()
         torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    flop = 2.0 * m * k * n
     print(json.dumps({"probe": "bf16 GEMM C = A B through torch.matmul (hipBLASLt), calibration only",
-                      "N": n, "ms_per_gemm": ms, "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12,
-                      "frac_of_peak": 2.0 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+                      "M": m, "K": k, "N": n, "ms_per_gemm": ms, "tflops": flop / (ms * 1e-3) / 1e12,
+                      "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
                       "clock": clk.summary()}), flush=True)
 
 
@@ -447,9 +451,10 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, time a plain device copy of this many MiB "
                          "(calibrates the HBM byte counters of rocprofv3)")
-    ap.add_argument("--gemm-probe", type=int, default=0,
-                    help="instead of attention, time a bf16 N x N x N GEMM through torch "
-                         "(calibration: what a dense matrix-core kernel reaches on this GPU)")
+    ap.add_argument("--gemm-probe", default="",
+                    help="instead of attention, time a bf16 GEMM through torch, N (N x N x N) "
+                         "or M,K,N (calibration: what a dense matrix-core kernel reaches on "
+                         "this GPU)")
     ap.add_argument("--overlap-probe", type=int, default=0,
                     help="instead of attention, run the matrix-core / vector-ALU overlap probe "
                          "with this many iterations (calibration; libsdpa_calib.so)")

@@ -27,9 +27,11 @@ def _inputs(B, H, Lq, Lk, d, lengths, seed):
 
 
 # (B, H, Lq, Lk, d, lengths): the long decode step, then smaller ones with
-# padding (on the key-split path, d = 64 and 128), then a head size outside it
+# padding (on the key-split paths: one query row at d = 128, several at d = 64
+# and 128), then a head size outside them
 CALLS = [
     (4, 16, 1, 8192, 64, None),
+    (1, 2, 1, 2000, 128, [1999]),
     (2, 4, 5, 3000, 64, [3000, 1234]),
     (1, 2, 3, 700, 128, [650]),
     (1, 2, 3, 300, 256, [250]),

@@ -145,8 +145,9 @@ bool split_applies(int64_t Lq, int64_t d_k, int64_t d_v, int dtype)
     return dtype == SDPA_BF16 && d_k == d_v && (d_k == 64 || d_k == 128) && Lq >= 1 && Lq <= 32;
 }
 
-// Chunks per head.  With many heads (at least kWgHeads = 256: four waves per
-// head then give every CU a few waves), n_split = 0: each head's keys are split
+// Chunks per head of the matrix-core decode kernels (2 to 32 query rows).  With
+// many heads (at least kWgHeads = 256: four waves per head then give every CU a
+// few waves), n_split = 0: each head's keys are split
 // over the four waves of one workgroup and merged in LDS.  Otherwise enough
 // chunks for about 1536 one-wave workgroups (three per CU, two rounds), at
 // least two 64-key tiles per chunk, merged by a second kernel (n_split = 1:

@@ -30,7 +30,7 @@
 //    them against the two weights.  At the end the partial sums of the groups
 //    are added across lanes (DPP row rotation, v_permlane16_swap,
 //    v_permlane32_swap).
-//  * Two loads sets (two steps) are in flight: the next step's rows are
+//  * Two load sets (two steps) are in flight: the next step's rows are
 //    loaded while the current one is computed.  Loads past the wave's keys
 //    read 0 through the buffer descriptor's bound and cost no memory traffic.
 //

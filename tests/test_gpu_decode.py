@@ -95,6 +95,7 @@ ROW_CASES = [
     (1, 1, 1025, None),                          # two chunks (d = 64), the second with one key
     (2, 3, 300, [300, 0]),                       # a sequence without keys
     (3, 2, 1000, [1, 999, 5000]),                # one key, one short of Lk, past Lk
+    (2, 3, 700, [-5, 700]),                      # a negative length reads as no key
     (1, 2, 4096, [512]),                         # the length on a chunk boundary
     (1, 2, 4096, [513]),                         # one key into the next chunk
     (1, 4, 32768 + 5, None),                     # many chunks per head

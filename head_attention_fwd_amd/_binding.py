@@ -33,6 +33,17 @@ EXPORTED = ("sdpa_decode", "sdpa_decode_noalloc", "sdpa_decode_workspace_bytes",
             "sdpa_forward_restricted", "sdpa_last_hip_error", "sdpa_multihead_forward",
             "sdpa_multihead_workspace_bytes", "sdpa_status_str")
 
+# the package's public names (head_attention_fwd_amd re-exports exactly these)
+__all__ = [
+    "DECODE_NOALLOC_SCRATCH_BYTES", "EXPORTED", "LIBRARY", "SDPA_BF16", "SDPA_ERR_ALIAS",
+    "SDPA_ERR_BAD_SHAPE", "SDPA_ERR_HIP", "SDPA_ERR_NULL_POINTER", "SDPA_ERR_SCRATCH_LIMIT",
+    "SDPA_ERR_UNSUPPORTED", "SDPA_ERR_WORKSPACE", "SDPA_F32", "SDPA_OK", "SdpaError", "decode",
+    "decode_noalloc", "forward", "load_library", "multihead", "restricted", "sdpa_decode",
+    "sdpa_decode_noalloc", "sdpa_decode_workspace_bytes", "sdpa_forward", "sdpa_forward_restricted",
+    "sdpa_last_hip_error", "sdpa_multihead_forward", "sdpa_multihead_workspace_bytes",
+    "sdpa_status_str",
+]
+
 _lib = None
 
 

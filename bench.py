@@ -721,12 +721,12 @@ def main():
                           "(sdpa_fwd_mfma_kernel); per-kernel split in the rocprofv3 summary")
     elif c.entry == "restricted":
         roof["kernel"] = ("sdpa_fwd_mfma_band_kernel" if mfma_path else
-                          "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 128 else "sdpa_fwd_generic_kernel")
+                          "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 8 else "sdpa_fwd_generic_kernel")
     elif wide_mfma:
         roof["kernel"] = "sdpa_fwd_mfma_wide_kernel"
     else:
         roof["kernel"] = ("sdpa_fwd_mfma_kernel" if mfma_path else
-                          "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 128 else "sdpa_fwd_generic_kernel")
+                          "sdpa_fwd_wide_kernel" if max(c.d_k, c.d_v) > 8 else "sdpa_fwd_generic_kernel")
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
     roof["traffic_ratio"] = None if traffic is None else traffic / nbytes

@@ -8,10 +8,10 @@
 // It is the path for fp32 inputs and for head sizes the matrix-core kernel is
 // not built for.
 //
-// Head sizes up to 128 (sdpa_fwd_generic_kernel): one wave (64 lanes) per
-// workgroup, one query row per lane, 64 rows per workgroup; a 1-D grid of
-// ceil(Lq / 64) * B*H workgroups, the query tile index varying fastest.  Keys
-// and values are
+// Head sizes up to 8 (sdpa_fwd_generic_kernel; the pages' worked examples and
+// the tiny fp32 configuration): one wave (64 lanes) per workgroup, one query
+// row per lane, 64 rows per workgroup; a 1-D grid of ceil(Lq / 64) * B*H
+// workgroups, the query tile index varying fastest.  Keys and values are
 // staged through LDS in tiles of TK rows converted to fp32; every lane reads the
 // same LDS word at a time (a broadcast, free of bank conflicts).  The softmax
 // is evaluated online, tile by tile: the running maximum m and sum l per row
@@ -20,14 +20,15 @@
 // (แบบจับต้องได้)", section on dividing by sqrt(d_k): [100,100,100] splits
 // like [0,0,0]).
 //
-// Head sizes 129 .. 512 (sdpa_fwd_wide_kernel; Table 3 row (A) of page
+// Head sizes 9 .. 512 (sdpa_fwd_wide_kernel; Table 3 row (A) of page
 // "Attention Is All You Need/paper/es" ends at h = 1, d_k = d_v = 512): a
-// row's q and accumulator no longer fit one lane, so G = 8 (d <= 256) or 16
-// (d <= 512) lanes share a query row, lane l holding dims 32*l .. 32*l + 31;
-// 256 / G rows per 256-thread workgroup.  A score is the sum of the G lanes'
+// whole row's q and accumulator in one lane would spill to scratch from
+// d = 32 on, so G = 2 (d <= 64), 4 (d <= 128), 8 (d <= 256) or 16 (d <= 512)
+// lanes share a query row, lane l holding dims 32*l .. 32*l + 31; 256 / G
+// rows per 256-thread workgroup.  A score is the sum of the G lanes'
 // partial dot products (log2 G xor shuffles inside the group), after which all
 // G lanes hold the same score and run the same online softmax on their own
-// dims.  K and V tiles (16 or 8 keys) are staged as fp32 with each lane's
+// dims.  K and V tiles (32, 16 or 8 keys) are staged as fp32 with each lane's
 // chunk padded by 16 bytes, so that the G lanes' 16-byte reads of one key row
 // fall in distinct banks (the other rows of the wave read the same addresses:
 // broadcast), and the next tile's rows are loaded into registers while the
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kWThreads) void sdpa_fwd_wide_kernel(
 {
     constexpr int DL = kWDL;
     constexpr int kRowsWG = kWThreads / G;  // query rows per workgroup
-    constexpr int kTK = G >= 16 ? 8 : 16;   // keys per LDS tile
+    constexpr int kTK = G >= 16 ? 8 : (G >= 4 ? 16 : 32);   // keys per LDS tile
     constexpr int kDim = G * DL;            // dims covered (>= d_k, d_v)
     constexpr int kLane = DL + 4;           // floats per lane chunk in LDS (16 B padding)
     constexpr int kRowF = G * kLane;        // floats per staged key row
@@ -383,9 +384,8 @@ hipError_t launch_d(const void *Q, const void *K, const void *V, const int32_t *
 {
     const int d = d_k > d_v ? d_k : d_v;
     if (d <= 8) return launch_t<T, 8>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
-    if (d <= 32) return launch_t<T, 32>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
-    if (d <= 64) return launch_t<T, 64>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
-    if (d <= 128) return launch_t<T, 128>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
+    if (d <= 64) return launch_wide<T, 2>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
+    if (d <= 128) return launch_wide<T, 4>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
     if (d <= 256) return launch_wide<T, 8>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
     return launch_wide<T, 16>(Q, K, V, kl, causal, r, out, B, H, Lq, Lk, d_k, d_v, stream);
 }

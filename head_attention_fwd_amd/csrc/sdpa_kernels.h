@@ -12,7 +12,8 @@ namespace sdpa {
 
 // Any 1 <= d_k, d_v <= 512; elements are fp32 (is_bf16 = false) or bf16.
 // fp32 arithmetic throughout on the vector units: one lane per query row up to
-// d = 128, 8 (d <= 256) or 16 (d <= 512) lanes per query row above.  radius >= 0:
+// d = 8, then 2 (d <= 64), 4 (d <= 128), 8 (d <= 256) or 16 (d <= 512) lanes per
+// query row.  radius >= 0:
 // restricted self-attention (|i - j| <= radius); radius < 0: no restriction.
 hipError_t launch_generic(const void *Q, const void *K, const void *V,
                           const int32_t *key_lengths, int causal, int64_t radius, void *out,

@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name", ["tiny_causal_f32", "base_encoder_bf16",
                                   "base_decoder_causal_bf16", "big_cross_bf16",
                                   "rowA_h4_d128_encoder_bf16", "rowA_h16_d32_encoder_bf16",
-                                  "rowA_h32_d16_encoder_bf16", "rowA_h1_d512_encoder_bf16"])
+                                  "rowA_h32_d16_encoder_bf16", "rowA_h1_d512_encoder_bf16",
+                                  "base_encoder_f32", "encoder_d96_bf16"])
 def test_config_full(name):
     x = workloads.generate(name)
     c = x.config

@@ -94,6 +94,17 @@ CONFIGS = {
         "h = 1 head of d_k = d_v = 512 (Table 3 row A)", "bf16",
         B=64, H=1, Lq=256, Lk=256, d_k=512, d_v=512, causal=False, key_len_range=(64, 256),
         scale=1.0, seed=16),
+    # The vector-unit paths at the base encoder's shape: fp32 (all head sizes)
+    # and bf16 with a head size the matrix-core kernels do not take.
+    "base_encoder_f32": Config(
+        "base_encoder_f32", "base-model encoder self-attention with key padding, fp32", "f32",
+        B=64, H=8, Lq=256, Lk=256, d_k=64, d_v=64, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=19),
+    "encoder_d96_bf16": Config(
+        "encoder_d96_bf16", "encoder self-attention with key padding, h = 8 heads of "
+        "d_k = d_v = 96 (a head size without a matrix-core layout)", "bf16",
+        B=64, H=8, Lq=256, Lk=256, d_k=96, d_v=96, causal=False, key_len_range=(64, 256),
+        scale=1.0, seed=20),
     "long_causal_d128_bf16": Config(
         "long_causal_d128_bf16", "long-sequence causal self-attention, d_model = 1024 as "
         "h = 8 heads of d_k = d_v = 128, inputs scaled by 0.5", "bf16",
@@ -162,7 +173,7 @@ ORDER = ["tiny_causal_f32", "base_encoder_bf16", "base_decoder_causal_bf16",
          "long_causal_d128_bf16", "restricted_long_bf16",
          "restricted_long_causal_bf16", "mha_base_encoder_bf16", "mha_big_cross_bf16",
          "mha_long_causal_bf16", "decode_base_bf16", "decode_long_bf16", "decode_base_d128_bf16",
-         "decode_long_d128_bf16"]
+         "decode_long_d128_bf16", "base_encoder_f32", "encoder_d96_bf16"]
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:

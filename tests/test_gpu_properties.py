@@ -169,6 +169,16 @@ def test_zero_keys_and_empty_calls():
     assert torch.all(out == 0)
     e = torch.empty(0, 2, 5, 64, device=dev, dtype=torch.bfloat16)
     assert sdpa.forward(e, e, e).shape == (0, 2, 5, 64)
+    # decode steps against an empty cache: the single-row kernel (Lq = 1) and
+    # the matrix-core decode kernels (Lq = 3) also give 0
+    for lq, d in ((1, 64), (1, 128), (3, 64)):
+        q = torch.randn(2, 2, lq, d, device=dev).to(torch.bfloat16)
+        k = torch.empty(2, 2, 0, d, device=dev, dtype=torch.bfloat16)
+        out = torch.full((2, 2, lq, d), float("nan"), device=dev, dtype=torch.bfloat16)
+        announce("decode Lk = 0, Lq = %d, d = %d" % (lq, d))
+        sdpa.decode(q, k, k, out=out)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0)
 
 
 def test_error_paths_raise():

@@ -558,10 +558,18 @@ struct Attn {
     // in flight, tiles t and t+1 (and Q at t = 0); after it, tiles t and t+1
     // are in LDS for every wave and every wave is done with tile t-1, whose
     // buffer takes tile t+2.  At t = 0 the wave first reads its Q rows, which
-    // lie where its own copies of tile 2 land.
+    // lie where its own copies of tile 2 land.  With Q staged in LDS (and
+    // outside the band kernel, whose ring may start at tile 1) tile 0 waits
+    // for Q and tile 0 only: tile 1's copies, issued last, may still be in
+    // flight (vector memory loads complete in issue order), so a workgroup
+    // starts computing after two thirds of its first burst of loads.
+    static constexpr bool kFirstWaitOne = kQViaLds && !BAND;
     __device__ __forceinline__ void tile_begin(int t, uint16_t *knext, uint16_t *vnext)
     {
-        wait_vmem_keep<0>();
+        if (kFirstWaitOne && t == 0 && n_tiles > 1)
+            wait_vmem_keep<TileLoader<NW, BN, D>::kLoadsPerTile>();
+        else
+            wait_vmem_keep<0>();
         __syncthreads();
         if (t == 0) {
             SDPA_STAMP(1);
@@ -635,14 +643,29 @@ struct Attn {
         }
         for (int t = 0; t < n_tiles;) {
             if (t == 1 && n_full > 1) {
-                f32x16_t s_io = scores(kbuf[1], 0);   // tile 1 landed before tile 0's barrier
-                for (; t + 2 < n_full; t += 3) {
-                    tile_full<1>(t, s_io);
-                    tile_full<2>(t + 1, s_io);
-                    tile_full<0>(t + 2, s_io);
+                if constexpr (kFirstWaitOne) {
+                    // tile 1 is in LDS for every wave after its own barrier;
+                    // each later tile has landed at the barrier before its own
+                    tile_begin(1, kbuf[0], vbuf[0]);
+                    f32x16_t s_io = scores(kbuf[1], 0);
+                    tile_blocks_full(kbuf[1], vbuf[1], kbuf[2], s_io);
+                    for (t = 2; t + 2 < n_full; t += 3) {
+                        tile_full<2>(t, s_io);
+                        tile_full<0>(t + 1, s_io);
+                        tile_full<1>(t + 2, s_io);
+                    }
+                    if (t < n_full) tile_full<2>(t++, s_io);
+                    if (t < n_full) tile_full<0>(t++, s_io);
+                } else {
+                    f32x16_t s_io = scores(kbuf[1], 0);   // tile 1 landed before tile 0's barrier
+                    for (; t + 2 < n_full; t += 3) {
+                        tile_full<1>(t, s_io);
+                        tile_full<2>(t + 1, s_io);
+                        tile_full<0>(t + 2, s_io);
+                    }
+                    if (t < n_full) tile_full<1>(t++, s_io);
+                    if (t < n_full) tile_full<2>(t++, s_io);
                 }
-                if (t < n_full) tile_full<1>(t++, s_io);
-                if (t < n_full) tile_full<2>(t++, s_io);
             } else {
                 tile_any(t++);
             }

@@ -559,11 +559,13 @@ struct Attn {
     // are in LDS for every wave and every wave is done with tile t-1, whose
     // buffer takes tile t+2.  At t = 0 the wave first reads its Q rows, which
     // lie where its own copies of tile 2 land.  With Q staged in LDS (and
-    // outside the band kernel, whose ring may start at tile 1) tile 0 waits
-    // for Q and tile 0 only: tile 1's copies, issued last, may still be in
-    // flight (vector memory loads complete in issue order), so a workgroup
-    // starts computing after two thirds of its first burst of loads.
-    static constexpr bool kFirstWaitOne = kQViaLds && !BAND;
+    // outside the band kernel, whose ring may start at tile 1, and the
+    // one-wave key-split kernel, where the peeled tile raised the spilled
+    // SGPRs from 78 to 116 at d = 128) tile 0 waits for Q and tile 0 only: tile 1's
+    // copies, issued last, may still be in flight (vector memory loads
+    // complete in issue order), so a workgroup starts computing after two
+    // thirds of its first burst of loads.
+    static constexpr bool kFirstWaitOne = kQViaLds && !BAND && NW > 1;
     __device__ __forceinline__ void tile_begin(int t, uint16_t *knext, uint16_t *vnext)
     {
         if (kFirstWaitOne && t == 0 && n_tiles > 1)

@@ -165,3 +165,46 @@ def test_long_keys_sampled_rows(d):
     rows = _sample_rows(B, H, Lq, n_random=4, seed=3)
     ref, _ = oracle.attention_rows(q, k, v, rows, key_lengths=lengths)
     assert_parity(got[rows[:, 0], rows[:, 1], rows[:, 2]], ref, v, "bf16", "long keys")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_tile_ring_phases(d, causal):
+    """Every entry into the unrolled loop over fully legal key tiles: one batch
+    entry per count of fully legal tiles (1 .. 9 tiles of 64 keys, alternately
+    whole and with a ragged tail that the masked path takes after the loop),
+    and, causal, waves whose diagonal ends the loop at every tile of the ring.
+    Q rows past the last full query tile test the bounded row range."""
+    B, H, Lq, Lk = 9, 2, 600, 600
+    lengths = [64 * n + (7 if n % 2 else 0) for n in range(1, 10)]
+    q, k, v, _ = workloads.draw(B, H, Lq, Lk, d, d, dtype="bf16", seed=600 + d + causal)
+    announce("tile ring phases d=%d causal=%s lengths=%s" % (d, causal, lengths))
+    got = run(q, k, v, lengths, causal, "bf16", fill=float("nan"))
+    ref = oracle.attention(q, k, v, key_lengths=lengths, causal=causal)
+    assert_parity(got, ref, v, "bf16", "ring phases d=%d causal=%s" % (d, causal))
+
+
+PADDED_CASES = [
+    # (B, H, Lq, Lk, lengths): non-causal launches whose batch entries end at
+    # every kind of tile boundary, with empty entries, ties, negative and
+    # over-long lengths (clamped to [0, Lk])
+    (16, 4, 200, 300, [300, 0, 17, 64, 65, 300, 1, -3, 999, 128, 129, 250, 64, 200, 33, 300]),
+    (64, 1, 130, 256, None),   # 64 entries, lengths drawn below
+    (8, 3, 64, 96, [96, 96, 0, 0, 40, 40, 96, 1]),
+]
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("case", PADDED_CASES, ids=lambda c: "B%d_h%d" % (c[0], c[1]))
+def test_padded_lengths_full(case, d):
+    """Per-entry key lengths of every kind on each matrix-core head size; the
+    output is NaN-filled first (each query tile must be written) and compared
+    element by element."""
+    B, H, Lq, Lk, lengths = case
+    if lengths is None:
+        lengths = np.random.default_rng(64).integers(0, Lk, size=B, endpoint=True).tolist()
+    q, k, v, _ = workloads.draw(B, H, Lq, Lk, d, d, dtype="bf16", seed=700 + d + B)
+    announce("padded lengths B=%d h=%d d=%d lengths=%s" % (B, H, d, lengths))
+    got = run(q, k, v, lengths, False, "bf16", fill=float("nan"))
+    ref = oracle.attention(q, k, v, key_lengths=lengths, causal=False)
+    assert_parity(got, ref, v, "bf16", "padded lengths B=%d h=%d d=%d" % (B, H, d))

@@ -643,22 +643,17 @@ struct Attn {
             const int64_t diag = (q0w + 1) / BN;   // (t+1)*BN - 1 <= q0w
             if (diag < n_full) n_full = diag;
         }
-        for (int t = 0; t < n_tiles;) {
-            if (t == 1 && n_full > 1) {
-                if constexpr (kFirstWaitOne) {
-                    // tile 1 is in LDS for every wave after its own barrier;
-                    // each later tile has landed at the barrier before its own
-                    tile_begin(1, kbuf[0], vbuf[0]);
-                    f32x16_t s_io = scores(kbuf[1], 0);
-                    tile_blocks_full(kbuf[1], vbuf[1], kbuf[2], s_io);
-                    for (t = 2; t + 2 < n_full; t += 3) {
-                        tile_full<2>(t, s_io);
-                        tile_full<0>(t + 1, s_io);
-                        tile_full<1>(t + 2, s_io);
-                    }
-                    if (t < n_full) tile_full<2>(t++, s_io);
-                    if (t < n_full) tile_full<0>(t++, s_io);
-                } else {
+        // Three phases, each with its own copy of the code, so that the
+        // accumulators stay in place from one phase to the next (one loop over
+        // both kinds of tile made the register allocator copy them at every
+        // masked tile).
+        if constexpr (NW == 1) {
+            // the one-wave key-split kernel keeps a single loop: with the
+            // phases, its d = 128 form got an accumulation register as an
+            // operand of the rescale's inline multiplies (rejected by the
+            // assembler)
+            for (int t = 0; t < n_tiles;) {
+                if (t == 1 && n_full > 1) {
                     f32x16_t s_io = scores(kbuf[1], 0);   // tile 1 landed before tile 0's barrier
                     for (; t + 2 < n_full; t += 3) {
                         tile_full<1>(t, s_io);
@@ -667,11 +662,40 @@ struct Attn {
                     }
                     if (t < n_full) tile_full<1>(t++, s_io);
                     if (t < n_full) tile_full<2>(t++, s_io);
+                } else {
+                    tile_any(t++);
                 }
+            }
+            return;
+        }
+        tile_any(0);
+        int t = 1;
+        if (n_full > 1) {
+            if constexpr (kFirstWaitOne) {
+                // tile 1 is in LDS for every wave after its own barrier; each
+                // later tile has landed at the barrier before its own
+                tile_begin(1, kbuf[0], vbuf[0]);
+                f32x16_t s_io = scores(kbuf[1], 0);
+                tile_blocks_full(kbuf[1], vbuf[1], kbuf[2], s_io);
+                for (t = 2; t + 2 < n_full; t += 3) {
+                    tile_full<2>(t, s_io);
+                    tile_full<0>(t + 1, s_io);
+                    tile_full<1>(t + 2, s_io);
+                }
+                if (t < n_full) tile_full<2>(t++, s_io);
+                if (t < n_full) tile_full<0>(t++, s_io);
             } else {
-                tile_any(t++);
+                f32x16_t s_io = scores(kbuf[1], 0);   // tile 1 landed before tile 0's barrier
+                for (; t + 2 < n_full; t += 3) {
+                    tile_full<1>(t, s_io);
+                    tile_full<2>(t + 1, s_io);
+                    tile_full<0>(t + 2, s_io);
+                }
+                if (t < n_full) tile_full<1>(t++, s_io);
+                if (t < n_full) tile_full<2>(t++, s_io);
             }
         }
+        for (; t < n_tiles; ++t) tile_any(t);
     }
 
     // BAND: the fully legal tiles of this wave form the middle range

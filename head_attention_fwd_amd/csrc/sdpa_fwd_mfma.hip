@@ -89,13 +89,17 @@ constexpr int kSplitKeyBlocks = 1;     // 32-key blocks per LDS tile of the key-
 constexpr int kShortCausalKeys = 512;  // d = 64 causal launches up to this many keys take 32-key tiles
 constexpr int kCausalHeadGroup = 4;    // causal order: heads per group on an XCD
 constexpr int kWavesPerSimd64 = 3;     // register budget at d = 64 with 64-key tiles
+constexpr int kWavesPerSimd128 = 2;    // register budget of the forward kernel at d = 128 ...
+constexpr int kWavesPerSimd128Long = 3;   // ... and of its form for long key ranges
+constexpr int kLongKeys128 = 1024;     // d = 128 launches with more keys take the long form
 constexpr int kBandKeyBlocks64 = 1;    // restricted attention, d = 64: 32-key tiles (finer band edges)
 // Waves per SIMD the register budget is set for, by head size: D = 128 needs
-// 64 accumulator and 32 Q-operand registers (2 waves), D = 32 and D = 16 fit 4;
-// D = 64 with 32-key tiles (one score block in flight) fits 4 as well.
-template <int D, int NB = 2>
+// 64 accumulator and 32 Q-operand registers (2 waves; 3 for long key ranges,
+// 167 VGPRs), D = 32 and D = 16 fit 4; D = 64 with 32-key tiles (one score
+// block in flight) fits 4 as well.
+template <int D, int NB = 2, bool BAND = false>
 struct Occupancy {
-    static constexpr int kWaves = D >= 128 ? 2 : (D >= 64 ? (NB == 1 ? 4 : kWavesPerSimd64) : 4);
+    static constexpr int kWaves = D >= 128 ? (BAND ? 2 : kWavesPerSimd128) : (D >= 64 ? (NB == 1 ? 4 : kWavesPerSimd64) : 4);
 };
 
 // 16-byte chunk swizzles of a row of D bf16 values (D/8 chunks), XORed into
@@ -719,24 +723,27 @@ struct Attn {
             const int64_t diag = (qrel + 1) / BN;
             if (diag < f_hi) f_hi = diag;
         }
-        for (int t = 0; t < n_tiles;) {
-            if (t == f_lo && f_hi > f_lo) {
-                // tile f_lo landed before tile f_lo-1's barrier; enter the ring
-                // at its phase
-                f32x16_t s_io = scores(kbuf[0] + (t % 3) * kBufStride, 0);
-                if (t % 3 == 2) tile_full<2>(t++, s_io);
-                if (t % 3 == 0 && t < f_hi) tile_full<0>(t++, s_io);
-                for (; t + 2 < f_hi; t += 3) {
-                    tile_full<1>(t, s_io);
-                    tile_full<2>(t + 1, s_io);
-                    tile_full<0>(t + 2, s_io);
-                }
-                if (t < f_hi) tile_full<1>(t++, s_io);
-                if (t < f_hi) tile_full<2>(t++, s_io);
-            } else {
-                tile_any(t++);
+        // In phases, as in run(): the masked tiles before the ring, the ring,
+        // the masked tiles after it.
+        const bool ring = f_hi > f_lo;
+        const int64_t ring_lo = ring ? f_lo : n_tiles;
+        int t = 0;
+        for (; t < ring_lo && t < n_tiles; ++t) tile_any(t);
+        if (ring && t == f_lo) {
+            // tile f_lo landed before tile f_lo-1's barrier; enter the ring at
+            // its phase
+            f32x16_t s_io = scores(kbuf[0] + (t % 3) * kBufStride, 0);
+            if (t % 3 == 2) tile_full<2>(t++, s_io);
+            if (t % 3 == 0 && t < f_hi) tile_full<0>(t++, s_io);
+            for (; t + 2 < f_hi; t += 3) {
+                tile_full<1>(t, s_io);
+                tile_full<2>(t + 1, s_io);
+                tile_full<0>(t + 2, s_io);
             }
+            if (t < f_hi) tile_full<1>(t++, s_io);
+            if (t < f_hi) tile_full<2>(t++, s_io);
         }
+        for (; t < n_tiles; ++t) tile_any(t);
     }
 };
 
@@ -955,9 +962,12 @@ __device__ __forceinline__ void attend_query_tile(
             const int c = 4 * db + rq4;
             *(u32x2_t *)((char *)stage + l32 * kRowBytes + ((c ^ oswz(l32)) << 4) + 8 * g) = w;
         }
+    // the lane index recomputed (mbcnt) rather than kept live across the key
+    // loop: at d = 128 keeping it cost a spilled register
+    const int lane_o = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
     for (int i = 0; i < 32 / kRps; ++i) {
-        const int r = kRps * i + lane / kC, c = lane % kC;
+        const int r = kRps * i + lane_o / kC, c = lane_o % kC;
         const u32x4_t w = *(const u32x4_t *)((const char *)stage + r * kRowBytes + ((c ^ oswz(r)) << 4));
         __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(r * kRowBytes + c * 16), 0, 0);
     }
@@ -980,9 +990,9 @@ __device__ __forceinline__ void attend_query_tile(
 //    fetched 550 MiB per launch into L2, all 8 at once 1188 MiB, one at a time
 //    196 MiB but with the long tiles of the last head starting late).  Short
 //    heads fit the L2 together, and taking all of them at once balances best.
-template <int NW, int NB, int D>
+template <int NW, int NB, int D, int WAVES = Occupancy<D, NB>::kWaves>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::kWaves))) void sdpa_fwd_mfma_kernel(
+__attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void sdpa_fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
@@ -1034,7 +1044,7 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::k
 // is used.
 template <int NW, int NB, int D>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(Occupancy<D, NB>::kWaves, Occupancy<D, NB>::kWaves))) void sdpa_fwd_mfma_band_kernel(
+__attribute__((amdgpu_waves_per_eu(Occupancy<D, NB, true>::kWaves, Occupancy<D, NB, true>::kWaves))) void sdpa_fwd_mfma_band_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     int64_t radius, uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
@@ -1375,6 +1385,18 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
             hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, 1, D>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths, causal,
                                (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (D == 128) {
+        // Long key ranges: a register budget of three waves per SIMD (167
+        // VGPRs), long causal 496 -> 480 us; short launches keep two (19.1
+        // against 19.7 us on the h = 4 encoder).
+        if (Lk > kLongKeys128) {
+            hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D, kWavesPerSimd128Long>), dim3(n_qtiles * n_bh),
+                               dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
+                               (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
+                               scale_log2, n_qtiles, n_bh);
             return hipGetLastError();
         }
     }

@@ -101,6 +101,9 @@ RAGGED += [
     (2, 2, 70, 90, 32, 32, True, [50, 90]),
     (2, 2, 70, 90, 128, 128, False, [90, 3]),
     (2, 3, 160, 97, 128, 128, True, [97, 33]),   # several 32-key tiles, ragged tail
+    # d = 128 past 1024 keys: the form budgeted for three waves per SIMD
+    (2, 2, 300, 1500, 128, 128, True, [1500, 1100]),
+    (2, 2, 129, 1100, 128, 128, False, [1100, 1025]),
     (2, 3, 300, 700, 16, 16, True, [700, 250]),  # several 128-key tiles, ragged tail
     # d = 64 causal: 32-key tiles up to 512 keys, 64-key tiles beyond
     (2, 2, 300, 512, 64, 64, True, [512, 129]),

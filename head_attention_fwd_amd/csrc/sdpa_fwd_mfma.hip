@@ -315,7 +315,10 @@ struct Attn {
     }
 
     // acc += V^T P^T for block bk (its two 16-key slabs kk = 2*bk, 2*bk + 1).
-    __device__ __forceinline__ void pv(const uint16_t *Vs, int bk, const bf16x8_t *p)
+    // zero: the accumulator is known to be 0 (the first product of the key
+    // loop; a constant after unrolling), so the first MFMA starts from 0
+    // instead of reading it.
+    __device__ __forceinline__ void pv(const uint16_t *Vs, int bk, const bf16x8_t *p, bool zero = false)
     {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -326,7 +329,7 @@ struct Attn {
                 const u32x2_t lo = ds_read_tr16_b64((const uint16_t *)(vb + (16 * kk) * kRowBytes));
                 const u32x2_t hi = ds_read_tr16_b64((const uint16_t *)(vb + (16 * kk + 4) * kRowBytes));
                 const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-                acc[db] = mfma32(as_bf16x8(a), p[h], acc[db]);
+                acc[db] = mfma32(as_bf16x8(a), p[h], (zero && h == 0) ? f32x16_t{} : acc[db]);
             }
         }
     }
@@ -372,8 +375,15 @@ struct Attn {
 
     // Move the reference maximum of the rows whose block maximum grew by more
     // than kTau over it, rescaling what was accumulated against the old one.
-    __device__ __forceinline__ void rescale_if_needed(float mxs)
+    // fresh: no legal key has been seen yet (the key loop's first block; a
+    // constant after unrolling), so the accumulator and the row sum are 0 and
+    // the reference maximum is simply the block maximum.
+    __device__ __forceinline__ void rescale_if_needed(float mxs, bool fresh = false)
     {
+        if (fresh) {
+            m_run = mxs;
+            return;
+        }
         const bool grow = mxs > m_run + kTau;    // false while mxs is -inf
         if (__builtin_expect(__any(grow), 0)) {
             // Keep this a real branch: after the first blocks it is rarely taken,
@@ -504,6 +514,10 @@ struct Attn {
     // with no legal key for any row of the wave contributes exactly 0.
     // Decisions are per row, so a row's result depends on its own legal keys
     // only.
+    // FIRST: the first tile of the key loop (the accumulator and the row sum
+    // are still 0: its first block sets the reference maxima without scaling,
+    // and its first product starts from 0).
+    template <bool FIRST = false>
     __device__ __forceinline__ void tile_blocks_masked(const uint16_t *Ks, const uint16_t *Vs, int lim,
                                                        int lo = 0)
     {
@@ -528,12 +542,12 @@ struct Attn {
                     if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;
             }
             const float mxs = block_max(s[b]);
-            if (b > 0) pv(Vs, b - 1, p[b - 1]);
-            rescale_if_needed(mxs);
+            if (b > 0) pv(Vs, b - 1, p[b - 1], FIRST && b == 1);
+            rescale_if_needed(mxs, FIRST && b == 0);
             if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
             l_run += weights(s[b], p[b]);
         }
-        pv(Vs, NB - 1, p[NB - 1]);
+        pv(Vs, NB - 1, p[NB - 1], FIRST && NB == 1);
     }
 
     // Issue the copies of tile u into buffer u % kBuffers.
@@ -593,6 +607,19 @@ struct Attn {
     {
         tile_begin(t, kbuf[(BUF + 2) % 3], vbuf[(BUF + 2) % 3]);
         tile_blocks_full(kbuf[BUF], vbuf[BUF], kbuf[(BUF + 1) % 3], s_io);
+    }
+
+    // Tile 0 of the unrestricted kernel: every wave has keys in it (key 0 is
+    // legal for every row when the tile exists), so there is no early exit,
+    // and the accumulator is still 0.
+    __device__ __forceinline__ void tile_first()
+    {
+        tile_begin(0, kbuf[2], vbuf[2]);
+        int64_t lim64 = len;
+        const int64_t causal_lim = q0w + l32 + 1;
+        if (causal && causal_lim < lim64) lim64 = causal_lim;
+        const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));
+        tile_blocks_masked<true>(kbuf[0], vbuf[0], lim);
     }
 
     // Any other tile, with the buffer chosen at run time.
@@ -672,7 +699,7 @@ struct Attn {
             }
             return;
         }
-        tile_any(0);
+        tile_first();
         int t = 1;
         if (n_full > 1) {
             if constexpr (kFirstWaitOne) {

@@ -622,7 +622,9 @@ struct Attn {
         tile_blocks_masked<true>(kbuf[0], vbuf[0], lim);
     }
 
-    // Any other tile, with the buffer chosen at run time.
+    // Any other tile, with the buffer chosen at run time (FIRST: tile 0, whose
+    // blocks start from a zero accumulator).
+    template <bool FIRST = false>
     __device__ __forceinline__ void tile_any(int t)
     {
         const int buf = t % 3;
@@ -643,7 +645,7 @@ struct Attn {
             const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));
             const int64_t lo64 = (qrel - kv0) + l32 - radius;
             const int lo = (int)(lo64 < 0 ? 0 : (lo64 > BN ? BN : lo64));
-            tile_blocks_masked(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim, lo);
+            tile_blocks_masked<FIRST>(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim, lo);
             return;
         }
         // A wave whose rows all precede the tile's first key has nothing to do.
@@ -654,7 +656,7 @@ struct Attn {
         const int64_t causal_lim = (q0w - kv0) + l32 + 1;
         if (causal && causal_lim < lim64) lim64 = causal_lim;
         const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));
-        tile_blocks_masked(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim);
+        tile_blocks_masked<FIRST>(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim);
     }
 
     // All key tiles: the first, then the fully legal ones in a loop unrolled
@@ -754,7 +756,8 @@ struct Attn {
         // the masked tiles after it.
         const bool ring = f_hi > f_lo;
         const int64_t ring_lo = ring ? f_lo : n_tiles;
-        int t = 0;
+        tile_any<true>(0);    // f_lo >= 1
+        int t = 1;
         for (; t < ring_lo && t < n_tiles; ++t) tile_any(t);
         if (ring && t == f_lo) {
             // tile f_lo landed before tile f_lo-1's barrier; enter the ring at

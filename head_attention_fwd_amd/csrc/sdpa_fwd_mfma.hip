@@ -95,7 +95,7 @@ constexpr int kLongKeys128 = 1024;     // d = 128 launches with more keys take t
 constexpr int kBandKeyBlocks64 = 1;    // restricted attention, d = 64: 32-key tiles (finer band edges)
 // Waves per SIMD the register budget is set for, by head size: D = 128 needs
 // 64 accumulator and 32 Q-operand registers (2 waves; 3 for long key ranges,
-// 167 VGPRs), D = 32 and D = 16 fit 4; D = 64 with 32-key tiles (one score
+// 168 VGPRs), D = 32 and D = 16 fit 4; D = 64 with 32-key tiles (one score
 // block in flight) fits 4 as well.
 template <int D, int NB = 2, bool BAND = false>
 struct Occupancy {
@@ -1397,8 +1397,8 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
                          hipStream_t stream)
 {
     // D = 16: 2-wave workgroups (64 query rows) with 64-key tiles, so that each
-    // wave copies one whole 1 KiB slice and, at 12 KiB of LDS and 98 VGPRs, a CU
-    // holds 8 of them (2048 slots; 4-wave workgroups with 128-key tiles: 1024).
+    // wave copies one whole 1 KiB slice and, at 12 KiB of LDS and 86 VGPRs, a CU
+    // holds 10 of them (2560 slots; 4-wave workgroups with 128-key tiles: 1024).
     constexpr int NW = D <= 16 ? 2 : kWaves;
     // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB.
     constexpr int NB = D >= 128 ? 1 : (D >= 32 ? kKeyBlocks : 2);
@@ -1408,7 +1408,7 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     if constexpr (D == 64) {
         // Causal self-attention over short key ranges: 32-key tiles at four
-        // waves per SIMD (24 KiB of LDS, 127 VGPRs), so that every query tile of
+        // waves per SIMD (24 KiB of LDS, 115 VGPRs), so that every query tile of
         // the base model's decoder is resident at once, and the tiles that
         // cross the diagonal are half as long.
         if (causal && Lk <= kShortCausalKeys) {
@@ -1419,7 +1419,7 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
         }
     }
     if constexpr (D == 128) {
-        // Long key ranges: a register budget of three waves per SIMD (167
+        // Long key ranges: a register budget of three waves per SIMD (168
         // VGPRs), long causal 496 -> 480 us; short launches keep two (19.1
         // against 19.7 us on the h = 4 encoder).
         if (Lk > kLongKeys128) {

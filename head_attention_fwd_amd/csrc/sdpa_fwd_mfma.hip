@@ -536,7 +536,10 @@ struct Attn {
                     const int off = 16 * (r >> 3) + (r & 7);
                     if (off >= lim_g || off < lo_g) s[b][r] = -INFINITY;
                 }
-            } else {
+            } else if (__builtin_amdgcn_ballot_w64(lim_g < 24) != 0) {
+                // some lane's last legal key offset is below 23 (else the
+                // block is fully legal for the wave: no per-element masks)
+                asm volatile("" ::: "memory");
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;

@@ -517,7 +517,11 @@ struct Attn {
     // FIRST: the first tile of the key loop (the accumulator and the row sum
     // are still 0: its first block sets the reference maxima without scaling,
     // and its first product starts from 0).
-    template <bool FIRST = false>
+    // MAXFREE: a later tile of the unrestricted kernel (every row met key 0
+    // in tile 0, so its reference maximum is finite): no block maxima, the
+    // weights are taken against the reference as on the fully legal tiles,
+    // masked keys give exp2(-inf) = 0.
+    template <bool FIRST = false, bool MAXFREE = false>
     __device__ __forceinline__ void tile_blocks_masked(const uint16_t *Ks, const uint16_t *Vs, int lim,
                                                        int lo = 0)
     {
@@ -544,11 +548,18 @@ struct Attn {
                 for (int r = 0; r < 16; ++r)
                     if (16 * (r >> 3) + (r & 7) >= lim_g) s[b][r] = -INFINITY;
             }
-            const float mxs = block_max(s[b]);
-            if (b > 0) pv(Vs, b - 1, p[b - 1], FIRST && b == 1);
-            rescale_if_needed(mxs, FIRST && b == 0);
-            if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
-            l_run += weights(s[b], p[b]);
+            if constexpr (MAXFREE) {
+                if (b > 0) pv(Vs, b - 1, p[b - 1]);
+                if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
+                const float bsum = weights(s[b], p[b]);
+                finish_max_free(s[b], p[b], bsum);
+            } else {
+                const float mxs = block_max(s[b]);
+                if (b > 0) pv(Vs, b - 1, p[b - 1], FIRST && b == 1);
+                rescale_if_needed(mxs, FIRST && b == 0);
+                if (b + 1 < NB) s[b + 1] = scores(Ks, b + 1);
+                l_run += weights(s[b], p[b]);
+            }
         }
         pv(Vs, NB - 1, p[NB - 1], FIRST && NB == 1);
     }
@@ -627,7 +638,7 @@ struct Attn {
 
     // Any other tile, with the buffer chosen at run time (FIRST: tile 0, whose
     // blocks start from a zero accumulator).
-    template <bool FIRST = false>
+    template <bool FIRST = false, bool MAXFREE = false>
     __device__ __forceinline__ void tile_any(int t)
     {
         const int buf = t % 3;
@@ -659,7 +670,7 @@ struct Attn {
         const int64_t causal_lim = (q0w - kv0) + l32 + 1;
         if (causal && causal_lim < lim64) lim64 = causal_lim;
         const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BN ? BN : lim64));
-        tile_blocks_masked<FIRST>(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim);
+        tile_blocks_masked<FIRST, MAXFREE>(kbuf[0] + buf * kBufStride, vbuf[0] + buf * kBufStride, lim);
     }
 
     // All key tiles: the first, then the fully legal ones in a loop unrolled
@@ -731,7 +742,7 @@ struct Attn {
                 if (t < n_full) tile_full<2>(t++, s_io);
             }
         }
-        for (; t < n_tiles; ++t) tile_any(t);
+        for (; t < n_tiles; ++t) tile_any<false, true>(t);   // reference maxima finite since tile 0
     }
 
     // BAND: the fully legal tiles of this wave form the middle range

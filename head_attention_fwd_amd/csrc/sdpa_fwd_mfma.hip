@@ -51,12 +51,13 @@
 //    wave needs independent matrix work in its instruction stream to keep both
 //    units busy).  P.V of block b-1 is issued before block b's rescale check,
 //    so a rare move of the reference maximum only rescales the accumulator.
-//  * Fully legal tiles after the first compute no row maximum: a row's
-//    weights are taken against its reference maximum, and only when they sum
-//    past 2^20 (rare) does the row recompute them against the block maximum.
-//    The first tile and tiles crossing the causal diagonal or the padding end
-//    compute block maxima; only the latter apply masks.  Tiles entirely beyond the key
-//    length are never loaded.
+//  * Tiles after the first compute no row maximum: a row's weights are taken
+//    against its reference maximum, and only when they sum past 2^20 (rare)
+//    does the row recompute them against the block maximum.  Only the first
+//    tile computes block maxima (restricted attention: every tile outside
+//    the fully legal middle range); tiles crossing the causal diagonal or the
+//    padding end apply masks.  Tiles entirely beyond the key length are never
+//    loaded.
 //  * Work order: one query tile per workgroup, each XCD on its own run of
 //    heads so the workgroups streaming one head's K/V share an L2; causal
 //    grids dispatch the longest query tiles first (greedy longest-first over
@@ -507,13 +508,13 @@ struct Attn {
     }
 
     // Any other tile (the first, one crossing the causal diagonal or the
-    // padding end, one beyond this wave's rows) block by block, with block
-    // maxima and masks: key kv0 + 32*b + 16*(r/8) + 8*g + r%8 is legal iff
-    // that offset < lim.  On the first tile the block maxima set every row's
-    // reference maximum (key 0 is legal for every row when len > 0).  A block
-    // with no legal key for any row of the wave contributes exactly 0.
-    // Decisions are per row, so a row's result depends on its own legal keys
-    // only.
+    // padding end, one beyond this wave's rows) block by block, with masks
+    // (key kv0 + 32*b + 16*(r/8) + 8*g + r%8 is legal iff that offset < lim)
+    // and, unless MAXFREE, block maxima.  On the first tile the block maxima
+    // set every row's reference maximum (key 0 is legal for every row when
+    // len > 0).  A block with no legal key for any row of the wave
+    // contributes exactly 0.  Decisions are per row, so a row's result
+    // depends on its own legal keys only.
     // FIRST: the first tile of the key loop (the accumulator and the row sum
     // are still 0: its first block sets the reference maxima without scaling,
     // and its first product starts from 0).

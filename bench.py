@@ -10,7 +10,7 @@ workloads (--config) are available for profiling; they are parity cases, not
 headline lines.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
-                  [--no-cpu-baseline] [--rotate R] [--settle-ms MS]
+                  [--no-cpu-baseline] [--rotate R] [--settle-ms MS] [--sustain-s S]
   python bench.py --copy-mib 512      (calibration: a plain device copy)
   python bench.py --gemm-probe 8192   (calibration: a bf16 GEMM through torch;
                                        also M,K,N, e.g. 32768,1024,3072)
@@ -25,8 +25,10 @@ Besides the metric, the line carries: the roofline of the dominant kernel (with
 the measured HBM traffic per launch and its ratio to the algorithmic bytes while
 the counters match the kernel source), the oracle on the host cores beside it
 (all cores and one thread, with the CPU model), the GPU output compared with
-the oracle's values on the oracle's sample of rows ("parity"), and the shader
-clock sampled during the timed window.
+the oracle's values on the oracle's sample of rows ("parity"), the shader
+clock sampled during the timed window, and ("sustained", --sustain-s, default
+2 s) the rate of the same launches kept up for seconds, with the board power
+beside the board's power limit.
 
 FLOPs are algorithmic: (2*d_k + 2*d_v) per (query, key) pair the mask allows
 (page "Attention Is All You Need/paper/es", §4, Table 1: O(n^2 d) per layer),
@@ -229,15 +231,21 @@ def parity_record(got, ref, v_absmax, dtype, what):
 
 
 class ClockSampler:
-    """Samples the shader clock the driver reports (sysfs pp_dpm_sclk, the line
-    marked current) from a host thread while the GPU works."""
+    """Samples, from a host thread while the GPU works, the shader clock the
+    driver reports (sysfs pp_dpm_sclk, the line marked current) and the board
+    power with its limit (hwmon power1_input / power1_cap, microwatts; the
+    driver's reading is a running average that takes ~0.4 s to follow a change
+    of load)."""
 
     def __init__(self, period_s=0.002):
         import glob
         import threading
         self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.hwmon = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*"))[:1]
         self.period = period_s
         self.samples = []
+        self.power = []          # (seconds since start, watts)
+        self.cap_w = None
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
@@ -252,15 +260,29 @@ class ClockSampler:
                 continue
         return None
 
+    def _read_hwmon(self, name):
+        for d in self.hwmon:
+            try:
+                with open(os.path.join(d, name), encoding="ascii") as f:
+                    return int(f.read().strip()) * 1e-6
+            except (OSError, ValueError):
+                continue
+        return None
+
     def _run(self):
+        t0 = time.perf_counter()
         while not self._stop.is_set():
             v = self._read()
             if v is not None:
                 self.samples.append(v)
+            w = self._read_hwmon("power1_input")
+            if w is not None:
+                self.power.append((time.perf_counter() - t0, w))
             time.sleep(self.period)
 
     def __enter__(self):
-        if self.paths:
+        if self.paths or self.hwmon:
+            self.cap_w = self._read_hwmon("power1_cap")
             self._thread.start()
         return self
 
@@ -276,6 +298,45 @@ class ClockSampler:
         return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1], "n": len(v),
                 "source": "sysfs pp_dpm_sclk (current level), sampled every 2 ms during the "
                           "timed window"}
+
+    def power_summary(self, after_s=0.0):
+        """Board power over the samples taken at least after_s into the window."""
+        w = sorted(p for t, p in self.power if t >= after_s)
+        if not w:
+            return None
+        return {"median_w": w[len(w) // 2], "min_w": w[0], "max_w": w[-1], "n": len(w),
+                "cap_w": self.cap_w, "from_s": after_s,
+                "source": "hwmon power1_input / power1_cap (driver's running average)"}
+
+
+def sustained(torch, stream, launch, flops_per_launch, seconds, batch=20):
+    """Keep the GPU on one workload for `seconds`: batches of `batch` launches, each
+    batch bracketed by events on the launch stream, the board power and clock
+    sampled beside them.  Reports the rate over the second half of the window,
+    once the power reading has followed the load, with the power and clock of
+    the same half.  Not part of `value`: it shows where the sustained rate sits
+    against the board's power limit."""
+    batches = []
+    with ClockSampler(period_s=0.005) as smp:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(batch):
+                launch()
+            e1.record(stream)
+            e1.synchronize()
+            batches.append((time.perf_counter() - t0, e0, e1))
+    half = seconds / 2
+    late = [(e0, e1) for t, e0, e1 in batches if t >= half] or [(e0, e1) for _, e0, e1 in batches]
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in late) / (batch * len(late))
+    clk = sorted(smp.samples[len(smp.samples) // 2:])
+    return {"seconds": seconds, "launches_averaged": batch * len(late), "ms_per_launch": ms,
+            "tflops": flops_per_launch / (ms * 1e-3) / 1e12 if flops_per_launch else None,
+            "power": smp.power_summary(after_s=half),
+            "clock_median_mhz": clk[len(clk) // 2] if clk else None,
+            "window": "second half of %.1f s of back-to-back launches" % seconds}
 
 
 TIMELINE_FILES = ("fwd", "wide", "row")   # instrumented sources (readers sdpa_timeline_<name>)
@@ -380,10 +441,15 @@ def gemm_probe(torch, dev, args):
         torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
     flop = 2.0 * m * k * n
+    sust = None
+    if args.sustain_s > 0:
+        sust = sustained(torch, torch.cuda.current_stream(dev), lambda: torch.matmul(a, b, out=c),
+                         flop, args.sustain_s, batch=5)
+        sust["frac_of_peak"] = sust["tflops"] / PEAK_TFLOPS["bf16"]
     print(json.dumps({"probe": "bf16 GEMM C = A B through torch.matmul (hipBLASLt), calibration only",
                       "M": m, "K": k, "N": n, "ms_per_gemm": ms, "tflops": flop / (ms * 1e-3) / 1e12,
                       "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
-                      "clock": clk.summary()}), flush=True)
+                      "clock": clk.summary(), "sustained": sust}), flush=True)
 
 
 def overlap_probe(torch, dev, args):
@@ -428,6 +494,15 @@ def overlap_probe(torch, dev, args):
             raise RuntimeError("sdpa_calib_overlap failed")
         torch.cuda.synchronize()
     res = {}
+    if args.sustain_s > 0:
+        def launcher(which):
+            def go():
+                if lib.sdpa_calib_overlap(0, which, out.data_ptr(), n_wg, iters, stream.cuda_stream) != 0:
+                    raise RuntimeError("sdpa_calib_overlap failed")
+            return go
+        res["sustained_vgpr_accumulators"] = {
+            k: sustained(torch, stream, launcher(w), None, args.sustain_s, batch=5)
+            for k, w in (("matrix_only", 0), ("vector_only", 1), ("both", 2))}
     for mode, name in ((0, "vgpr_accumulators"), (1, "accumulation_registers")):
         r = {k: timed(mode, w) for k, w in (("matrix_only", 0), ("vector_only", 1), ("both", 2))}
         r["both_over_sum"] = r["both"]["ms"] / (r["matrix_only"]["ms"] + r["vector_only"]["ms"])
@@ -465,6 +540,9 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="per-workgroup phases of single cold launches (timestamped build "
                          "libsdpa_timeline.so) instead of the timed steps")
+    ap.add_argument("--sustain-s", type=float, default=2.0,
+                    help="after the timed steps, keep launching for this long and report the "
+                         "sustained rate with the board power and its limit (0: skip)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through (0: enough for >= 1 GiB on HBM-bound "
                          "workloads, 1 otherwise)")
@@ -732,6 +810,22 @@ def main():
     roof["traffic_ratio"] = None if traffic is None else traffic / nbytes
     roof["kernel_ms"] = kern_ms
 
+    sust = None
+    if args.sustain_s > 0:
+        if use_graph:
+            def launch():
+                with torch.cuda.stream(gs):
+                    graph.replay()
+            sust = sustained(torch, gs, launch, flops * args.steps, args.sustain_s, batch=1)
+            sust["launch"] = "one replay of the %d-step graph" % args.steps
+        else:
+            ctr = [0]
+
+            def launch():
+                step(ctr[0])
+                ctr[0] += 1
+            sust = sustained(torch, stream, launch, flops, args.sustain_s)
+
     # The output of input set 0 (written by the timed steps) against the oracle's
     # values on the rows the CPU baseline computes: the line checks itself.
     cpu, parity = None, None
@@ -770,6 +864,7 @@ def main():
         "clock": None if clk is None else clk.summary(),
         "launch_us": launch_us,
         "warm": warm,
+        "sustained": sust,
         "wall_s_timed": wall,
     }
     print(json.dumps(rec), flush=True)

@@ -54,6 +54,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw (stride 0) dword buffer access
+// Cache policy of the key/value loads: non-temporal (nt; the builtin's slc
+// position on gfx950).  A decode step reads each cached K/V row exactly once,
+// so the rows stream through instead of being allocated in the L2 and the
+// Infinity Cache.  Measured (interleaved rounds, cold caches): long decode
+// -6.6 % (d = 64) and -4.6 % (d = 128), base decode -3.5 % and -6.5 %.
+constexpr int kLoadStreaming = 2;
 constexpr float kTau = 8.0f;             // lazy-rescale threshold, log2 units
 constexpr int kLoads = 8;                // 16-byte loads of K (and of V) per lane per step
 constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;
@@ -164,10 +170,10 @@ __global__ __launch_bounds__(64 * NW) void sdpa_decode_row_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kLoads; ++i)
-            kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, loff + (uint32_t)(i * kJ * kRowBytes), 0, 0);
+            kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, loff + (uint32_t)(i * kJ * kRowBytes), 0, kLoadStreaming);
 #pragma unroll
         for (int i = 0; i < kLoads; ++i)
-            vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, loff + (uint32_t)(i * kJ * kRowBytes), 0, 0);
+            vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, loff + (uint32_t)(i * kJ * kRowBytes), 0, kLoadStreaming);
         __builtin_amdgcn_sched_barrier(0);
     };
 

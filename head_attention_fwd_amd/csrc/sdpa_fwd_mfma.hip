@@ -89,6 +89,7 @@ constexpr int kKeyBlocks = 2;          // 32-key blocks per LDS tile (d = 128: 1
 constexpr int kSplitKeyBlocks = 1;     // 32-key blocks per LDS tile of the key-split kernel
 constexpr int kShortCausalKeys = 512;  // d = 64 causal launches up to this many keys take 32-key tiles
 constexpr int kCausalHeadGroup = 4;    // causal order: heads per group on an XCD
+constexpr int kStreamQueryTiles = 4;   // K/V copies non-temporal up to this many query tiles per head
 constexpr int kWavesPerSimd64 = 3;     // register budget at d = 64 with 64-key tiles
 constexpr int kWavesPerSimd128 = 2;    // register budget of the forward kernel at d = 128 ...
 constexpr int kWavesPerSimd128Long = 3;   // ... and of its form for long key ranges
@@ -193,12 +194,18 @@ constexpr int kStoreStreaming = 2;
 // therefore orders these copies itself (wait_vmem_keep before each barrier).
 // M0 is written here and nowhere else in this kernel (nothing else in it uses
 // M0 on gfx950), so it is not declared clobbered (it is a reserved register).
+// STREAM: the non-temporal cache policy (nt), for rows that few workgroups read.
+template <bool STREAM = false>
 __device__ inline void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint16_t *dst, uint32_t voff)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)dst);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
 }
 
 // K/V tile loads go straight from HBM into LDS (buffer_load_dwordx4 ... lds): no
@@ -235,9 +242,10 @@ struct TileLoader {
         }
     }
 
-    // Issue the asynchronous copies of rows kv0 .. kv0+BN-1 (rows >= valid read 0).
+    // Issue the asynchronous copies of rows kv0 .. kv0+BN-1 (rows >= valid read 0);
+    // stream (wave-uniform): with the non-temporal cache policy.
     __device__ inline void issue(const uint16_t *Kh, const uint16_t *Vh, int64_t kv0,
-                                 int64_t valid, uint16_t *Ks, uint16_t *Vs) const
+                                 int64_t valid, uint16_t *Ks, uint16_t *Vs, bool stream = false) const
     {
         int64_t rows = valid - kv0;
         rows = rows < 0 ? 0 : (rows > BN ? BN : rows);
@@ -246,10 +254,18 @@ struct TileLoader {
             __builtin_amdgcn_make_buffer_rsrc((void *)(Kh + kv0 * D), (short)0, nbytes, kBufferRsrcWord3);
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void *)(Vh + kv0 * D), (short)0, nbytes, kBufferRsrcWord3);
+        if (stream) {
 #pragma unroll
-        for (int j = 0; j < kPerWave; ++j) {
-            copy_to_lds(rk, Ks + (slice0 + j) * 512, koff[j]);
-            copy_to_lds(rv, Vs + (slice0 + j) * 512, voff[j]);
+            for (int j = 0; j < kPerWave; ++j) {
+                copy_to_lds<true>(rk, Ks + (slice0 + j) * 512, koff[j]);
+                copy_to_lds<true>(rv, Vs + (slice0 + j) * 512, voff[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPerWave; ++j) {
+                copy_to_lds(rk, Ks + (slice0 + j) * 512, koff[j]);
+                copy_to_lds(rv, Vs + (slice0 + j) * 512, voff[j]);
+            }
         }
     }
 };
@@ -297,6 +313,7 @@ struct Attn {
     int n_tiles;
     int64_t qrel;                    // BAND: q0w relative to the first key of the range
     int64_t radius;                  // BAND: neighbourhood radius
+    bool kv_stream = false;          // K/V copies non-temporal (few query tiles per head)
     float scale_log2;
     int g;                           // lane half
 
@@ -575,7 +592,7 @@ struct Attn {
     // Issue the copies of tile u into buffer u % kBuffers.
     __device__ __forceinline__ void prefetch(int u, uint16_t *kb, uint16_t *vb)
     {
-        ld.issue(Kh, Vh, (int64_t)u * BN, len, kb, vb);
+        ld.issue(Kh, Vh, (int64_t)u * BN, len, kb, vb, kv_stream);
     }
 
     // Q^T as the B operand of the score MFMA, from where the prologue staged it
@@ -820,7 +837,7 @@ __device__ __forceinline__ void attend_query_tile(
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
     uint32_t bh, uint32_t qt, int wave, int lane, int64_t kv_lo, int64_t kv_hi, const SplitOut &so, uint32_t u,
-    int64_t radius = 0)
+    int64_t radius = 0, bool kv_stream = false)
 {
     using A = Attn<NW, NB, D, BAND>;
     constexpr int BM = A::BM;
@@ -836,6 +853,7 @@ __device__ __forceinline__ void attend_query_tile(
 #pragma unroll
     for (int i = 0; i < A::kBuffers; ++i) { st.kbuf[i] = kbuf[i]; st.vbuf[i] = vbuf[i]; }
     st.causal = causal;
+    st.kv_stream = kv_stream;
     st.scale_log2 = scale_log2;
     st.g = g;
     st.q0w = q0 + 32 * wave;
@@ -1048,7 +1066,7 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void sdpa_fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
-    uint32_t n_qtiles, uint32_t n_bh)
+    uint32_t n_qtiles, uint32_t n_bh, int kv_stream)
 {
     using A = Attn<NW, NB, D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride + A::kLdsPad];
@@ -1087,7 +1105,8 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void sdpa_fwd_mfma_kernel(
         qt = item % n_qtiles;
     }
     attend_query_tile<NW, NB, D, false>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk,
-                                     scale_log2, bh, qt, wave, lane, 0, Lk, SplitOut{}, 0);
+                                     scale_log2, bh, qt, wave, lane, 0, Lk, SplitOut{}, 0, 0,
+                                     kv_stream != 0);
 }
 
 
@@ -1428,6 +1447,9 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    // Each K/V row is copied once per query tile of its head: with few of them
+    // the rows stream through the caches (non-temporal copies).
+    const int kv_stream = n_qtiles <= kStreamQueryTiles;
     if constexpr (D == 64) {
         // Causal self-attention over short key ranges: 32-key tiles at four
         // waves per SIMD (24 KiB of LDS, 115 VGPRs), so that every query tile of
@@ -1436,7 +1458,7 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
         if (causal && Lk <= kShortCausalKeys) {
             hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, 1, D>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths, causal,
-                               (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh);
+                               (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh, kv_stream);
             return hipGetLastError();
         }
     }
@@ -1448,14 +1470,14 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
             hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D, kWavesPerSimd128Long>), dim3(n_qtiles * n_bh),
                                dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
                                (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
-                               scale_log2, n_qtiles, n_bh);
+                               scale_log2, n_qtiles, n_bh, kv_stream);
             return hipGetLastError();
         }
     }
     hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D>), dim3(n_qtiles * n_bh),
                        dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
                        (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
-                       scale_log2, n_qtiles, n_bh);
+                       scale_log2, n_qtiles, n_bh, kv_stream);
     return hipGetLastError();
 }
 

@@ -943,7 +943,11 @@ __device__ __forceinline__ void attend_query_tile(
                 const int r0 = kRps * sl;                    // first Q row of this copy
                 const uint16_t *dst = D < 32 ? st.kbuf[2] + 32 * wave * kD
                                              : (r0 < 16 ? st.kbuf[2] : st.vbuf[2]) + (16 * wave + (r0 & 15)) * kD;
-                copy_to_lds(rq, dst, (uint32_t)(qrow * kRowBytes + (((lane % kC) ^ swz<D>(qrow)) << 4)));
+                const uint32_t voff = (uint32_t)(qrow * kRowBytes + (((lane % kC) ^ swz<D>(qrow)) << 4));
+                // Q rows are read by this workgroup only: on the short launches
+                // non-temporal too (big cross -2.4 %; on long launches no gain)
+                if (kv_stream) copy_to_lds<true>(rq, dst, voff);
+                else copy_to_lds(rq, dst, voff);
             }
         } else {
             // Q^T operand straight into registers: lane (l32, g) holds row l32,

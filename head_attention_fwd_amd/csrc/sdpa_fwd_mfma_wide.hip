@@ -89,6 +89,10 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw (stride 0) dword buffer access
 // written once and not read by the launch (Table 3 row (A) encoder, d = 512:
 // -3.7 % on cold inputs).
 constexpr int kStoreStreaming = 2;
+// K/V copies non-temporal when a head has at most this many query tiles (each
+// K/V row copied into LDS by at most four workgroups at nearly the same time):
+// the d = 512 encoder -4.6 %.
+constexpr int kStreamQueryTiles = 4;
 constexpr int kPF = 2;                  // LDS operand reads issued this many MFMA steps ahead
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
 
@@ -125,12 +129,18 @@ __device__ inline f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c)
 // before each LDS read) nor reorders LDS accesses across it; the kernel waits
 // for its copies itself (vmcnt(0) before each barrier).  Nothing else in this
 // kernel uses M0 on gfx950.
+// STREAM: the non-temporal cache policy (nt).
+template <bool STREAM = false>
 __device__ inline void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, const uint16_t *dst, uint32_t voff)
 {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)dst);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m0), "v"(voff), "s"(rsrc) : "memory");
 }
 
 // Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups holding one
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(512
 void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                                const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths,
                                int causal, uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk,
-                               float scale_log2, uint32_t n_qtiles, uint32_t n_bh)
+                               float scale_log2, uint32_t n_qtiles, uint32_t n_bh, int kv_stream)
 {
     static_assert(D == 256 || D == 512, "wide heads only");
     constexpr int kRowBytes = 2 * D;
@@ -238,12 +248,21 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void *)(Vh + kv0 * D), (short)0, nbytes, kRsrcWord3);
         uint16_t *kb = lds + (t & 1) * 2 * kTileElems;
+        if (kv_stream) {
 #pragma unroll
-        for (int j = 0; j < kSlicesPerWave; ++j) {
-            copy_to_lds(rk, kb + (wave * kSlicesPerWave + j) * 512, coff[j]);
-            // V: XOR with chunk_xor(r) instead of r mod 16
-            const uint32_t vo = coff[j] ^ (uint32_t)(((cpos[j] & 15) ^ chunk_xor(cpos[j])) << 4);
-            copy_to_lds(rv, kb + kTileElems + (wave * kSlicesPerWave + j) * 512, vo);
+            for (int j = 0; j < kSlicesPerWave; ++j) {
+                copy_to_lds<true>(rk, kb + (wave * kSlicesPerWave + j) * 512, coff[j]);
+                // V: XOR with chunk_xor(r) instead of r mod 16
+                const uint32_t vo = coff[j] ^ (uint32_t)(((cpos[j] & 15) ^ chunk_xor(cpos[j])) << 4);
+                copy_to_lds<true>(rv, kb + kTileElems + (wave * kSlicesPerWave + j) * 512, vo);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kSlicesPerWave; ++j) {
+                copy_to_lds(rk, kb + (wave * kSlicesPerWave + j) * 512, coff[j]);
+                const uint32_t vo = coff[j] ^ (uint32_t)(((cpos[j] & 15) ^ chunk_xor(cpos[j])) << 4);
+                copy_to_lds(rv, kb + kTileElems + (wave * kSlicesPerWave + j) * 512, vo);
+            }
         }
     };
 
@@ -397,7 +416,8 @@ hipError_t launch_wide_d(const void *Q, const void *K, const void *V, const int3
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     hipLaunchKernelGGL((sdpa_fwd_mfma_wide_kernel<D>), dim3(n_qtiles * n_bh), dim3(kWaves * 64), 0,
                        stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                       key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh);
+                       key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh,
+                       (int)(n_qtiles <= kStreamQueryTiles));
     return hipGetLastError();
 }
 

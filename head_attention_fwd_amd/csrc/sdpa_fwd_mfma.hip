@@ -87,7 +87,7 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 constexpr int kWaves = 4;              // waves per workgroup (32 query rows each); d = 16: 2
 constexpr int kKeyBlocks = 2;          // 32-key blocks per LDS tile (d = 128: 1)
 constexpr int kSplitKeyBlocks = 1;     // 32-key blocks per LDS tile of the key-split kernel
-constexpr int kShortCausalKeys = 512;  // d = 64 causal launches up to this many keys take 32-key tiles
+constexpr int kShortKeys = 512;        // d = 64 launches up to this many keys take 32-key tiles
 constexpr int kCausalHeadGroup = 4;    // causal order: heads per group on an XCD
 constexpr int kStreamQueryTiles = 4;   // K/V copies non-temporal up to this many query tiles per head
 constexpr int kWavesPerSimd64 = 3;     // register budget at d = 64 with 64-key tiles
@@ -1455,11 +1455,13 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     // the rows stream through the caches (non-temporal copies).
     const int kv_stream = n_qtiles <= kStreamQueryTiles;
     if constexpr (D == 64) {
-        // Causal self-attention over short key ranges: 32-key tiles at four
-        // waves per SIMD (24 KiB of LDS, 115 VGPRs), so that every query tile of
-        // the base model's decoder is resident at once, and the tiles that
-        // cross the diagonal are half as long.
-        if (causal && Lk <= kShortCausalKeys) {
+        // Short key ranges: 32-key tiles at four waves per SIMD (24 KiB of
+        // LDS, 115 VGPRs), so that every query tile of the base model's
+        // launches is resident at once (causal: the tiles that cross the
+        // diagonal are also half as long).  Base encoder -4 %, big cross -2 %
+        // against 64-key tiles at three waves per SIMD, once the stores and the
+        // short launches' copies were non-temporal.
+        if (Lk <= kShortKeys) {
             hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, 1, D>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0, stream,
                                (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths, causal,
                                (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh, kv_stream);

@@ -115,7 +115,7 @@ sdpa_status validate(const void *Q, const void *K, const void *V, const int32_t 
 sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                             int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
                             int64_t d_k, int64_t d_v, int dtype, hipStream_t s,
-                            int64_t radius = -1)
+                            int64_t radius = -1, bool streaming = true)
 {
     // A radius that reaches every (query, key) pair restricts nothing: the
     // largest |i - j| is max(Lq, Lk) - 1.  Then the unrestricted kernels run
@@ -128,11 +128,11 @@ sdpa_status forward_kernels(const void *Q, const void *K, const void *V, const i
             return hip_status(sdpa::launch_mfma_band(Q, K, V, key_lengths, causal ? 1 : 0, radius, out,
                                                      B, H, Lq, Lk, (int)d_k, s));
         return hip_status(sdpa::launch_mfma(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
-                                            (int)d_k, s));
+                                            (int)d_k, streaming, s));
     }
     if (dtype == SDPA_BF16 && d_k == d_v && (d_k == 256 || d_k == 512) && radius < 0)
         return hip_status(sdpa::launch_mfma_wide(Q, K, V, key_lengths, causal ? 1 : 0, out, B, H, Lq, Lk,
-                                                 (int)d_k, s));
+                                                 (int)d_k, streaming, s));
     return hip_status(sdpa::launch_generic(Q, K, V, key_lengths, causal ? 1 : 0, radius, out, B, H,
                                            Lq, Lk, (int)d_k, (int)d_v, dtype == SDPA_BF16, s));
 }
@@ -430,7 +430,10 @@ sdpa_status sdpa_multihead_forward(const void *Xq, const void *Xkv, const void *
     }
 
     // 2. head_i = Attention(...) for every head (Eq. (1) with the masks).
-    r = forward_kernels(Qh, Kh, Vh, key_lengths, causal, Ah, B, h, Lq, Lk, d_k, d_v, SDPA_BF16, s);
+    // the heads were just written by the projection and the output projection
+    // reads the result next: no streaming cache policy
+    r = forward_kernels(Qh, Kh, Vh, key_lengths, causal, Ah, B, h, Lq, Lk, d_k, d_v, SDPA_BF16, s,
+                        -1, false);
     if (r != SDPA_OK) return r;
 
     // 3. Concat(head_1, ..., head_h) W^O, the concatenation read in place.

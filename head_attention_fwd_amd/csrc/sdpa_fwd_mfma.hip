@@ -831,13 +831,20 @@ struct SplitOut {
 
 // One query tile (BM rows of head bh) against keys [kv_lo, kv_hi): load Q,
 // stream the key tiles, store O (or, with SPLIT, the partial result).
-template <int NW, int NB, int D, bool SPLIT, bool BAND = false>
+// OUT_NT: output stores non-temporal; copies_nt: Q/K/V copies non-temporal
+// (the launcher sets it for heads with few query tiles).  A caller that reads
+// the output right away (the multi-head path's output projection) or whose
+// inputs were just written (its Q/K/V projections) takes neither: there the
+// lines are worth keeping (multi-head base encoder step +2.3 % with them).
+// OUT_NT is a template parameter: as a run-time flag it cost 1 % on the base
+// encoder.
+template <int NW, int NB, int D, bool SPLIT, bool BAND = false, bool OUT_NT = true>
 __device__ __forceinline__ void attend_query_tile(
     uint16_t *const *kbuf, uint16_t *const *vbuf, const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
     uint32_t bh, uint32_t qt, int wave, int lane, int64_t kv_lo, int64_t kv_hi, const SplitOut &so, uint32_t u,
-    int64_t radius = 0, bool kv_stream = false)
+    int64_t radius = 0, bool copies_nt = false)
 {
     using A = Attn<NW, NB, D, BAND>;
     constexpr int BM = A::BM;
@@ -853,7 +860,7 @@ __device__ __forceinline__ void attend_query_tile(
 #pragma unroll
     for (int i = 0; i < A::kBuffers; ++i) { st.kbuf[i] = kbuf[i]; st.vbuf[i] = vbuf[i]; }
     st.causal = causal;
-    st.kv_stream = kv_stream;
+    st.kv_stream = copies_nt;
     st.scale_log2 = scale_log2;
     st.g = g;
     st.q0w = q0 + 32 * wave;
@@ -946,7 +953,7 @@ __device__ __forceinline__ void attend_query_tile(
                 const uint32_t voff = (uint32_t)(qrow * kRowBytes + (((lane % kC) ^ swz<D>(qrow)) << 4));
                 // Q rows are read by this workgroup only: on the short launches
                 // non-temporal too (big cross -2.4 %; on long launches no gain)
-                if (kv_stream) copy_to_lds<true>(rq, dst, voff);
+                if (copies_nt) copy_to_lds<true>(rq, dst, voff);
                 else copy_to_lds(rq, dst, voff);
             }
         } else {
@@ -1039,11 +1046,13 @@ __device__ __forceinline__ void attend_query_tile(
     // the lane index recomputed (mbcnt) rather than kept live across the key
     // loop: at d = 128 keeping it cost a spilled register
     const int lane_o = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    // one branch for the whole stage (the cache policy is an immediate)
 #pragma unroll
     for (int i = 0; i < 32 / kRps; ++i) {
         const int r = kRps * i + lane_o / kC, c = lane_o % kC;
         const u32x4_t w = *(const u32x4_t *)((const char *)stage + r * kRowBytes + ((c ^ oswz(r)) << 4));
-        __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(r * kRowBytes + c * 16), 0, kStoreStreaming);
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, (uint32_t)(r * kRowBytes + c * 16), 0,
+                                               OUT_NT ? kStoreStreaming : 0);
     }
     SDPA_STAMP(3);
 }
@@ -1064,13 +1073,13 @@ __device__ __forceinline__ void attend_query_tile(
 //    fetched 550 MiB per launch into L2, all 8 at once 1188 MiB, one at a time
 //    196 MiB but with the long tiles of the last head starting late).  Short
 //    heads fit the L2 together, and taking all of them at once balances best.
-template <int NW, int NB, int D, int WAVES = Occupancy<D, NB>::kWaves>
+template <int NW, int NB, int D, int WAVES = Occupancy<D, NB>::kWaves, bool OUT_NT = true>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void sdpa_fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths, int causal,
     uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk, float scale_log2,
-    uint32_t n_qtiles, uint32_t n_bh, int kv_stream)
+    uint32_t n_qtiles, uint32_t n_bh, int copies_nt)
 {
     using A = Attn<NW, NB, D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[A::kBuffers * A::kBufStride + A::kLdsPad];
@@ -1108,9 +1117,9 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void sdpa_fwd_mfma_kernel(
         bh = item / n_qtiles;
         qt = item % n_qtiles;
     }
-    attend_query_tile<NW, NB, D, false>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H, Lq, Lk,
-                                     scale_log2, bh, qt, wave, lane, 0, Lk, SplitOut{}, 0, 0,
-                                     kv_stream != 0);
+    attend_query_tile<NW, NB, D, false, false, OUT_NT>(kbuf, vbuf, Q, K, V, key_lengths, causal, O, H,
+                                                    Lq, Lk, scale_log2, bh, qt, wave, lane, 0, Lk,
+                                                    SplitOut{}, 0, 0, copies_nt != 0);
 }
 
 
@@ -1436,10 +1445,29 @@ hipError_t launch_merge_d(const float *ws, void *out, int64_t n_bh, int64_t Lq, 
     return hipGetLastError();
 }
 
+template <int NW, int NB, int D, int WAVES>
+hipError_t launch_fwd(const void *Q, const void *K, const void *V, const int32_t *key_lengths, int causal,
+                      void *out, int64_t H, int64_t Lq, int64_t Lk, float scale_log2, uint32_t n_qtiles,
+                      uint32_t n_bh, bool streaming, hipStream_t stream)
+{
+    // Each K/V row is copied once per query tile of its head: with few of them
+    // the rows stream through the caches (non-temporal copies).
+    const int copies_nt = streaming && n_qtiles <= kStreamQueryTiles;
+    if (streaming)
+        hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D, WAVES, true>), dim3(n_qtiles * n_bh), dim3(NW * 64),
+                           0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths,
+                           causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh, copies_nt);
+    else
+        hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D, WAVES, false>), dim3(n_qtiles * n_bh), dim3(NW * 64),
+                           0, stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths,
+                           causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh, copies_nt);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                          int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                         hipStream_t stream)
+                         bool streaming, hipStream_t stream)
 {
     // D = 16: 2-wave workgroups (64 query rows) with 64-key tiles, so that each
     // wave copies one whole 1 KiB slice and, at 12 KiB of LDS and 86 VGPRs, a CU
@@ -1451,9 +1479,6 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    // Each K/V row is copied once per query tile of its head: with few of them
-    // the rows stream through the caches (non-temporal copies).
-    const int kv_stream = n_qtiles <= kStreamQueryTiles;
     if constexpr (D == 64) {
         // Short key ranges: 32-key tiles at four waves per SIMD (24 KiB of
         // LDS, 115 VGPRs), so that every query tile of the base model's
@@ -1461,30 +1486,20 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
         // diagonal are also half as long).  Base encoder -4 %, big cross -2 %
         // against 64-key tiles at three waves per SIMD, once the stores and the
         // short launches' copies were non-temporal.
-        if (Lk <= kShortKeys) {
-            hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, 1, D>), dim3(n_qtiles * n_bh), dim3(NW * 64), 0, stream,
-                               (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V, key_lengths, causal,
-                               (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh, kv_stream);
-            return hipGetLastError();
-        }
+        if (Lk <= kShortKeys)
+            return launch_fwd<NW, 1, D, Occupancy<D, 1>::kWaves>(Q, K, V, key_lengths, causal, out, H, Lq, Lk,
+                                                                 scale_log2, n_qtiles, n_bh, streaming, stream);
     }
     if constexpr (D == 128) {
         // Long key ranges: a register budget of three waves per SIMD (168
         // VGPRs), long causal 496 -> 480 us; short launches keep two (19.1
         // against 19.7 us on the h = 4 encoder).
-        if (Lk > kLongKeys128) {
-            hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D, kWavesPerSimd128Long>), dim3(n_qtiles * n_bh),
-                               dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
-                               (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
-                               scale_log2, n_qtiles, n_bh, kv_stream);
-            return hipGetLastError();
-        }
+        if (Lk > kLongKeys128)
+            return launch_fwd<NW, NB, D, kWavesPerSimd128Long>(Q, K, V, key_lengths, causal, out, H, Lq, Lk,
+                                                               scale_log2, n_qtiles, n_bh, streaming, stream);
     }
-    hipLaunchKernelGGL((sdpa_fwd_mfma_kernel<NW, NB, D>), dim3(n_qtiles * n_bh),
-                       dim3(NW * 64), 0, stream, (const uint16_t *)Q, (const uint16_t *)K,
-                       (const uint16_t *)V, key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk,
-                       scale_log2, n_qtiles, n_bh, kv_stream);
-    return hipGetLastError();
+    return launch_fwd<NW, NB, D, Occupancy<D, NB>::kWaves>(Q, K, V, key_lengths, causal, out, H, Lq, Lk,
+                                                           scale_log2, n_qtiles, n_bh, streaming, stream);
 }
 
 template <int D>
@@ -1522,13 +1537,13 @@ hipError_t launch_mfma_band(const void *Q, const void *K, const void *V, const i
 
 hipError_t launch_mfma(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                        int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
-                       hipStream_t stream)
+                       bool streaming, hipStream_t stream)
 {
     switch (d) {
-    case 16: return launch_mfma_d<16>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
-    case 32: return launch_mfma_d<32>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
-    case 64: return launch_mfma_d<64>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
-    case 128: return launch_mfma_d<128>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
+    case 16: return launch_mfma_d<16>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, streaming, stream);
+    case 32: return launch_mfma_d<32>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, streaming, stream);
+    case 64: return launch_mfma_d<64>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, streaming, stream);
+    case 128: return launch_mfma_d<128>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, streaming, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -160,12 +160,15 @@ constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
 
 // Waves per SIMD: D = 512 takes all 256 VGPRs and 128 KiB of LDS (one
 // workgroup per CU); D = 256 fits two workgroups per CU (64 KiB of LDS each).
-template <int D>
+// OUT_NT: output stores non-temporal (not when the caller reads the output right
+// away); copies_nt: K/V copies non-temporal (few query tiles per head, and not
+// when the caller has just written the inputs).
+template <int D, bool OUT_NT = true>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(512 / D, 512 / D)))
 void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
                                const uint16_t *__restrict__ V, const int32_t *__restrict__ key_lengths,
                                int causal, uint16_t *__restrict__ O, int H, int64_t Lq, int64_t Lk,
-                               float scale_log2, uint32_t n_qtiles, uint32_t n_bh, int kv_stream)
+                               float scale_log2, uint32_t n_qtiles, uint32_t n_bh, int copies_nt)
 {
     static_assert(D == 256 || D == 512, "wide heads only");
     constexpr int kRowBytes = 2 * D;
@@ -248,7 +251,7 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
         const __amdgpu_buffer_rsrc_t rv =
             __builtin_amdgcn_make_buffer_rsrc((void *)(Vh + kv0 * D), (short)0, nbytes, kRsrcWord3);
         uint16_t *kb = lds + (t & 1) * 2 * kTileElems;
-        if (kv_stream) {
+        if (copies_nt) {
 #pragma unroll
             for (int j = 0; j < kSlicesPerWave; ++j) {
                 copy_to_lds<true>(rk, kb + (wave * kSlicesPerWave + j) * 512, coff[j]);
@@ -401,7 +404,8 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
     for (int i = 0; i < 16 / kRps; ++i) {
         const int r = kRps * i + lane / kC, c = lane % kC;
         const u32x4_t v = *(const u32x4_t *)(stage + r * kRowBytes + ((c ^ (r & 15)) << 4));
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)(r * kRowBytes + c * 16), 0, kStoreStreaming);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)(r * kRowBytes + c * 16), 0,
+                                               OUT_NT ? kStoreStreaming : 0);
     }
     SDPA_STAMP(3);
 }
@@ -409,15 +413,22 @@ void sdpa_fwd_mfma_wide_kernel(const uint16_t *__restrict__ Q, const uint16_t *_
 template <int D>
 hipError_t launch_wide_d(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                          int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                         hipStream_t stream)
+                         bool streaming, hipStream_t stream)
 {
     const uint32_t n_qtiles = (uint32_t)((Lq + kBM - 1) / kBM);
     const uint32_t n_bh = (uint32_t)(B * H);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    hipLaunchKernelGGL((sdpa_fwd_mfma_wide_kernel<D>), dim3(n_qtiles * n_bh), dim3(kWaves * 64), 0,
-                       stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
-                       key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh,
-                       (int)(n_qtiles <= kStreamQueryTiles));
+    const int copies_nt = streaming && n_qtiles <= kStreamQueryTiles;
+    if (streaming)
+        hipLaunchKernelGGL((sdpa_fwd_mfma_wide_kernel<D, true>), dim3(n_qtiles * n_bh), dim3(kWaves * 64), 0,
+                           stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                           key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh,
+                           copies_nt);
+    else
+        hipLaunchKernelGGL((sdpa_fwd_mfma_wide_kernel<D, false>), dim3(n_qtiles * n_bh), dim3(kWaves * 64), 0,
+                           stream, (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                           key_lengths, causal, (uint16_t *)out, (int)H, Lq, Lk, scale_log2, n_qtiles, n_bh,
+                           copies_nt);
     return hipGetLastError();
 }
 
@@ -425,10 +436,10 @@ hipError_t launch_wide_d(const void *Q, const void *K, const void *V, const int3
 
 hipError_t launch_mfma_wide(const void *Q, const void *K, const void *V, const int32_t *key_lengths,
                             int causal, void *out, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
-                            hipStream_t stream)
+                            bool streaming, hipStream_t stream)
 {
-    if (d == 256) return launch_wide_d<256>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
-    if (d == 512) return launch_wide_d<512>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, stream);
+    if (d == 256) return launch_wide_d<256>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, streaming, stream);
+    if (d == 512) return launch_wide_d<512>(Q, K, V, key_lengths, causal, out, B, H, Lq, Lk, streaming, stream);
     return hipErrorInvalidValue;
 }
 

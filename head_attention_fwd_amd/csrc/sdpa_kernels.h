@@ -21,18 +21,22 @@ hipError_t launch_generic(const void *Q, const void *K, const void *V,
                           int d_k, int d_v, bool is_bf16, hipStream_t stream);
 
 // bf16, d_k = d_v = d with d in {16, 32, 64, 128}, on the matrix cores
-// (hipErrorInvalidValue for any other d).
+// (hipErrorInvalidValue for any other d).  streaming: the inputs come from and
+// the output goes to memory nobody reads soon (output stores, and for heads
+// with few query tiles the Q/K/V copies, with the non-temporal cache policy);
+// false when the output is read right away or the inputs were just written.
 hipError_t launch_mfma(const void *Q, const void *K, const void *V,
                        const int32_t *key_lengths, int causal, void *out,
                        int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
-                       hipStream_t stream);
+                       bool streaming, hipStream_t stream);
 
 // bf16, d_k = d_v = d with d in {256, 512}, on the matrix cores (16 query rows
 // per wave, v_mfma_f32_16x16x32_bf16); hipErrorInvalidValue for any other d.
+// streaming: as for launch_mfma.
 hipError_t launch_mfma_wide(const void *Q, const void *K, const void *V,
                             const int32_t *key_lengths, int causal, void *out,
                             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int d,
-                            hipStream_t stream);
+                            bool streaming, hipStream_t stream);
 
 // As launch_mfma, restricted self-attention: key j is legal for query i only
 // when |i - j| <= radius (radius >= 0).

@@ -25,12 +25,12 @@ hipError_t launch_generic(const void *, const void *, const void *, const int32_
     return counted();
 }
 hipError_t launch_mfma(const void *, const void *, const void *, const int32_t *, int, void *,
-                       int64_t, int64_t, int64_t, int64_t, int, hipStream_t)
+                       int64_t, int64_t, int64_t, int64_t, int, bool, hipStream_t)
 {
     return counted();
 }
 hipError_t launch_mfma_wide(const void *, const void *, const void *, const int32_t *, int, void *,
-                            int64_t, int64_t, int64_t, int64_t, int, hipStream_t)
+                            int64_t, int64_t, int64_t, int64_t, int, bool, hipStream_t)
 {
     return counted();
 }

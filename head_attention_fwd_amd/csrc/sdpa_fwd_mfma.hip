@@ -1064,23 +1064,25 @@ __device__ __forceinline__ void attend_query_tile(
     SDPA_STAMP(3);
 }
 
-// Balanced order of a non-causal launch with per-entry key lengths (at most 64
-// entries, a multiple of 8 (entry, head) pairs, at most kBalancedMaxTiles key
-// tiles per entry).  The query tiles of a pair cost about the entry's count of
-// key tiles.  Every wave ranks the entries by that count (longest first, ties
-// by index; one ballot per count), then reads its query tile off a fixed plan:
-// pairs in rank order are dealt to the 8 XCDs in a snake (0..7, 7..0, ...),
-// and within an XCD its query tiles, longest first, fill rounds of 32
-// dispatch positions (one per CU), every other round reversed, so that the
-// workgroups a CU runs at once add up to about the same work.  The hardware
-// starts workgroup w on XCD w % 8 and an XCD's workgroups in order of w / 8;
-// the order affects speed only (every query tile is taken exactly once).
-// Measured before it was built, by permuting the entries' lengths on the host
-// to the same effect: base encoder -10.5 %, big cross -10 %, d = 128 encoder
-// -13 %.  Returns the entry's key length, clamped to [0, Lk].
+// Balanced order of a launch with per-entry key lengths (at most 64 entries, a
+// multiple of 8 (entry, head) pairs, at most kBalancedMaxTiles key tiles per
+// entry).  The query tiles of a pair cost about the entry's count of key tiles
+// (causal: the later query tile more; both grow with the length).  Every wave
+// ranks the entries by that count (longest first, ties by index; one ballot
+// per count), then reads its query tile off a fixed plan: pairs in rank order
+// are dealt to the 8 XCDs in a snake (0..7, 7..0, ...), and within an XCD its
+// query tiles, longest first, fill rounds of 32 dispatch positions (one per
+// CU), every other round reversed, so that the workgroups a CU runs at once
+// add up to about the same work.  The hardware starts workgroup w on XCD
+// w % 8 and an XCD's workgroups in order of w / 8; the order affects speed
+// only (every query tile is taken exactly once).  Measured before it was
+// built, by permuting the entries' lengths on the host to the same effect:
+// base encoder -10.5 %, big cross -10 %, d = 128 encoder -13 %.  Returns the
+// entry's key length, clamped to [0, Lk].
 __device__ inline int64_t balanced_item(uint32_t w, uint32_t n_qtiles, uint32_t n_bh, int H,
                                         const int32_t *__restrict__ key_lengths, int64_t Lk, int BN,
-                                        int lane, int wave, int *s_len, uint32_t &bh, uint32_t &qt)
+                                        int lane, int wave, int *s_len, int causal, uint32_t &bh,
+                                        uint32_t &qt)
 {
     const int B = (int)(n_bh / (uint32_t)H);
     // Wave 0 reads the lengths and hands them to the other waves through LDS:
@@ -1114,6 +1116,7 @@ __device__ inline int64_t balanced_item(uint32_t w, uint32_t n_qtiles, uint32_t 
     const uint32_t i = 32 * r + ((r & 1) ? s - 1 - p : p);    // rank of the tile in the XCD
     const uint32_t u = i / n_qtiles;                          // rank of its pair in the XCD
     qt = i % n_qtiles;
+    if (causal) qt = n_qtiles - 1 - qt;                       // the pair's longest tile first
     const uint32_t k = 8 * u + ((u & 1) ? 7 - x : x);         // global rank of the pair
     const uint32_t e = k / (uint32_t)H;                       // rank of its entry
     const uint64_t mb = __builtin_amdgcn_ballot_w64(t >= 0 && rank == e);
@@ -1163,7 +1166,10 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void sdpa_fwd_mfma_kernel(
     const uint32_t w = blockIdx.x;
     uint32_t bh, qt;
     int64_t len_known = -1;
-    if (causal) {
+    if (flags & kFlagBalanced) {
+        len_known = balanced_item(w, n_qtiles, n_bh, H, key_lengths, Lk, A::BN, lane, wave, s_len, causal,
+                                  bh, qt);
+    } else if (causal) {
         if ((n_bh & 7) == 0) {
             const uint32_t hx = n_bh >> 3, j = w >> 3;   // heads per XCD, position in the XCD
             // groups of G heads in turn, longest tiles first within a group,
@@ -1178,8 +1184,6 @@ __attribute__((amdgpu_waves_per_eu(WAVES, WAVES))) void sdpa_fwd_mfma_kernel(
             bh = w % n_bh;
             qt = n_qtiles - 1 - w / n_bh;
         }
-    } else if (flags & kFlagBalanced) {
-        len_known = balanced_item(w, n_qtiles, n_bh, H, key_lengths, Lk, A::BN, lane, wave, s_len, bh, qt);
     } else {
         const uint32_t n_items = n_qtiles * n_bh;
         const uint32_t item = (n_items & 7) == 0 ? (w & 7) * (n_items >> 3) + (w >> 3) : w;
@@ -1523,13 +1527,13 @@ hipError_t launch_fwd(const void *Q, const void *K, const void *V, const int32_t
     // Each K/V row is copied once per query tile of its head: with few of them
     // the rows stream through the caches (non-temporal copies).
     int flags = (streaming && n_qtiles <= kStreamQueryTiles) ? kFlagCopiesNt : 0;
-    // Balanced order: non-causal launches with per-entry key lengths whose
-    // workgroups are all resident at once (with more, the hardware balances
-    // by handing free slots to the next workgroups, and the per-workgroup
-    // ranking only costs: d = 32 encoder +9 %, d = 16 +5 %).
+    // Balanced order: launches with per-entry key lengths whose workgroups
+    // are all resident at once (with more, the hardware balances by handing
+    // free slots to the next workgroups, and the per-workgroup ranking only
+    // costs: d = 32 encoder +9 %, d = 16 +5 %).
     const int64_t B = n_bh / H;
     const int64_t slots = (int64_t)kCUs * (4 * WAVES / NW);
-    if (!causal && key_lengths && B <= 64 && (n_bh & 7) == 0 &&
+    if (key_lengths && B <= 64 && (n_bh & 7) == 0 &&
         (Lk + 32 * NB - 1) / (32 * NB) <= kBalancedMaxTiles && (int64_t)n_qtiles * n_bh <= slots)
         flags |= kFlagBalanced;
     if (streaming)

@@ -213,11 +213,11 @@ def test_padded_lengths_full(case, d):
     assert_parity(got, ref, v, "bf16", "padded lengths B=%d h=%d d=%d" % (B, H, d))
 
 
-# Non-causal launches with per-entry key lengths whose workgroups are all
-# resident at once take the balanced work order (entries ranked by their count
-# of key tiles in every wave, query tiles dealt over XCDs and dispatch rounds
-# from that rank): every query tile must still be computed exactly once, for
-# any mix of lengths (ties, empty and over-long entries).
+# Launches with per-entry key lengths whose workgroups are all resident at
+# once take the balanced work order (entries ranked by their count of key
+# tiles in every wave, query tiles dealt over XCDs and dispatch rounds from
+# that rank), causal or not: every query tile must still be computed exactly
+# once, for any mix of lengths (ties, empty and over-long entries).
 BALANCED = [
     (64, 8, 256, 256, 64),    # the base encoder's shape, d = 64 (32-key tiles)
     (32, 16, 256, 320, 64),   # the big cross-attention shape
@@ -229,8 +229,9 @@ BALANCED = [
 ]
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
 @pytest.mark.parametrize("case", BALANCED, ids=lambda c: "B%d_h%d_Lq%d_Lk%d_d%d" % c)
-def test_balanced_order_full(case):
+def test_balanced_order_full(case, causal):
     B, H, Lq, Lk, d = case
     rng = np.random.default_rng(B * 131 + H)
     lengths = rng.integers(-3, Lk + 5, size=B).tolist()
@@ -239,7 +240,7 @@ def test_balanced_order_full(case):
         lengths[1] = 0                   # and an empty one
         lengths[2] = lengths[3 % B] if B > 3 else lengths[2]   # a tie
     q, k, v, _ = workloads.draw(B, H, Lq, Lk, d, d, dtype="bf16", seed=900 + B + H + d)
-    announce("balanced order B=%d h=%d Lq=%d Lk=%d d=%d" % case)
-    got = run(q, k, v, lengths, False, "bf16", fill=float("nan"))
-    ref = oracle.attention(q, k, v, key_lengths=lengths, causal=False)
-    assert_parity(got, ref, v, "bf16", "balanced order %s" % (case,))
+    announce("balanced order B=%d h=%d Lq=%d Lk=%d d=%d causal=%s" % (case + (causal,)))
+    got = run(q, k, v, lengths, causal, "bf16", fill=float("nan"))
+    ref = oracle.attention(q, k, v, key_lengths=lengths, causal=causal)
+    assert_parity(got, ref, v, "bf16", "balanced order %s causal=%s" % (case, causal))

@@ -8,6 +8,8 @@ the same on every run.  Head sizes cover the matrix-core sizes (16, 32, 64,
 (129 .. 512).  Sizes stay small enough for the oracle to finish in well under a
 second per case.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -70,3 +72,42 @@ def test_sweep(case):
         got = out.float().cpu().numpy().astype(np.float64)
     ref = oracle.attention(q, k, v, key_lengths=lengths, causal=causal, radius=radius)
     assert_parity(got, ref, v, dtype, _id(case))
+
+
+def _balanced_cases(n=24, seed=20261203):
+    """Shapes that take the balanced work order of the matrix-core kernel: bf16,
+    d_k = d_v in {16, 32, 64, 128}, per-entry key lengths, at most 64 entries and
+    a multiple of 8 (entry, head) pairs, few enough query tiles to be resident at
+    once (the launcher decides; shapes past its limits take the fixed order and
+    are checked the same way)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = int(rng.choice([1, 2, 4, 8, 16]))
+        step = 8 // math.gcd(8, H)          # B * H a multiple of 8
+        B = int(rng.integers(1, 65))
+        B = max(step, B - B % step)
+        Lq = int(rng.integers(1, 400))
+        Lk = int(rng.integers(1, 700))
+        d = int(rng.choice([16, 32, 64, 128]))
+        causal = bool(rng.random() < 0.5)
+        lengths = [int(x) for x in rng.integers(-2, Lk + 3, size=B)]
+        while B * H * Lq * Lk * 2 * d > 4e8:
+            Lq = max(1, Lq // 2)
+        out.append((B, H, Lq, Lk, d, causal, lengths))
+    return out
+
+
+BALANCED_CASES = _balanced_cases()
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES,
+                         ids=lambda c: "%dx%dx%dx%d_d%d%s" % (c[0], c[1], c[2], c[3], c[4], "_c" if c[5] else ""))
+def test_sweep_balanced(case):
+    B, H, Lq, Lk, d, causal, lengths = case
+    assert (B * H) % 8 == 0 and B <= 64
+    q, k, v, _ = workloads.draw(B, H, Lq, Lk, d, d, dtype="bf16", seed=Lq * 17 + Lk + d)
+    announce("balanced sweep %s" % (case[:6],))
+    got = run(q, k, v, lengths, causal, "bf16", fill=float("nan"))
+    ref = oracle.attention(q, k, v, key_lengths=lengths, causal=causal)
+    assert_parity(got, ref, v, "bf16", "balanced sweep %s" % (case[:6],))

@@ -62,7 +62,11 @@
 //    heads so the workgroups streaming one head's K/V share an L2; causal
 //    grids dispatch the longest query tiles first (greedy longest-first over
 //    the workgroup slots, which the hardware dispatcher fills in order), a
-//    few heads at a time per XCD.
+//    few heads at a time per XCD.  Launches with per-entry key lengths whose
+//    workgroups are all resident at once instead deal their query tiles to
+//    the XCDs and CUs balanced over the entries' key lengths (balanced_item).
+//  * Cache policy: output stores non-temporal (O is not read again by the
+//    launch); on heads with few query tiles the Q/K/V copies too.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

@@ -89,17 +89,15 @@ constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
 
 // Shape of the kernels (each value measured on MI355X against its neighbours).
 constexpr int kWaves = 4;              // waves per workgroup (32 query rows each); d = 16: 2
-constexpr int kKeyBlocks = 2;          // 32-key blocks per LDS tile (d = 128: 1)
+constexpr int kKeyBlocks = 2;          // 32-key blocks per LDS tile at d = 32 (d = 64, 128: 1)
 constexpr int kSplitKeyBlocks = 1;     // 32-key blocks per LDS tile of the key-split kernel
-constexpr int kShortKeys = 512;        // d = 64 launches up to this many keys take 32-key tiles
 constexpr int kCausalHeadGroup = 4;    // causal order: heads per group on an XCD
 constexpr int kStreamQueryTiles = 4;   // K/V copies non-temporal up to this many query tiles per head
 constexpr int kBalancedMaxTiles = 32;  // balanced order up to this many key tiles per entry
 constexpr int kCUs = 256;              // compute units of an MI355X (8 XCDs of 32)
 // Run-time flags of the forward kernel, set by the launcher.
 constexpr int kFlagCopiesNt = 1;       // Q/K/V copies non-temporal
-constexpr int kFlagBalanced = 2;       // non-causal work order balanced over the entries' key lengths
-constexpr int kWavesPerSimd64 = 3;     // register budget at d = 64 with 64-key tiles
+constexpr int kFlagBalanced = 2;       // work order balanced over the entries' key lengths
 constexpr int kWavesPerSimd128 = 2;    // register budget of the forward kernel at d = 128 ...
 constexpr int kWavesPerSimd128Long = 3;   // ... and of its form for long key ranges
 constexpr int kLongKeys128 = 1024;     // d = 128 launches with more keys take the long form
@@ -110,7 +108,7 @@ constexpr int kBandKeyBlocks64 = 1;    // restricted attention, d = 64: 32-key t
 // block in flight) fits 4 as well.
 template <int D, int NB = 2, bool BAND = false>
 struct Occupancy {
-    static constexpr int kWaves = D >= 128 ? (BAND ? 2 : kWavesPerSimd128) : (D >= 64 ? (NB == 1 ? 4 : kWavesPerSimd64) : 4);
+    static constexpr int kWaves = D >= 128 ? (BAND ? 2 : kWavesPerSimd128) : (D >= 64 ? (NB == 1 ? 4 : 3) : 4);
 };
 
 // 16-byte chunk swizzles of a row of D bf16 values (D/8 chunks), XORed into
@@ -1561,22 +1559,18 @@ hipError_t launch_mfma_d(const void *Q, const void *K, const void *V, const int3
     // holds 10 of them (2560 slots; 4-wave workgroups with 128-key tiles: 1024).
     constexpr int NW = D <= 16 ? 2 : kWaves;
     // D = 128: 32-key tiles, so that the three-buffer ring stays at 48 KiB.
-    constexpr int NB = D >= 128 ? 1 : (D >= 32 ? kKeyBlocks : 2);
+    // D = 64: 32-key tiles at four waves per SIMD (24 KiB of LDS, 115 VGPRs),
+    // so that every query tile of the base model's launches is resident at
+    // once (causal: the tiles that cross the diagonal are also half as long).
+    // Against 64-key tiles at three waves per SIMD (148 VGPRs, 48 KiB): base
+    // encoder -4 %, big cross -2 % (once the stores and the short launches'
+    // copies were non-temporal), long causal -0.7 to -0.9 %, its multi-head
+    // step -1.5 %.
+    constexpr int NB = D >= 64 ? 1 : (D >= 32 ? kKeyBlocks : 2);
     constexpr int BM = 32 * NW;
     const uint32_t n_qtiles = (uint32_t)((Lq + BM - 1) / BM);
     const uint32_t n_bh = (uint32_t)(B * H);
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    if constexpr (D == 64) {
-        // Short key ranges: 32-key tiles at four waves per SIMD (24 KiB of
-        // LDS, 115 VGPRs), so that every query tile of the base model's
-        // launches is resident at once (causal: the tiles that cross the
-        // diagonal are also half as long).  Base encoder -4 %, big cross -2 %
-        // against 64-key tiles at three waves per SIMD, once the stores and the
-        // short launches' copies were non-temporal.
-        if (Lk <= kShortKeys)
-            return launch_fwd<NW, 1, D, Occupancy<D, 1>::kWaves>(Q, K, V, key_lengths, causal, out, H, Lq, Lk,
-                                                                 scale_log2, n_qtiles, n_bh, streaming, stream);
-    }
     if constexpr (D == 128) {
         // Long key ranges: a register budget of three waves per SIMD (168
         // VGPRs), long causal 496 -> 480 us; short launches keep two (19.1
